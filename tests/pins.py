@@ -1,0 +1,293 @@
+"""Checks that pin the oracle to facts outside itself.
+
+Each check takes an object ``o`` exposing the oracle's functions, so the
+mutation tests can hand in a copy with one step deliberately broken (on the
+CPU) and confirm the check then fails.  Sources for each fact are given per
+check; see ``oracle/uq_oracle.py`` for the readings R-* they refer to.
+"""
+from __future__ import annotations
+
+import os
+import re
+from fractions import Fraction
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# ---------------------------------------------------------------------------
+# Golden fixture parsing
+# ---------------------------------------------------------------------------
+def load_packing_cases():
+    """Parse tests/golden/packing_handbuilt.txt into a list of case dicts."""
+    cases, cur = [], None
+    with open(os.path.join(GOLDEN, "packing_handbuilt.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            if line.startswith("case "):
+                _, name, scheme, g, n, k = line.split()
+                cur = dict(name=name, scheme=scheme, group=int(g[2:]),
+                           n=int(n[2:]), k=int(k[2:]), w={}, codes={}, params={})
+                cases.append(cur)
+                continue
+            key, val = line.split(":", 1)
+            m = re.fullmatch(r"(w|codes|params)(\d+)", key)
+            kind, row = m.group(1), int(m.group(2))
+            if kind == "w":
+                cur["w"][row] = val.strip()
+            elif kind == "codes":
+                cur["codes"][row] = bytes(int(b, 16) for b in val.split())
+            else:
+                cur["params"][row] = [int(p, 16) for p in val.split()]
+    return cases
+
+
+def build_case_weights(case, codebook):
+    """Evaluate the per-row recipes of a golden case into an fp32 [n, k] matrix."""
+    n, k = case["n"], case["k"]
+    w = np.zeros((n, k), dtype=np.float64)
+    for r in range(n):
+        expr = case["w"][r]
+        for col in range(k):
+            w[r, col] = eval(expr, {"__builtins__": {}},  # own fixture file
+                             {"k": col, "C": [float(c) for c in codebook]})
+    w32 = w.astype(np.float32)
+    assert np.array_equal(w32.astype(np.float64), w), "recipe not exact in fp32"
+    return w32
+
+
+# ---------------------------------------------------------------------------
+# P1: bit-exact packing on hand-built matrices
+# ---------------------------------------------------------------------------
+def check_packing_golden(o):
+    """Quantize + pack each hand-built case; bytes and params must equal the fixture.
+
+    Source: Ultra LLM Engine, Core Components > Quantization (codes packed into
+    bytes); the expected bytes are derived by hand in the fixture file.
+    """
+    cb = o.nf4_codebook()
+    for case in load_packing_cases():
+        w = build_case_weights(case, cb)
+        bits = o.BITS[case["scheme"]]
+        if case["scheme"] == "nf4":
+            q, a16 = o.quantize_nf4(w, case["group"])
+            params = o.pack_params_nf4(a16)
+            wdq = o.dequant_nf4(q, a16, case["group"])
+        else:
+            q, s16, z16 = o.quantize_int(w, bits, case["group"])
+            params = o.pack_params_int(s16, z16)
+            wdq = o.dequant_int(q, s16, z16, case["group"])
+        codes = o.pack_codes(q, bits)
+        for r in range(case["n"]):
+            assert codes[r].tobytes() == case["codes"][r], (case["name"], r, codes[r].tobytes().hex())
+            got = [int(v) for v in np.asarray(params[r]).reshape(-1)]
+            assert got == case["params"][r], (case["name"], r, [hex(v) for v in got])
+        # every weight of these cases lies on the grid: dequant must return it
+        assert np.array_equal(wdq, w), case["name"]
+        # unpacking returns the codes
+        assert np.array_equal(o.unpack_codes(codes, bits, case["k"]), q), case["name"]
+
+
+# ---------------------------------------------------------------------------
+# Exact grid recovery: W = q*s + z built from known q, s, z
+# ---------------------------------------------------------------------------
+def check_grid_recovery(o, bits, group, seed=0, n=6, k=None):
+    """Weights built exactly on a known grid are recovered exactly.
+
+    Source: Ultra LLM Engine, Core Components > Quantization, ``int`` row
+    (asymmetric uniform group-wise quantization).  With s = 2^-e, a dyadic z
+    and each group holding both code 0 and code qmax, the scale
+    (max - min)/qmax is s, the zero (min) is z, every division is exact, and
+    so quantize must return (q, s, z) and dequant must return W.
+    """
+    rng = np.random.default_rng(seed)
+    k = k or 4 * group
+    qmax = (1 << bits) - 1
+    g = k // group
+    q = rng.integers(0, qmax + 1, size=(n, g, group))
+    perm = rng.permuted(np.tile(np.arange(group), (n, g, 1)), axis=2)
+    np.put_along_axis(q, perm[..., :1], 0, axis=2)       # code 0 somewhere
+    np.put_along_axis(q, perm[..., 1:2], qmax, axis=2)   # code qmax somewhere
+    e = rng.integers(3, 11, size=(n, g))
+    s = np.ldexp(1.0, -e)
+    z = rng.integers(-1023, 1024, size=(n, g)) * 2.0 ** -10
+    w64 = q * s[..., None] + z[..., None]
+    w = w64.astype(np.float32).reshape(n, k)
+    assert np.array_equal(w.astype(np.float64).reshape(n, g, group), w64)
+    q2, s16, z16 = o.quantize_int(w, bits, group)
+    assert np.array_equal(q2.reshape(n, g, group), q.astype(np.uint8)), "codes"
+    assert np.array_equal(s16.astype(np.float64), s), "scale"
+    assert np.array_equal(z16.astype(np.float64), z), "zero"
+    assert np.array_equal(o.dequant_int(q2, s16, z16, group), w), "dequant"
+
+
+# ---------------------------------------------------------------------------
+# P2: round-trip error bound
+# ---------------------------------------------------------------------------
+def check_roundtrip_int(o, w, bits, group):
+    """|w' - w| <= s/2 plus half an fp32 ulp of w' (rounding of w').
+
+    Follows from rounding (w - z)/s to the nearest integer code; constant
+    groups (s = 0) return fp16(w), within half an fp16 ulp.
+    Returns the largest ratio error / bound seen.
+    """
+    q, s16, z16 = o.quantize_int(w, bits, group)
+    wdq = o.dequant_int(q, s16, z16, group)
+    n, k = w.shape
+    err = np.abs(wdq.astype(np.float64) - w.astype(np.float64)).reshape(n, k // group, group)
+    s = s16.astype(np.float64)[..., None]
+    half_ulp32 = np.spacing(np.abs(wdq)).astype(np.float64).reshape(err.shape) / 2
+    half_ulp16 = np.spacing(np.abs(w).astype(np.float16)).astype(np.float64).reshape(err.shape) / 2
+    bound = np.where(s > 0, s / 2 + half_ulp32, half_ulp16 + half_ulp32)
+    ratio = float((err / bound).max())
+    assert ratio <= 1.0, f"round trip exceeds s/2: ratio {ratio}"
+    # every non-constant group uses both end codes
+    qg = q.reshape(err.shape)
+    live = s16 > 0
+    assert (qg.min(axis=2)[live] == 0).all(), "a group lacks code 0"
+    assert (qg.max(axis=2)[live] == (1 << bits) - 1).all(), "a group lacks code qmax"
+    return ratio
+
+
+def check_roundtrip_nf4(o, w, group=64):
+    """|w' - w| <= a * (max half gap of the codebook, or |v| - 1 past the ends) + 1/2 ulp."""
+    cb = o.nf4_codebook().astype(np.float64)
+    q, a16 = o.quantize_nf4(w, group)
+    wdq = o.dequant_nf4(q, a16, group)
+    n, k = w.shape
+    a = a16.astype(np.float64)[..., None]
+    w64 = w.astype(np.float64).reshape(n, k // group, group)
+    v = w64 / a
+    halfgap = float(np.max(np.diff(cb))) / 2
+    reach = np.maximum(halfgap, np.abs(v) - 1.0)
+    bound = a * reach * (1 + 1e-12) + np.spacing(np.abs(wdq)).reshape(v.shape) / 2
+    err = np.abs(wdq.astype(np.float64).reshape(v.shape) - w64)
+    ratio = float((err / bound).max())
+    assert ratio <= 1.0, f"NF4 round trip exceeds bound: {ratio}"
+    return ratio
+
+
+# ---------------------------------------------------------------------------
+# P3 / P4: codebook and nearest-code rule
+# ---------------------------------------------------------------------------
+def check_codebook(o):
+    """Invariants of the NormalFloat construction, via an independent inverse CDF.
+
+    Source: Ultra LLM Engine, Core Components > Quantization, ``nf4`` row
+    (QLoRA codebook).  Checked against scipy's normal quantile function (a
+    different implementation from the oracle's) and against the defining
+    property: the positive entries, scaled back, sit at equally spaced
+    normal-CDF probabilities from 0.5 to p*, the negative ones likewise.
+    """
+    from scipy.stats import norm
+    c = o.nf4_codebook()
+    assert c.dtype == np.float32 and c.shape == (16,)
+    assert (np.diff(c) > 0).all(), "not strictly increasing"
+    assert c[0] == -1.0 and c[7] == 0.0 and c[15] == 1.0
+    assert (c < 0).sum() == 7 and (c > 0).sum() == 8
+    p = o.NF4_PSTAR
+    top = norm.ppf(p)
+    pos = norm.ppf(np.linspace(p, 0.5, 9)[:-1])
+    neg = -norm.ppf(np.linspace(p, 0.5, 8)[:-1])
+    ref = (np.sort(np.concatenate([pos, [0.0], neg])) / top).astype(np.float32)
+    assert np.array_equal(ref.view(np.uint32), c.view(np.uint32)), "scipy route differs"
+    probs_pos = norm.cdf(c[8:].astype(np.float64) * top)
+    assert np.allclose(probs_pos, np.linspace(0.5, p, 9)[1:], atol=1e-6)
+    probs_neg = norm.cdf(-c[:7].astype(np.float64) * top)
+    assert np.allclose(np.sort(probs_neg), np.linspace(0.5, p, 8)[1:], atol=1e-6)
+
+
+def check_nearest_bruteforce(o, seed=0, n=16, k=256):
+    """NF4 codes equal a brute-force argmin over |v - C_j| (first index on ties)."""
+    c = o.nf4_codebook().astype(np.float64)
+    rng = np.random.default_rng(seed)
+    w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    # plant exact midpoint ties where the midpoint is an fp32 value: between 0
+    # and C[8] the midpoint is C[8]/2; force a = 1 by placing 1.0 in the group
+    w[0, 0] = 1.0
+    w[0, 1] = np.float32(c[8] / 2)     # midway between C[7] = 0 and C[8]
+    w[0, 2] = np.float32(c[6] / 2)     # midway between C[6] and C[7] = 0
+    q, a16 = o.quantize_nf4(w, 64)
+    v = w.astype(np.float64).reshape(n, k // 64, 64) / a16.astype(np.float64)[..., None]
+    d = np.abs(v[..., None] - c)
+    brute = d.argmin(axis=-1).reshape(n, k)    # argmin returns the first minimum
+    assert np.array_equal(q, brute.astype(np.uint8))
+    assert q[0, 1] == 7 and q[0, 2] == 6, "a tie must go to the lower index"
+
+
+# ---------------------------------------------------------------------------
+# P5 / P6: products
+# ---------------------------------------------------------------------------
+def check_products_exact(o, seed=0, m=3, n=5, k=48):
+    """fp64 products agree with exact rational dot products on tiny shapes.
+
+    Bound for an fp64 dot product of length k: k * 2^-53 * sum |x*w|.
+    Shapes are non-square so a transposed operand cannot pass.
+    """
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((m, k)).astype(np.float16)
+    w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    for ref_fn, xs, ws in ((o.gemv_ref, x.astype(np.float64), w.astype(np.float64)),
+                           (o.gemm_ref, o.bf16_rne(x.astype(np.float32)).astype(np.float64),
+                            o.bf16_rne(w).astype(np.float64))):
+        y = ref_fn(x, w)
+        assert y.shape == (m, n)
+        for i in range(m):
+            for j in range(n):
+                exact = sum(Fraction(float(xs[i, t])) * Fraction(float(ws[j, t])) for t in range(k))
+                mag = float(np.abs(xs[i] * ws[j]).sum())
+                assert abs(Fraction(float(y[i, j])) - exact) <= Fraction(k * mag) * Fraction(2) ** -53
+
+
+def check_one_hot(o, seed=0, n=7, k=64):
+    """x = e_t returns column t of w' (GEMV) and of bf16(w') (GEMM) exactly."""
+    rng = np.random.default_rng(seed)
+    w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    eye = np.eye(k, dtype=np.float16)
+    assert np.array_equal(o.gemv_ref(eye, w), w.astype(np.float64).T)
+    assert np.array_equal(o.gemm_ref(eye, w), o.bf16_rne(w).astype(np.float64).T)
+
+
+def check_int8_integer_matmul(o, seed=0, m=4, n=6, k=128, group=64):
+    """INT8 with s = 1, z = 0 (integer weights spanning 0..255) is an integer matmul."""
+    rng = np.random.default_rng(seed)
+    wi = rng.integers(0, 256, size=(n, k))
+    wi[:, ::group] = 0
+    wi[:, 1::group] = 255
+    x = rng.integers(-8, 9, size=(m, k)).astype(np.float16)
+    codes, params = o.quantize_pack(wi.astype(np.float32), "int8", group)
+    assert np.array_equal(codes, wi.astype(np.uint8))
+    wdq = o.dequant_packed(codes, params, "int8", group, k)
+    y = o.gemv_ref(x, wdq)
+    assert np.array_equal(y, (x.astype(np.int64) @ wi.T).astype(np.float64))
+
+
+def check_bf16(o, seed=0):
+    """bf16 rounding equals torch's CPU conversion (nearest, ties to even)."""
+    import torch
+    rng = np.random.default_rng(seed)
+    a = (rng.standard_normal(4096) * 10.0 ** rng.integers(-6, 6, 4096)).astype(np.float32)
+    ties = rng.integers(0, 2 ** 31, 512, dtype=np.uint64).astype(np.uint32)
+    ties = (ties & np.uint32(0x7F7F0000)) | np.uint32(0x8000)      # exact halfway cases
+    a = np.concatenate([a, ties.view(np.float32), -ties.view(np.float32)])
+    ref = torch.from_numpy(a).to(torch.bfloat16).to(torch.float32).numpy()
+    assert np.array_equal(o.bf16_rne(a).view(np.uint32), ref.view(np.uint32))
+    # hand values: 1 + 2^-8 is halfway between 1 and 1 + 2^-7 -> even (1.0);
+    # 1 + 3*2^-8 is halfway between 1 + 2^-7 and 1 + 2^-6 -> even (1 + 2^-6)
+    hv = np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, 1 + 2 ** -8 + 2 ** -20], dtype=np.float32)
+    assert o.bf16_rne(hv).tolist() == [1.0, 1 + 2 ** -6, 1 + 2 ** -7]
+
+
+def check_fp16_conversion(seed=0):
+    """numpy's fp32 -> fp16 conversion (the oracle's primitive) rounds to nearest even."""
+    import torch
+    rng = np.random.default_rng(seed)
+    a = (rng.standard_normal(8192) * 10.0 ** rng.integers(-9, 5, 8192)).astype(np.float32)
+    ref = torch.from_numpy(a).to(torch.float16).numpy()
+    assert np.array_equal(a.astype(np.float16).view(np.uint16), ref.view(np.uint16))
+    # hand values: 1 + 2^-11 is halfway -> 1.0; 1 + 3*2^-11 -> 1 + 2^-9
+    hv = np.array([1 + 2 ** -11, 1 + 3 * 2 ** -11, 2 ** -4], dtype=np.float32)
+    assert hv.astype(np.float16).view(np.uint16).tolist() == [0x3C00, 0x3C02, 0x2C00]

@@ -1,0 +1,124 @@
+"""Each pin must fail when a plausible mistake is planted in the oracle (CPU only).
+
+The mistakes are planted in a copy of the oracle's function table; the oracle
+module itself is untouched.
+"""
+import types
+
+import numpy as np
+import pytest
+
+import oracle as o
+from tests import pins
+
+
+def mutant(**overrides):
+    ns = types.SimpleNamespace(**{name: getattr(o, name) for name in o.__all__})
+    for k, v in overrides.items():
+        setattr(ns, k, v)
+    return ns
+
+
+def dequant_drop_zero(q, s16, z16, group):
+    return o.dequant_int(q, s16, np.zeros_like(z16), group)
+
+
+def dequant_zero_sign(q, s16, z16, group):
+    return o.dequant_int(q, s16, -z16, group)
+
+
+def quantize_wrong_qmax(w, bits, group):
+    # divides the span by 2^b instead of 2^b - 1
+    n, k = w.shape
+    wg = w.reshape(n, k // group, group)
+    mn, mx = wg.min(2), wg.max(2)
+    s16 = ((mx - mn) / np.float32(1 << bits)).astype(np.float16)
+    z16 = mn.astype(np.float16)
+    q = np.clip(np.rint((wg - z16[..., None].astype(np.float64)) / s16[..., None]), 0,
+                (1 << bits) - 1)
+    return q.astype(np.uint8).reshape(n, k), s16, z16
+
+
+def quantize_truncating(w, bits, group):
+    # floor instead of round-to-nearest for the code
+    q, s16, z16 = o.quantize_int(w, bits, group)
+    n, k = w.shape
+    wg = w.reshape(n, k // group, group).astype(np.float64)
+    d = (wg - z16.astype(np.float64)[..., None]) / s16.astype(np.float64)[..., None]
+    q2 = np.clip(np.floor(d), 0, (1 << bits) - 1)
+    return q2.astype(np.uint8).reshape(n, k), s16, z16
+
+
+def pack_high_first(q, bits):
+    n, k = q.shape
+    per = 8 // bits
+    qq = q.astype(np.uint32).reshape(n, k // per, per)[:, :, ::-1]
+    return o.pack_codes(qq.reshape(n, k).astype(np.uint8), bits)
+
+
+def quantize_nf4_ties_up(w, group=64, codebook=None):
+    c = o.nf4_codebook()
+    n, k = w.shape
+    wg = w.reshape(n, k // group, group)
+    a16 = np.abs(wg).max(2).astype(np.float16)
+    v = wg.astype(np.float64) / a16.astype(np.float64)[..., None]
+    mid = (c[:-1].astype(np.float64) + c[1:].astype(np.float64)) / 2
+    q = np.searchsorted(mid, v.reshape(-1), side="right").reshape(v.shape)
+    return q.astype(np.uint8).reshape(n, k), a16
+
+
+def codebook_symmetric():
+    # a plausible wrong table: symmetric quantiles, no exact zero
+    c = o.nf4_codebook().copy()
+    c[:8] = -c[8:][::-1]
+    return c
+
+
+def gemv_transposed_rows(x16, wdq):
+    return (x16.astype(np.float64) @ wdq.astype(np.float64).T)[:, ::-1]
+
+
+def gemv_fp32(x16, wdq):
+    return (x16.astype(np.float32) @ wdq.astype(np.float32).T).astype(np.float64)
+
+
+def gemm_no_x_cast(x16, wdq):
+    return x16.astype(np.float64) @ o.bf16_rne(wdq).astype(np.float64).T
+
+
+def bf16_truncate(a):
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    return (u & np.uint32(0xFFFF0000)).view(np.float32)
+
+
+CASES = [
+    ("dequant drops the zero term", dict(dequant_int=dequant_drop_zero),
+     lambda ns: pins.check_grid_recovery(ns, 4, 64)),
+    ("dequant flips the zero sign", dict(dequant_int=dequant_zero_sign),
+     lambda ns: pins.check_packing_golden(ns)),
+    ("scale divides by 2^b", dict(quantize_int=quantize_wrong_qmax),
+     lambda ns: pins.check_grid_recovery(ns, 4, 32)),
+    ("code truncates", dict(quantize_int=quantize_truncating),
+     lambda ns: pins.check_roundtrip_int(
+         ns, (np.random.default_rng(0).standard_normal((8, 256)) * .02).astype(np.float32), 4, 64)),
+    ("high nibble first", dict(pack_codes=pack_high_first),
+     lambda ns: pins.check_packing_golden(ns)),
+    ("NF4 ties go up", dict(quantize_nf4=quantize_nf4_ties_up),
+     lambda ns: pins.check_nearest_bruteforce(ns)),
+    ("symmetric codebook", dict(nf4_codebook=codebook_symmetric),
+     lambda ns: pins.check_codebook(ns)),
+    ("GEMV output columns reversed", dict(gemv_ref=gemv_transposed_rows),
+     lambda ns: pins.check_products_exact(ns)),
+    ("GEMV in fp32", dict(gemv_ref=gemv_fp32),
+     lambda ns: pins.check_products_exact(ns, k=64)),
+    ("GEMM skips the bf16 cast of x", dict(gemm_ref=gemm_no_x_cast),
+     lambda ns: pins.check_products_exact(ns)),
+    ("bf16 truncates", dict(bf16_rne=bf16_truncate),
+     lambda ns: pins.check_bf16(ns)),
+]
+
+
+@pytest.mark.parametrize("label,over,check", CASES, ids=[c[0] for c in CASES])
+def test_planted_mistake_is_caught(label, over, check):
+    with pytest.raises(AssertionError):
+        check(mutant(**over))

@@ -1,0 +1,99 @@
+"""Seeded synthetic inputs shared by the tests, the smoke check and the benchmark.
+
+This module holds shapes and random draws only -- none of the quantization or
+product arithmetic.  Both the oracle and the HIP path receive the arrays it
+returns; neither is imported here.
+
+Shapes follow the models the "Ultra LLM Engine" page runs: a small random
+decoder (Quick Start: hidden 256) and 4096-wide checkpoints (CLI Examples:
+hidden 4096), with 7B-style projection widths (MLP up-projection 11008, wide
+MLP 14336, attention 4096).  Weights are N(0, 0.02) drawn in fp64 and rounded
+to fp32, optionally with 0.1 % of entries scaled by 20 (outliers); activations
+are N(0, 1) rounded to fp16.  The page's own models are randomly initialised
+(Quick Start and Current Scope), so random weights stand in faithfully.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    scheme: str          # "int2" | "int4" | "int8" | "nf4"
+    group: int
+    k: int
+    n: int
+    ms: tuple            # activation row counts exercised
+    outliers: bool = False
+    seed: int = 0
+    path: str = "gemv"   # "gemv" (M <= 8) or "gemm" (bf16 matrix cores)
+    note: str = field(default="", compare=False)
+
+    @property
+    def mmax(self) -> int:
+        return max(self.ms)
+
+
+# The five workloads (names say what they are).
+WORKLOADS = {
+    "int4_g32_k256_n768": Workload(
+        "int4_g32_k256_n768", "int4", 32, 256, 768, (1,),
+        note="small decoder layer, hidden 256"),
+    "int4_g64_k4096_n11008": Workload(
+        "int4_g64_k4096_n11008", "int4", 64, 4096, 11008, (1, 4), outliers=True,
+        note="7B-style MLP up-projection, decode"),
+    "int8_g128_k4096_n4096": Workload(
+        "int8_g128_k4096_n4096", "int8", 128, 4096, 4096, (1, 8),
+        note="attention q/o projection"),
+    "int2_g16_k4096_n4096": Workload(
+        "int2_g16_k4096_n4096", "int2", 16, 4096, 4096, (1, 8),
+        note="attention q/o projection"),
+    "nf4_g64_k4096_n14336": Workload(
+        "nf4_g64_k4096_n14336", "nf4", 64, 4096, 14336, (1,),
+        note="wide MLP projection"),
+    "int4_g128_k4096_n11008_gemm": Workload(
+        "int4_g128_k4096_n11008_gemm", "int4", 128, 4096, 11008, (16, 64, 256),
+        path="gemm", note="batched decode / prefill"),
+}
+
+# The workload the headline throughput figure is quoted on.
+HEADLINE = "int4_g64_k4096_n11008"
+
+
+def make_weights(n: int, k: int, seed: int = 0, outliers: bool = False,
+                 rng: np.random.Generator | None = None) -> np.ndarray:
+    """fp32 [n, k] ~ N(0, 0.02); with outliers, 0.1 % of entries (no repeats) x20."""
+    rng = np.random.default_rng(seed) if rng is None else rng
+    w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    if outliers:
+        idx = rng.choice(n * k, (n * k) // 1000, replace=False)
+        w.flat[idx] *= np.float32(20.0)
+    return w
+
+
+def make_x(m: int, k: int, rng: np.random.Generator) -> np.ndarray:
+    """fp16 [m, k] ~ N(0, 1)."""
+    return rng.standard_normal((m, k)).astype(np.float16)
+
+
+def make_workload(wl: Workload):
+    """(W fp32 [n, k], x fp16 [mmax, k]) from one generator seeded with wl.seed.
+
+    W is drawn first, then the outlier positions, then x; smaller M use the
+    first rows of x.
+    """
+    rng = np.random.default_rng(wl.seed)
+    w = make_weights(wl.n, wl.k, outliers=wl.outliers, rng=rng)
+    x = make_x(wl.mmax, wl.k, rng)
+    return w, x
+
+
+def make_random(n: int, k: int, m: int, seed: int, outliers: bool = False):
+    """Small seeded case for parity sweeps: (W fp32 [n, k], x fp16 [m, k])."""
+    rng = np.random.default_rng(seed)
+    w = make_weights(n, k, outliers=outliers, rng=rng)
+    x = make_x(m, k, rng)
+    return w, x
