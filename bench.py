@@ -1,0 +1,286 @@
+"""Benchmark of the fused dequant-GEMV hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--m M]
+
+One step is one fused dequant + GEMV (or GEMM) launch over one activation
+batch, with the packed weights already resident in HBM.  Weight copies are
+rotated so every step streams its weights from HBM rather than from the
+256 MB Infinity Cache.  The K timed launches are replayed from a HIP graph on
+one stream and bracketed by HIP events on that stream.  Prints one JSON line.
+
+Extra reports: ``--all`` times every workload and activation count and
+writes a markdown table (stderr, and ``--report PATH``).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix cores, published
+METRIC = "dequant-GEMV weight GB/s & % HBM peak, INT4 g64 K=4096 N=11008 M=1"
+KERNEL_SOURCES = ("gemm_group_wise_amd/csrc/gemv.hip", "gemm_group_wise_amd/csrc/gemm.hip",
+                  "gemm_group_wise_amd/csrc/device_common.hpp")
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def weight_bytes(wl: workloads.Workload) -> int:
+    bits = {"int2": 2, "int4": 4, "int8": 8, "nf4": 4}[wl.scheme]
+    per_group = 2 if wl.scheme == "nf4" else 4
+    return wl.n * wl.k * bits // 8 + wl.n * (wl.k // wl.group) * per_group
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+class Setup:
+    """Packed weights (rotated device copies), activations and output for one workload."""
+
+    def __init__(self, uq, wl: workloads.Workload, m: int, rotate: int | None):
+        import torch
+        self.uq, self.wl, self.m = uq, wl, m
+        w, x = workloads.make_workload(wl)
+        self.w_host, self.x_host = w, x[:m]
+        self.lay = uq.layout(wl.scheme, wl.group, wl.n, wl.k)
+        codes, params = uq.uq_pack_weights(self.lay, w)
+        self.codes_host, self.params_host = codes, params
+        self.bytes = codes.nbytes + params.nbytes
+        if rotate is None:  # > 256 MB Infinity Cache + 32 MB L2
+            rotate = max(16, math.ceil(320e6 / self.bytes))
+        self.rotate = rotate
+        dc, dp = torch.from_numpy(codes).cuda(), torch.from_numpy(params).cuda()
+        self.codes = [dc] + [dc.clone() for _ in range(rotate - 1)]
+        self.params = [dp] + [dp.clone() for _ in range(rotate - 1)]
+        self.x = torch.from_numpy(np.ascontiguousarray(self.x_host)).cuda()
+        self.y = torch.empty(m * wl.n, dtype=torch.float32, device="cuda")
+        self.fn = uq.uq_gemv if wl.path == "gemv" else uq.uq_gemm
+        torch.cuda.synchronize()
+
+    def launch(self, i: int, stream: int) -> None:
+        j = i % self.rotate
+        self.fn(self.lay, self.codes[j], self.params[j], self.x, self.y, self.m, stream=stream)
+
+    def graph(self, count: int, start: int = 0):
+        import torch
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            self.launch(start, s.cuda_stream)  # warm the launch path outside capture
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=s):
+                for i in range(count):
+                    self.launch(start + i, s.cuda_stream)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        return g
+
+    def time(self, steps: int, warmup: int):
+        """(ms per step, eager ms per step) over exactly `steps` launches."""
+        import torch
+        R = self.rotate
+        full = self.graph(R)
+        rem = self.graph(steps % R) if steps % R else None
+        stream = torch.cuda.current_stream()
+        for _ in range(max(1, math.ceil(warmup / R))):
+            full.replay()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for _ in range(steps // R):
+            full.replay()
+        if rem is not None:
+            rem.replay()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / steps
+        # eager cross-check (host launch overhead included)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n_eager = min(steps, 4 * R)
+        sp = stream.cuda_stream
+        e0.record(stream)
+        for i in range(n_eager):
+            self.launch(i, sp)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return ms, e0.elapsed_time(e1) / n_eager
+
+    def check_sample(self, rows: int = 96, seed: int = 1) -> float:
+        """Sampled parity of the timed output: oracle on `rows` random weight rows."""
+        import oracle as o
+        torch_y = self.y.cpu().numpy().reshape(self.m, self.wl.n)
+        idx = np.sort(np.random.default_rng(seed).choice(self.wl.n, min(rows, self.wl.n), replace=False))
+        codes, params = o.quantize_pack(self.w_host[idx], self.wl.scheme, self.wl.group)
+        wdq = o.dequant_packed(codes, params, self.wl.scheme, self.wl.group, self.wl.k)
+        if self.wl.path == "gemv":
+            ref, xs, ws = o.gemv_ref(self.x_host, wdq), self.x_host, wdq
+        else:
+            ref = o.gemm_ref(self.x_host, wdq)
+            xs, ws = o.bf16_rne(self.x_host.astype(np.float32)), o.bf16_rne(wdq)
+        got = torch_y[:, idx].astype(np.float64)
+        err = got - ref
+        rel = float(np.linalg.norm(err) / np.linalg.norm(ref))
+        bound = 2e-3 * math.sqrt(self.wl.k) * float(np.abs(xs).max()) * float(np.abs(ws).max())
+        if not (rel <= 1e-3 and float(np.abs(err).max()) <= bound):
+            raise SystemExit(f"bench output fails parity on sampled rows: rel-L2 {rel:.3e}")
+        return rel
+
+
+def cpu_baseline(wl: workloads.Workload, m: int, nbytes: int) -> dict:
+    """The oracle (unpack + dequant + fp64 product) on the same matrix, on host cores."""
+    import oracle as o
+    w, x = workloads.make_workload(wl)
+    codes, params = o.quantize_pack(w, wl.scheme, wl.group)   # offline for both sides
+    xs = x[:m]
+    ref = o.gemv_ref if wl.path == "gemv" else o.gemm_ref
+
+    def run():
+        wdq = o.dequant_packed(codes, params, wl.scheme, wl.group, wl.k)
+        return ref(xs, wdq)
+
+    run()
+    times = []
+    budget = time.perf_counter() + 30.0
+    for _ in range(5):
+        t = time.perf_counter()
+        run()
+        times.append(time.perf_counter() - t)
+        if time.perf_counter() > budget:
+            break
+    med = statistics.median(times)
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:  # threadpoolctl missing: report the pool size numpy was built with
+        blas = os.cpu_count() or 1
+    return {"value": round(nbytes / med / 1e9, 4), "unit": "GB/s", "cores": int(blas),
+            "kind": "oracle",
+            "sample": (f"whole {wl.name} matrix, M={m}: NumPy unpack + dequant + fp64 product, "
+                       f"median of {len(times)} runs after 1 warm-up ({med * 1e3:.0f} ms each); "
+                       f"elementwise steps single-threaded, product on {blas} BLAS threads")}
+
+
+def traffic_for(name: str, m: int):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if the kernel is unchanged."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{name}_m{m}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def report_all(uq, steps: int, warmup: int, path: str | None) -> None:
+    rows = ["| workload | path | M | weight MB | us/launch | weight GB/s | % HBM | TFLOP/s | % bf16 MFMA |",
+            "|---|---|---|---|---|---|---|---|---|"]
+    for name, wl in workloads.WORKLOADS.items():
+        for m in wl.ms:
+            st = Setup(uq, wl, m, None)
+            ms, _ = st.time(steps, warmup)
+            st.check_sample()
+            gbs = st.bytes / (ms * 1e-3) / 1e9
+            tfl = 2.0 * m * wl.k * wl.n / (ms * 1e-3) / 1e12
+            mfma = f"{100 * tfl / BF16_PEAK_TFLOPS:.1f}" if wl.path == "gemm" else "-"
+            rows.append(f"| {name} | {wl.path} | {m} | {st.bytes / 1e6:.2f} | {ms * 1e3:.2f} | "
+                        f"{gbs:.0f} | {100 * gbs / HBM_PEAK_GBS:.1f} | {tfl:.2f} | {mfma} |")
+            log(rows[-1])
+            del st
+    text = "\n".join(rows) + "\n"
+    log(text)
+    if path:
+        with open(path, "w") as f:
+            f.write(text)
+
+
+def main() -> None:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--workload", default=workloads.HEADLINE, choices=list(workloads.WORKLOADS))
+    ap.add_argument("--m", type=int, default=None)
+    ap.add_argument("--rotate", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--all", action="store_true", help="also time every workload (markdown)")
+    ap.add_argument("--report", default=None)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        raise SystemExit("bench.py measures one GPU: this build has no multi-GPU path "
+                         "(the sharding plan is documented, not built); run with --gpus 1")
+    import torch
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a ROCm GPU")
+    import gemm_group_wise_amd as uq
+
+    wl = workloads.WORKLOADS[args.workload]
+    m = args.m or wl.ms[0]
+    st = Setup(uq, wl, m, args.rotate)
+    torch.cuda.synchronize()
+    ms, eager_ms = st.time(args.steps, args.warmup)
+    rel = st.check_sample()
+    gbs = st.bytes / (ms * 1e-3) / 1e9
+    log(f"{wl.name} m={m}: {ms * 1e3:.3f} us/launch (graph), {eager_ms * 1e3:.3f} us/launch (eager), "
+        f"{gbs:.1f} GB/s, rotate={st.rotate}, sampled rel-L2 {rel:.2e}")
+
+    out = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16" if wl.path == "gemv" else "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name} {wl.path} m={m}", "scheme": wl.scheme, "group": wl.group,
+                   "m": m, "k": wl.k, "n": wl.n, "weight_bytes": st.bytes, "rotated_copies": st.rotate,
+                   "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+                   "tflops": round(2.0 * m * wl.k * wl.n / (ms * 1e-3) / 1e12, 3),
+                   "tokens_per_s_one_layer": round(m / (ms * 1e-3), 1)},
+    }
+    if wl.path == "gemv":
+        out["roofline"] = {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic_for(wl.name, m)}
+    else:
+        tfl = 2.0 * m * wl.k * wl.n / (ms * 1e-3) / 1e12
+        out["roofline"] = {"bound": "mfma", "achieved": round(tfl, 3), "peak": BF16_PEAK_TFLOPS,
+                           "unit": "TFLOP/s", "frac": round(tfl / BF16_PEAK_TFLOPS, 4),
+                           "traffic": traffic_for(wl.name, m)}
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host (cpu_baseline) ...")
+        out["cpu_baseline"] = cpu_baseline(wl, m, st.bytes)
+    del st
+    if args.all:
+        report_all(uq, args.steps, args.warmup, args.report)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,11 @@
+"""gemm_group_wise_amd -- fused group-wise dequant + GEMV/GEMM for MI355X (gfx950).
+
+The compute lives in ``libuq.so`` (HIP kernels behind the C ABI of
+``include/uq.h``); this package is its thin Python binding.  Importing it
+without a built library raises ImportError.
+"""
+from ._binding import (  # noqa: F401
+    BITS, EXPORTS, GEMM_MAX_M, GEMV_MAX_M, LIB_PATH, SCHEMES, Layout, UQError,
+    layout, raw_call, uq_dequant, uq_gemm, uq_gemv, uq_nf4_codebook, uq_pack_weights,
+    uq_packed_size, uq_status_str,
+)

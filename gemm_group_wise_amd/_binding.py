@@ -1,0 +1,141 @@
+"""ctypes binding of libuq (include/uq.h).  Argument marshalling only.
+
+Device buffers are passed as integers or as objects with ``data_ptr()``
+(torch tensors); streams as integers or objects with ``cuda_stream``.  When no
+stream is given the current torch stream is used.  Every non-OK status raises
+:class:`UQError`.  If the library is not built, importing this module raises:
+there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libuq.so")
+
+SCHEMES = {"int2": 1, "int4": 2, "int8": 3, "nf4": 4}
+BITS = {"int2": 2, "int4": 4, "int8": 8, "nf4": 4}
+GEMV_MAX_M = 8
+GEMM_MAX_M = 65536
+
+STATUS = {0: "UQ_OK", 1: "UQ_ERR_NULL", 2: "UQ_ERR_SHAPE", 3: "UQ_ERR_UNSUPPORTED",
+          4: "UQ_ERR_ALIGN", 5: "UQ_ERR_RANGE", 6: "UQ_ERR_HIP"}
+
+
+class UQError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        self.code = code
+        self.name = STATUS.get(code, f"status {code}")
+        super().__init__(f"{fn} failed: {self.name}")
+
+
+class Layout(ctypes.Structure):
+    _fields_ = [("scheme", ctypes.c_int32), ("group", ctypes.c_int32),
+                ("n", ctypes.c_int64), ("k", ctypes.c_int64)]
+
+    def __repr__(self):
+        return f"Layout(scheme={self.scheme}, group={self.group}, n={self.n}, k={self.k})"
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                      "(or python -m gemm_group_wise_amd.build)")
+_lib = ctypes.CDLL(LIB_PATH)
+
+_P = ctypes.c_void_p
+_L = ctypes.POINTER(Layout)
+_lib.uq_packed_size.argtypes = [_L, ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]
+_lib.uq_pack_weights.argtypes = [_L, _P, _P, _P]
+_lib.uq_gemv.argtypes = [_L, _P, _P, _P, _P, ctypes.c_int64, _P]
+_lib.uq_gemm.argtypes = [_L, _P, _P, _P, _P, ctypes.c_int64, _P]
+_lib.uq_dequant.argtypes = [_L, _P, _P, _P, _P]
+_lib.uq_nf4_codebook.argtypes = [_P]
+_lib.uq_status_str.argtypes = [ctypes.c_int]
+_lib.uq_status_str.restype = ctypes.c_char_p
+for _fn in ("uq_packed_size", "uq_pack_weights", "uq_gemv", "uq_gemm", "uq_dequant",
+            "uq_nf4_codebook"):
+    getattr(_lib, _fn).restype = ctypes.c_int
+
+EXPORTS = ("uq_packed_size", "uq_pack_weights", "uq_gemv", "uq_gemm", "uq_dequant",
+           "uq_nf4_codebook", "uq_status_str")
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise UQError(fn, status)
+
+
+def _ptr(obj) -> int | None:
+    if obj is None:
+        return None
+    if isinstance(obj, int):
+        return obj
+    if hasattr(obj, "data_ptr"):
+        return obj.data_ptr()
+    raise TypeError(f"expected a device pointer (int) or a tensor, got {type(obj)!r}")
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def layout(scheme: str | int, group: int, n: int, k: int) -> Layout:
+    s = SCHEMES[scheme] if isinstance(scheme, str) else int(scheme)
+    return Layout(s, group, n, k)
+
+
+def uq_packed_size(lay: Layout) -> tuple[int, int]:
+    cb, pb = ctypes.c_size_t(), ctypes.c_size_t()
+    _check("uq_packed_size", _lib.uq_packed_size(ctypes.byref(lay), ctypes.byref(cb), ctypes.byref(pb)))
+    return cb.value, pb.value
+
+
+def uq_pack_weights(lay: Layout, w: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Quantize + pack a host fp32 [n, k] matrix; returns (codes uint8, params uint16)."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    if w.shape != (lay.n, lay.k):
+        raise ValueError(f"w has shape {w.shape}, layout wants {(lay.n, lay.k)}")
+    cb, pb = uq_packed_size(lay)
+    codes = np.empty((lay.n, cb // lay.n), dtype=np.uint8)
+    params = np.empty(pb // 2, dtype=np.uint16)
+    _check("uq_pack_weights", _lib.uq_pack_weights(ctypes.byref(lay), w.ctypes.data,
+                                                  codes.ctypes.data, params.ctypes.data))
+    return codes, params.reshape(lay.n, -1)
+
+
+def uq_gemv(lay: Layout, codes, params, x, y, m: int, stream=None) -> None:
+    _check("uq_gemv", _lib.uq_gemv(ctypes.byref(lay), _ptr(codes), _ptr(params), _ptr(x), _ptr(y),
+                                   int(m), _stream(stream)))
+
+
+def uq_gemm(lay: Layout, codes, params, x, y, m: int, stream=None) -> None:
+    _check("uq_gemm", _lib.uq_gemm(ctypes.byref(lay), _ptr(codes), _ptr(params), _ptr(x), _ptr(y),
+                                   int(m), _stream(stream)))
+
+
+def uq_dequant(lay: Layout, codes, params, w, stream=None) -> None:
+    _check("uq_dequant", _lib.uq_dequant(ctypes.byref(lay), _ptr(codes), _ptr(params), _ptr(w),
+                                         _stream(stream)))
+
+
+def uq_nf4_codebook() -> np.ndarray:
+    out = np.empty(16, dtype=np.float32)
+    _check("uq_nf4_codebook", _lib.uq_nf4_codebook(out.ctypes.data))
+    return out
+
+
+def uq_status_str(code: int) -> str:
+    return _lib.uq_status_str(int(code)).decode()
+
+
+def raw_call(name: str, *args) -> int:
+    """Call an entry point with raw ctypes arguments and return its status (tests of error paths)."""
+    return getattr(_lib, name)(*args)

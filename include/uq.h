@@ -1,0 +1,140 @@
+/*
+ * uq.h -- C ABI of libuq: group-wise weight quantization and fused
+ * dequant-GEMV / dequant-GEMM for AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow the "Ultra LLM Engine" page:
+ *   - Core Components > Quantization (scheme table): group-wise asymmetric
+ *     uniform INT-2/4/8 ("int") and NormalFloat4 with the QLoRA codebook
+ *     ("nf4"); codes are packed several to a byte and come with matching
+ *     dequantizers.
+ *   - Core Components > Fused Kernels: a fused dequantized-weight GEMV for
+ *     single-token decode and a fused dequantized-weight GEMM for batched
+ *     decode.
+ *   - Core Components > Quantized Model: linear layers keep their weights
+ *     quantized (QuantLinear) and feed these products.
+ *
+ * Computation: y[m, n] = sum_k x[m, k] * w'[n, k], where w' is the
+ * dequantized weight, x is fp16 and y is fp32 (fp32 accumulation).
+ *
+ * Arithmetic fixed by this library (the page states none of it):
+ *   INT-N (b bits, qmax = 2^b - 1), per row n and group g of G consecutive k:
+ *     s = fp16(fp32(fp32(max - min) / qmax)), z = fp16(min)      (RNE)
+ *     q = clamp(rint((w - z) / s) in fp64, 0, qmax); q = 0 when s == 0
+ *     w' = fp32(q * s + z)              (one rounding; equals one fp32 FMA)
+ *   NF4 (G = 64): a = fp16(max |w|); q = nearest codebook entry to w / a
+ *     (fp64; a value on a midpoint takes the lower index; a == 0 gives q = 7);
+ *     w' = fp32(C[q] * a).
+ *
+ * Packed layout (what uq_pack_weights writes and the kernels read):
+ *   codes  : uint8 [n][k * b / 8], row-major.  INT4/NF4: byte j holds code
+ *            2j in bits 0-3 and code 2j+1 in bits 4-7.  INT2: byte j holds
+ *            code 4j+i in bits 2i..2i+1.  INT8: one code per byte.
+ *   params : INT-N: uint16 [n][k / G][2] = fp16 bit patterns (s, z)
+ *            interleaved per group (as uint32 little-endian: s | z << 16).
+ *            NF4:   uint16 [n][k / 64] = fp16 absmax bit patterns.
+ *
+ * Conventions for every call:
+ *   - Validation runs before any HIP call.  On any status other than UQ_OK
+ *     nothing was launched and no output was written.
+ *   - The caller owns every buffer.  The library allocates no memory, keeps
+ *     no mutable state, and never synchronizes: device calls are enqueued on
+ *     `stream` (a hipStream_t; NULL means the null stream) and return at
+ *     once.  Faults inside a kernel surface at the caller's next
+ *     synchronization.
+ *   - Outputs are overwritten, never accumulated into.
+ *   - All functions are thread-safe (no shared state).
+ */
+#ifndef UQ_H
+#define UQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum uq_status {
+  UQ_OK = 0,
+  UQ_ERR_NULL = 1,        /* a required pointer is NULL                      */
+  UQ_ERR_SHAPE = 2,       /* n, k, m or group out of range, or k not a whole
+                             number of groups and 16-byte code chunks        */
+  UQ_ERR_UNSUPPORTED = 3, /* unknown scheme or unsupported (scheme, group)   */
+  UQ_ERR_ALIGN = 4,       /* a device pointer is not suitably aligned        */
+  UQ_ERR_RANGE = 5,       /* a weight is NaN, infinite, or |w| > 65504       */
+  UQ_ERR_HIP = 6          /* the HIP runtime rejected a kernel launch        */
+} uq_status;
+
+typedef enum uq_scheme {
+  UQ_INT2 = 1, /* groups 16, 32, 64, 128 */
+  UQ_INT4 = 2, /* groups 32, 64, 128     */
+  UQ_INT8 = 3, /* groups 64, 128         */
+  UQ_NF4 = 4   /* group 64               */
+} uq_scheme;
+
+/* Shape and format of one quantized weight matrix W[n][k] (out x in). */
+typedef struct uq_layout {
+  int32_t scheme; /* a uq_scheme value                                   */
+  int32_t group;  /* G: consecutive k sharing one (s, z) or one absmax   */
+  int64_t n;      /* rows of W = output features, 1 .. 2^31 - 1          */
+  int64_t k;      /* columns of W = input features; a multiple of G and
+                     of the 16-byte chunk (128 / bits codes), <= 2^24    */
+} uq_layout;
+
+/* Limits. */
+#define UQ_GEMV_MAX_M 8     /* uq_gemv serves 1..8 activation rows        */
+#define UQ_GEMM_MAX_M 65536 /* uq_gemm serves 1..65536 activation rows    */
+
+/* Sizes in bytes of the two packed arrays for `layout`.
+ * Returns UQ_ERR_NULL / UQ_ERR_UNSUPPORTED / UQ_ERR_SHAPE on a bad layout. */
+uq_status uq_packed_size(const uq_layout* layout, size_t* code_bytes,
+                         size_t* param_bytes);
+
+/* Quantize and pack W on the host (Core Components > Quantization).
+ *   w      : host fp32 [n][k] row-major, finite with |w| <= 65504
+ *   codes  : host, uq_packed_size code_bytes, written
+ *   params : host, uq_packed_size param_bytes, written (uint16 fp16 bits)
+ * Deterministic and pure.  UQ_ERR_RANGE if any weight is out of range
+ * (checked before anything is written). */
+uq_status uq_pack_weights(const uq_layout* layout, const float* w,
+                          uint8_t* codes, uint16_t* params);
+
+/* Fused dequant + GEMV for single-token and small-batch decode
+ * (Core Components > Fused Kernels, GEMV during single-token decode):
+ *   y[m][n] = sum_k x[m][k] * w'[n][k]   for 1 <= m <= UQ_GEMV_MAX_M
+ *   codes, params : device, as packed by uq_pack_weights, 16-byte aligned
+ *   x : device fp16 [m][k] row-major (uint16 bit patterns), 16-byte aligned
+ *   y : device fp32 [m][n] row-major, 16-byte aligned, overwritten
+ * The products are formed from fp16 activations with fp32 accumulation;
+ * results match fp64 x . w'^T to within rounding (the NF4 codebook enters
+ * the products rounded to fp16). */
+uq_status uq_gemv(const uq_layout* layout, const void* codes,
+                  const void* params, const uint16_t* x, float* y, int64_t m,
+                  void* stream);
+
+/* Fused dequant + GEMM on the bf16 matrix cores for batched decode and
+ * prefill (Core Components > Fused Kernels, GEMM during batched decode):
+ *   y[m][n] = sum_k bf16(x[m][k]) * bf16(w'[n][k])  for 1 <= m <= UQ_GEMM_MAX_M
+ * Both casts round to nearest even; products accumulate in fp32.
+ * Arguments as for uq_gemv. */
+uq_status uq_gemm(const uq_layout* layout, const void* codes,
+                  const void* params, const uint16_t* x, float* y, int64_t m,
+                  void* stream);
+
+/* Dequantize the whole matrix (the matching dequantizer of
+ * Core Components > Quantization):  w[n][k] = w' exactly (bit for bit).
+ *   w : device fp32 [n][k] row-major, 16-byte aligned, overwritten */
+uq_status uq_dequant(const uq_layout* layout, const void* codes,
+                     const void* params, float* w, void* stream);
+
+/* The 16 NF4 codebook entries (fp32) the library uses; host call. */
+uq_status uq_nf4_codebook(float out[16]);
+
+/* Static, NUL-terminated name of a status code ("UQ_OK", ...). */
+const char* uq_status_str(uq_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* UQ_H */

@@ -1,0 +1,75 @@
+"""Helpers for the GPU parity tests: device buffers, guard bands, and the gate."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import oracle as o
+
+REL_L2_MAX = 1e-3
+ABS_COEF = 2e-3
+GUARD = 64          # fp32 guard elements on each side of an output (256 B keeps 16-byte alignment)
+SENTINEL = np.float32(-1.2345678e30)
+
+
+def note(msg: str) -> None:
+    """Name the case about to run on the GPU (flushed, so it survives a crash)."""
+    print(f"[gpu] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def dev(arr: np.ndarray):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(arr)).to("cuda:0")
+
+
+class Guarded:
+    """An fp32 output of `count` elements with sentinel guard bands on both sides."""
+
+    def __init__(self, count: int):
+        import torch
+        self.count = count
+        self.buf = torch.full((count + 2 * GUARD,), float(SENTINEL), dtype=torch.float32, device="cuda:0")
+
+    @property
+    def ptr(self) -> int:
+        return self.buf.data_ptr() + GUARD * 4
+
+    def result(self) -> np.ndarray:
+        import torch
+        torch.cuda.synchronize()
+        h = self.buf.cpu().numpy()
+        assert (h[:GUARD] == SENTINEL).all(), "write before the output"
+        assert (h[GUARD + self.count:] == SENTINEL).all(), "write past the output"
+        out = h[GUARD:GUARD + self.count]
+        assert not (out == SENTINEL).any(), "output element left unwritten"
+        return out
+
+
+def packed_on_device(lib, scheme, group, w):
+    """Pack with the library's host packer and copy to the GPU."""
+    lay = lib.layout(scheme, group, w.shape[0], w.shape[1])
+    codes, params = lib.uq_pack_weights(lay, w)
+    return lay, dev(codes), dev(params)
+
+
+def oracle_dequant(w, scheme, group):
+    codes, params = o.quantize_pack(w, scheme, group)
+    return o.dequant_packed(codes, params, scheme, group, w.shape[1])
+
+
+def gate(y, yref, xs, wdq, label=""):
+    """rel-L2 <= 1e-3 and max |y - yref| <= 2e-3 * sqrt(K) * max|x| * max|w'|."""
+    y = np.asarray(y, dtype=np.float64)
+    yref = np.asarray(yref, dtype=np.float64)
+    assert y.shape == yref.shape, (y.shape, yref.shape)
+    assert np.isfinite(y).all(), f"{label}: non-finite output"
+    k = wdq.shape[1]
+    err = y - yref
+    rel = float(np.linalg.norm(err) / max(np.linalg.norm(yref), 1e-300))
+    maxabs = float(np.abs(err).max()) if err.size else 0.0
+    bound = ABS_COEF * np.sqrt(k) * float(np.abs(xs).max()) * float(np.abs(wdq).max())
+    assert rel <= REL_L2_MAX, f"{label}: rel-L2 {rel:.3e} > {REL_L2_MAX}"
+    assert maxabs <= bound, f"{label}: max abs {maxabs:.3e} > {bound:.3e}"
+    return rel, maxabs

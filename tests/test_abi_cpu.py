@@ -1,0 +1,173 @@
+"""C ABI on the CPU: exports, host packer vs oracle, and validation error paths.
+
+No test here launches a kernel: every device-side call below is given an
+argument that validation rejects before the first HIP call.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as o
+import workloads
+from tests import pins
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+ALL_LAYOUTS = [("int2", g) for g in (16, 32, 64, 128)] + [("int4", g) for g in (32, 64, 128)] + \
+              [("int8", g) for g in (64, 128)] + [("nf4", 64)]
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "uq.h")).read()
+    return sorted(set(re.findall(r"^(?:uq_status|const char\*)\s+(uq_\w+)\(", text, re.M)))
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = header_functions()
+    assert set(names) == set(lib.EXPORTS), names
+    handle = ctypes.CDLL(lib.LIB_PATH)
+    for name in names:
+        assert hasattr(handle, name), name
+
+
+def test_status_strings(lib):
+    for code, name in lib._binding.STATUS.items():
+        assert lib.uq_status_str(code) == name
+    assert lib.uq_status_str(99) == "UQ_ERR_UNKNOWN"
+
+
+def test_codebook_matches_oracle_derivation(lib):
+    got = lib.uq_nf4_codebook()
+    assert np.array_equal(got.view(np.uint32), o.nf4_codebook().view(np.uint32))
+
+
+@pytest.mark.parametrize("scheme,group", ALL_LAYOUTS)
+def test_packed_size(lib, scheme, group):
+    k = 4 * max(group, 128 // o.BITS[scheme])
+    cb, pb = lib.uq_packed_size(lib.layout(scheme, group, 7, k))
+    assert cb == 7 * k * o.BITS[scheme] // 8
+    assert pb == 7 * (k // group) * (2 if scheme == "nf4" else 4)
+
+
+def test_packer_hand_built_golden(lib):
+    cb = o.nf4_codebook()
+    for case in pins.load_packing_cases():
+        w = pins.build_case_weights(case, cb)
+        lay = lib.layout(case["scheme"], case["group"], case["n"], case["k"])
+        codes, params = lib.uq_pack_weights(lay, w)
+        for r in range(case["n"]):
+            assert codes[r].tobytes() == case["codes"][r], case["name"]
+            assert [int(v) for v in params[r]] == case["params"][r], case["name"]
+
+
+@pytest.mark.parametrize("scheme,group", ALL_LAYOUTS)
+def test_packer_matches_oracle_random(lib, scheme, group):
+    for seed, outliers in ((0, False), (1, True)):
+        k = 4 * max(group, 128 // o.BITS[scheme])
+        w, _ = workloads.make_random(37, k, 1, seed=seed, outliers=outliers)
+        codes, params = lib.uq_pack_weights(lib.layout(scheme, group, 37, k), w)
+        rc, rp = o.quantize_pack(w, scheme, group)
+        assert np.array_equal(codes, rc)
+        assert np.array_equal(params.reshape(-1), rp.reshape(-1).view(np.uint16))
+
+
+@pytest.mark.parametrize("scheme,group", ALL_LAYOUTS)
+def test_packer_matches_oracle_edge_values(lib, scheme, group):
+    """Constant groups, zero groups, exact midpoints, extremes and fp16 subnormal scales."""
+    k = 4 * max(group, 128 // o.BITS[scheme])
+    rng = np.random.default_rng(5)
+    w = (rng.standard_normal((8, k)) * 0.02).astype(np.float32)
+    w[0] = 0.0                                   # zero row
+    w[1] = 0.37                                  # constant row
+    w[2] = rng.standard_normal(k).astype(np.float32) * 65000.0 / 5  # large range
+    w[2, 0] = 65504.0
+    w[2, 1] = -65504.0
+    w[3] = rng.standard_normal(k).astype(np.float32) * 1e-6         # subnormal fp16 scales
+    w[4] = np.float32(1e-3) * (np.arange(k) % 7).astype(np.float32)  # many ties
+    w[5, ::2] = -w[5, 1::2]                      # symmetric values
+    cb = o.nf4_codebook()
+    w[6] = np.resize(cb, k)                      # exact codebook entries (a = 1)
+    w[7] = np.resize((cb[:-1] + cb[1:]) / 2, k)  # near-midpoints
+    w[7, 0] = 1.0
+    w = np.clip(w, -65504, 65504).astype(np.float32)
+    codes, params = lib.uq_pack_weights(lib.layout(scheme, group, 8, k), w)
+    rc, rp = o.quantize_pack(w, scheme, group)
+    assert np.array_equal(codes, rc)
+    assert np.array_equal(params.reshape(-1), rp.reshape(-1).view(np.uint16))
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", list(workloads.WORKLOADS))
+def test_packer_matches_oracle_full_configs(lib, name):
+    wl = workloads.WORKLOADS[name]
+    w, _ = workloads.make_workload(wl)
+    codes, params = lib.uq_pack_weights(lib.layout(wl.scheme, wl.group, wl.n, wl.k), w)
+    rc, rp = o.quantize_pack(w, wl.scheme, wl.group)
+    assert np.array_equal(codes, rc)
+    assert np.array_equal(params.reshape(-1), rp.reshape(-1).view(np.uint16))
+
+
+# ---------------------------------------------------------------------------
+# Validation (no HIP call is reached)
+# ---------------------------------------------------------------------------
+def test_layout_errors(lib):
+    bad = [
+        (lib.layout(9, 64, 4, 256), "UQ_ERR_UNSUPPORTED"),
+        (lib.layout("int4", 16, 4, 256), "UQ_ERR_UNSUPPORTED"),
+        (lib.layout("int8", 32, 4, 256), "UQ_ERR_UNSUPPORTED"),
+        (lib.layout("nf4", 32, 4, 256), "UQ_ERR_UNSUPPORTED"),
+        (lib.layout("int4", 64, 0, 256), "UQ_ERR_SHAPE"),
+        (lib.layout("int4", 64, 4, 96), "UQ_ERR_SHAPE"),       # k % G
+        (lib.layout("int2", 16, 4, 48), "UQ_ERR_SHAPE"),       # not whole 16-byte chunks
+        (lib.layout("int4", 64, 4, (1 << 24) + 64), "UQ_ERR_SHAPE"),
+        (lib.layout("int4", 64, 1 << 31, 256), "UQ_ERR_SHAPE"),
+    ]
+    for lay, name in bad:
+        with pytest.raises(lib.UQError) as e:
+            lib.uq_packed_size(lay)
+        assert e.value.name == name, lay
+    assert lib.raw_call("uq_packed_size", None, None, None) == 1
+
+
+def test_pack_rejects_non_finite_and_huge(lib):
+    lay = lib.layout("int4", 32, 2, 64)
+    for bad in (np.nan, np.inf, -np.inf, 65505.0, -70000.0):
+        w = np.zeros((2, 64), dtype=np.float32)
+        w[1, 3] = bad
+        with pytest.raises(lib.UQError) as e:
+            lib.uq_pack_weights(lay, w)
+        assert e.value.name == "UQ_ERR_RANGE"
+    w = np.zeros((2, 64), dtype=np.float32)
+    assert lib.raw_call("uq_pack_weights", ctypes.byref(lay), None, None, None) == 1
+    assert lib.raw_call("uq_pack_weights", ctypes.byref(lay), w.ctypes.data, None, None) == 1
+
+
+@pytest.mark.parametrize("fn", ["uq_gemv", "uq_gemm"])
+def test_product_validation(lib, fn):
+    lay = lib.layout("int4", 64, 128, 256)
+    A = 1 << 20  # fake, 16-byte aligned addresses: never dereferenced
+    s = ctypes.byref
+    assert lib.raw_call(fn, None, A, A, A, A, 1, None) == 1                      # null layout
+    assert lib.raw_call(fn, s(lay), None, A, A, A, 1, None) == 1                 # null codes
+    assert lib.raw_call(fn, s(lay), A, A, A, None, 1, None) == 1                 # null y
+    assert lib.raw_call(fn, s(lay), A, A, A, A, 0, None) == 2                    # m = 0
+    mmax = 8 if fn == "uq_gemv" else 65536
+    assert lib.raw_call(fn, s(lay), A, A, A, A, mmax + 1, None) == 2             # m too big
+    assert lib.raw_call(fn, s(lay), A + 4, A, A, A, 1, None) == 4                # misaligned
+    assert lib.raw_call(fn, s(lay), A, A, A + 2, A, 1, None) == 4
+    assert lib.raw_call(fn, s(lay), A, A, A, A + 8, 1, None) == 4
+    bad = lib.layout("int4", 64, 128, 96)
+    assert lib.raw_call(fn, s(bad), A, A, A, A, 1, None) == 2
+    badg = lib.layout("int4", 16, 128, 256)
+    assert lib.raw_call(fn, s(badg), A, A, A, A, 1, None) == 3
+
+
+def test_dequant_validation(lib):
+    lay = lib.layout("nf4", 64, 16, 128)
+    A = 1 << 20
+    s = ctypes.byref
+    assert lib.raw_call("uq_dequant", s(lay), None, A, A, None) == 1
+    assert lib.raw_call("uq_dequant", s(lay), A, A, A + 4, None) == 4
+    assert lib.raw_call("uq_dequant", s(lib.layout("nf4", 128, 16, 128)), A, A, A, None) == 3

@@ -1,0 +1,230 @@
+"""GPU parity: the HIP path through the C ABI against the oracle (MI355X only).
+
+Dequantized weights must match bit for bit; products must pass the gate
+(rel-L2 <= 1e-3, max abs <= 2e-3 * sqrt(K) * max|x| * max|w'|), and the
+one-hot cases must reproduce w' exactly.
+"""
+import numpy as np
+import pytest
+
+import oracle as o
+import workloads
+from tests.gpu_util import Guarded, dev, gate, note, oracle_dequant, packed_on_device
+
+pytestmark = pytest.mark.gpu
+
+ALL_LAYOUTS = [("int2", g) for g in (16, 32, 64, 128)] + [("int4", g) for g in (32, 64, 128)] + \
+              [("int8", g) for g in (64, 128)] + [("nf4", 64)]
+CW = {"int2": 64, "int4": 32, "int8": 16, "nf4": 32}
+
+
+def small_k(scheme, group, mult=4):
+    return mult * max(group, CW[scheme])
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a ROCm GPU (gfx950)"
+    props = torch.cuda.get_device_properties(0)
+    note(f"device: {props.name} {getattr(props, 'gcnArchName', '')}")
+    yield
+    torch.cuda.synchronize()
+
+
+def run_gemv(lib, lay, codes, params, x, m):
+    y = Guarded(m * lay.n)
+    lib.uq_gemv(lay, codes, params, dev(x[:m]), y.ptr, m)
+    return y.result().reshape(m, lay.n)
+
+
+def run_gemm(lib, lay, codes, params, x, m):
+    y = Guarded(m * lay.n)
+    lib.uq_gemm(lay, codes, params, dev(x[:m]), y.ptr, m)
+    return y.result().reshape(m, lay.n)
+
+
+# ---------------------------------------------------------------------------
+# Dequant: bit-exact
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("scheme,group", ALL_LAYOUTS)
+def test_dequant_bit_exact(lib, scheme, group):
+    for n, k, seed in ((37, small_k(scheme, group), 0), (5, 4096, 1), (130, small_k(scheme, group, 2), 2)):
+        note(f"dequant {scheme} G{group} n={n} k={k}")
+        w, _ = workloads.make_random(n, k, 1, seed=seed, outliers=True)
+        lay, codes, params = packed_on_device(lib, scheme, group, w)
+        out = Guarded(n * k)
+        lib.uq_dequant(lay, codes, params, out.ptr)
+        got = out.result().reshape(n, k)
+        want = oracle_dequant(w, scheme, group)
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), (scheme, group, n, k)
+
+
+# ---------------------------------------------------------------------------
+# GEMV (M <= 8)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("scheme,group", ALL_LAYOUTS)
+def test_gemv_parity_small(lib, scheme, group):
+    for n, k, seed in ((37, small_k(scheme, group), 3), (1000, 1024, 4), (17, 4096, 5)):
+        w, x = workloads.make_random(n, k, 8, seed=seed, outliers=True)
+        lay, codes, params = packed_on_device(lib, scheme, group, w)
+        wdq = oracle_dequant(w, scheme, group)
+        for m in (1, 2, 3, 4, 5, 8):
+            note(f"gemv {scheme} G{group} n={n} k={k} m={m}")
+            y = run_gemv(lib, lay, codes, params, x, m)
+            gate(y, o.gemv_ref(x[:m], wdq), x[:m], wdq, f"{scheme} G{group} {n}x{k} m={m}")
+
+
+@pytest.mark.parametrize("scheme,group", [l for l in ALL_LAYOUTS if l[0] != "nf4"])
+def test_gemv_one_hot_bit_exact(lib, scheme, group):
+    """x = e_k reproduces column k of w' exactly (the scale times an integer code is exact)."""
+    n, k = 45, small_k(scheme, group)
+    w, _ = workloads.make_random(n, k, 1, seed=6, outliers=True)
+    lay, codes, params = packed_on_device(lib, scheme, group, w)
+    wdq = oracle_dequant(w, scheme, group)
+    cols = [0, 1, k // 2 + 3, k - 1, 5, 17, 31 % k, k - 2]
+    x = np.zeros((8, k), dtype=np.float16)
+    for i, c in enumerate(cols):
+        x[i, c] = 1.0
+    for m in (1, 3, 8):
+        note(f"gemv one-hot {scheme} G{group} m={m}")
+        y = run_gemv(lib, lay, codes, params, x, m)
+        want = np.stack([wdq[:, c] for c in cols[:m]])
+        assert np.array_equal(y.view(np.uint32), want.view(np.uint32)), (scheme, group, m)
+
+
+def test_gemv_one_hot_nf4(lib):
+    """NF4 products use the codebook rounded to fp16: within 2^-11 relative of w'."""
+    n, k = 45, 256
+    w, _ = workloads.make_random(n, k, 1, seed=7)
+    lay, codes, params = packed_on_device(lib, "nf4", 64, w)
+    wdq = oracle_dequant(w, "nf4", 64)
+    x = np.zeros((4, k), dtype=np.float16)
+    cols = [0, 63, 64, 255]
+    for i, c in enumerate(cols):
+        x[i, c] = 1.0
+    note("gemv one-hot nf4")
+    y = run_gemv(lib, lay, codes, params, x, 4)
+    want = np.stack([wdq[:, c] for c in cols]).astype(np.float64)
+    assert (np.abs(y - want) <= np.abs(want) * 2.0 ** -11 + 1e-30).all()
+
+
+def test_gemv_batched_equivalence(lib):
+    """Row i of an M-row GEMV equals the single-row GEMV of x[i], bit for bit."""
+    for scheme, group in (("int4", 64), ("int2", 16), ("int8", 128), ("nf4", 64)):
+        w, x = workloads.make_random(300, 2048, 8, seed=8, outliers=True)
+        lay, codes, params = packed_on_device(lib, scheme, group, w)
+        ys = [run_gemv(lib, lay, codes, params, x[i:i + 1], 1)[0] for i in range(8)]
+        for m in (2, 4, 8):
+            note(f"gemv batched equivalence {scheme} G{group} m={m}")
+            y = run_gemv(lib, lay, codes, params, x, m)
+            for i in range(m):
+                assert np.array_equal(y[i], ys[i]), (scheme, group, m, i)
+
+
+@pytest.mark.parametrize("m,k", [(1, 20480), (8, 8192), (4, 4224)])
+def test_gemv_k_blocks(lib, m, k):
+    """K larger than one LDS block of activations, with a ragged last block."""
+    w, x = workloads.make_random(70, k, m, seed=9)
+    for scheme, group in (("int4", 128), ("int2", 64), ("nf4", 64), ("int8", 64)):
+        if k % max(group, CW[scheme]):
+            continue
+        note(f"gemv k-blocks {scheme} G{group} m={m} k={k}")
+        lay, codes, params = packed_on_device(lib, scheme, group, w)
+        wdq = oracle_dequant(w, scheme, group)
+        y = run_gemv(lib, lay, codes, params, x, m)
+        gate(y, o.gemv_ref(x[:m], wdq), x[:m], wdq, f"k-blocks {scheme} m={m} k={k}")
+
+
+def test_gemv_on_side_stream(lib):
+    import torch
+    w, x = workloads.make_random(64, 512, 1, seed=10)
+    lay, codes, params = packed_on_device(lib, "int4", 32, w)
+    wdq = oracle_dequant(w, "int4", 32)
+    s = torch.cuda.Stream()
+    xd = dev(x)
+    y = Guarded(64)
+    torch.cuda.synchronize()
+    note("gemv on a side stream")
+    lib.uq_gemv(lay, codes, params, xd, y.ptr, 1, stream=s)
+    s.synchronize()
+    gate(y.result().reshape(1, 64), o.gemv_ref(x, wdq), x, wdq, "side stream")
+
+
+# ---------------------------------------------------------------------------
+# GEMM (bf16 matrix cores)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("scheme,group", ALL_LAYOUTS)
+def test_gemm_parity_small(lib, scheme, group):
+    for n, k, seed in ((100, 512, 11), (77, small_k(scheme, group), 12)):
+        w, x = workloads.make_random(n, k, 130, seed=seed, outliers=True)
+        lay, codes, params = packed_on_device(lib, scheme, group, w)
+        wdq = oracle_dequant(w, scheme, group)
+        for m in (1, 15, 16, 17, 40, 64, 130):
+            note(f"gemm {scheme} G{group} n={n} k={k} m={m}")
+            y = run_gemm(lib, lay, codes, params, x, m)
+            xb = o.bf16_rne(x[:m].astype(np.float32))
+            gate(y, o.gemm_ref(x[:m], wdq), xb, o.bf16_rne(wdq), f"gemm {scheme} G{group} m={m}")
+
+
+@pytest.mark.parametrize("scheme,group", ALL_LAYOUTS)
+def test_gemm_identity_bit_exact(lib, scheme, group):
+    """X = I (M = K) returns bf16(w')^T exactly."""
+    n, k = 70, 256
+    w, _ = workloads.make_random(n, k, 1, seed=13, outliers=True)
+    lay, codes, params = packed_on_device(lib, scheme, group, w)
+    wdq = oracle_dequant(w, scheme, group)
+    x = np.eye(k, dtype=np.float16)
+    note(f"gemm identity {scheme} G{group}")
+    y = run_gemm(lib, lay, codes, params, x, k)
+    want = o.bf16_rne(wdq).T
+    assert np.array_equal(y.view(np.uint32), np.ascontiguousarray(want).view(np.uint32))
+
+
+@pytest.mark.parametrize("k", [96, 160, 224])
+def test_gemm_k_tail(lib, k):
+    """K not a multiple of the 128-wide K step."""
+    w, x = workloads.make_random(65, k, 33, seed=14)
+    lay, codes, params = packed_on_device(lib, "int4", 32, w)
+    wdq = oracle_dequant(w, "int4", 32)
+    note(f"gemm k-tail k={k}")
+    y = run_gemm(lib, lay, codes, params, x, 33)
+    gate(y, o.gemm_ref(x, wdq), o.bf16_rne(x.astype(np.float32)), o.bf16_rne(wdq), f"k-tail {k}")
+
+
+def test_gemm_rows_match_gemv(lib):
+    """Batched decode equivalence across paths: GEMM rows agree with GEMV within the gate."""
+    w, x = workloads.make_random(256, 1024, 16, seed=15)
+    lay, codes, params = packed_on_device(lib, "int4", 128, w)
+    wdq = oracle_dequant(w, "int4", 128)
+    note("gemm rows vs gemv")
+    yg = run_gemm(lib, lay, codes, params, x, 16)
+    yv = np.concatenate([run_gemv(lib, lay, codes, params, x[i:i + 8], 8) for i in (0, 8)])
+    gate(yg, yv.astype(np.float64), x, wdq, "gemm vs gemv")
+
+
+# ---------------------------------------------------------------------------
+# Full-size workloads, in the launch configuration the benchmark times
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name", list(workloads.WORKLOADS))
+def test_full_workload(lib, name):
+    wl = workloads.WORKLOADS[name]
+    w, x = workloads.make_workload(wl)
+    lay, codes, params = packed_on_device(lib, wl.scheme, wl.group, w)
+    wdq = oracle_dequant(w, wl.scheme, wl.group)
+    if wl.path == "gemv":
+        note(f"full dequant {name}")
+        out = Guarded(wl.n * wl.k)
+        lib.uq_dequant(lay, codes, params, out.ptr)
+        assert np.array_equal(out.result().view(np.uint32), wdq.reshape(-1).view(np.uint32))
+        del out
+    for m in wl.ms:
+        note(f"full {wl.path} {name} m={m}")
+        if wl.path == "gemv":
+            y = run_gemv(lib, lay, codes, params, x, m)
+            rel, mx = gate(y, o.gemv_ref(x[:m], wdq), x[:m], wdq, f"{name} m={m}")
+        else:
+            y = run_gemm(lib, lay, codes, params, x, m)
+            rel, mx = gate(y, o.gemm_ref(x[:m], wdq), o.bf16_rne(x[:m].astype(np.float32)),
+                           o.bf16_rne(wdq), f"{name} m={m}")
+        note(f"  rel-L2 {rel:.3e}  max-abs {mx:.3e}")
