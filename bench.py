@@ -69,7 +69,7 @@ class Setup:
         if rotate is None:  # > 256 MB Infinity Cache + 32 MB L2
             rotate = max(16, math.ceil(320e6 / self.bytes))
         self.rotate = rotate
-        dc, dp = torch.from_numpy(codes).cuda(), torch.from_numpy(params).cuda()
+        dc, dp = torch.from_numpy(codes).cuda(), torch.from_numpy(params.view(np.int16)).cuda()
         self.codes = [dc] + [dc.clone() for _ in range(rotate - 1)]
         self.params = [dp] + [dp.clone() for _ in range(rotate - 1)]
         self.x = torch.from_numpy(np.ascontiguousarray(self.x_host)).cuda()

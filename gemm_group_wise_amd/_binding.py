@@ -43,6 +43,16 @@ class Layout(ctypes.Structure):
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
                       "(or python -m gemm_group_wise_amd.build)")
+
+# torch ships its own HIP runtime, which its libraries load by the unversioned
+# name libamdhip64.so.  libuq.so asks for libamdhip64.so.7; if it were opened
+# first, the dynamic loader would later map torch's copy as well and the
+# process would run two HIP/HSA runtimes on one device.  Importing torch first
+# lets libuq.so bind to the runtime torch already loaded (same SONAME).
+try:
+    import torch  # noqa: F401
+except ImportError:  # plain C-ABI use without torch
+    torch = None
 _lib = ctypes.CDLL(LIB_PATH)
 
 _P = ctypes.c_void_p

@@ -18,3 +18,11 @@ def lib():
     """The C-ABI library through its Python binding (fails loudly if unbuilt)."""
     import gemm_group_wise_amd as uq
     return uq
+
+
+def pytest_runtest_logreport(report):
+    """With UQ_FAILURE_LOG set, append each failure at once (survives a crash later on)."""
+    path = os.environ.get("UQ_FAILURE_LOG")
+    if path and report.failed:
+        with open(path, "a") as f:
+            f.write(f"=== {report.nodeid} ({report.when})\n{report.longreprtext}\n\n")

@@ -20,8 +20,12 @@ def note(msg: str) -> None:
 
 
 def dev(arr: np.ndarray):
+    """Copy a host array to cuda:0 (uint16 data travels as int16: same bits)."""
     import torch
-    return torch.from_numpy(np.ascontiguousarray(arr)).to("cuda:0")
+    arr = np.ascontiguousarray(arr)
+    if arr.dtype == np.uint16:
+        arr = arr.view(np.int16)
+    return torch.from_numpy(arr).to("cuda:0")
 
 
 class Guarded:

@@ -171,3 +171,16 @@ def test_dequant_validation(lib):
     assert lib.raw_call("uq_dequant", s(lay), None, A, A, None) == 1
     assert lib.raw_call("uq_dequant", s(lay), A, A, A + 4, None) == 4
     assert lib.raw_call("uq_dequant", s(lib.layout("nf4", 128, 16, 128)), A, A, A, None) == 3
+
+
+def test_single_hip_runtime_in_process():
+    """Importing the binding must leave exactly one HIP runtime mapped (torch's)."""
+    import subprocess
+    import sys
+    code = ("import gemm_group_wise_amd\n"
+            "maps = open('/proc/self/maps').read().splitlines()\n"
+            "hip = {l.split()[-1] for l in maps if 'libamdhip64' in l}\n"
+            "hsa = {l.split()[-1] for l in maps if 'libhsa-runtime64' in l}\n"
+            "print(len(hip), len(hsa))\n")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, check=True)
+    assert out.stdout.split() == ["1", "1"], out.stdout
