@@ -192,15 +192,21 @@ def test_gemm_k_tail(lib, k):
     gate(y, o.gemm_ref(x, wdq), o.bf16_rne(x.astype(np.float32)), o.bf16_rne(wdq), f"k-tail {k}")
 
 
-def test_gemm_rows_match_gemv(lib):
-    """Batched decode equivalence across paths: GEMM rows agree with GEMV within the gate."""
-    w, x = workloads.make_random(256, 1024, 16, seed=15)
+def test_gemm_batched_equivalence(lib):
+    """Row i of an M-row GEMM equals the single-row GEMM of x[i], bit for bit.
+
+    (GEMM and GEMV rows are not compared under the gate: the bf16 rounding of
+    w' alone moves the GEMM by ~2e-3 relative to the fp16 GEMV, which is why
+    the GEMM's oracle applies the same bf16 casts.)
+    """
+    w, x = workloads.make_random(200, 1024, 40, seed=15)
     lay, codes, params = packed_on_device(lib, "int4", 128, w)
-    wdq = oracle_dequant(w, "int4", 128)
-    note("gemm rows vs gemv")
-    yg = run_gemm(lib, lay, codes, params, x, 16)
-    yv = np.concatenate([run_gemv(lib, lay, codes, params, x[i:i + 8], 8) for i in (0, 8)])
-    gate(yg, yv.astype(np.float64), x, wdq, "gemm vs gemv")
+    ys = [run_gemm(lib, lay, codes, params, x[i:i + 1], 1)[0] for i in range(40)]
+    for m in (16, 40):
+        note(f"gemm batched equivalence m={m}")
+        y = run_gemm(lib, lay, codes, params, x, m)
+        for i in range(m):
+            assert np.array_equal(y[i], ys[i]), (m, i)
 
 
 # ---------------------------------------------------------------------------
