@@ -32,7 +32,7 @@ import workloads  # noqa: E402
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix cores, published
 METRIC = "dequant-GEMV weight GB/s & % HBM peak, INT4 g64 K=4096 N=11008 M=1"
-KERNEL_SOURCES = ("gemm_group_wise_amd/csrc/gemv.hip", "gemm_group_wise_amd/csrc/gemm.hip",
+KERNEL_SOURCES = ("gemm_group_wise_amd/csrc/gemv_impl.hpp", "gemm_group_wise_amd/csrc/gemm.hip",
                   "gemm_group_wise_amd/csrc/device_common.hpp")
 
 

@@ -22,7 +22,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libuq.so")
 
 ARCH = "gfx950"
-HIP_SOURCES = ["uq_api.hip", "gemv.hip", "gemm.hip", "dequant.hip"]
+HIP_SOURCES = ["uq_api.hip", "gemv.hip", "gemv_int2.hip", "gemv_int4.hip", "gemv_int8.hip",
+               "gemv_nf4.hip", "gemm.hip", "dequant.hip"]
 CXX_SOURCES = ["uq_pack.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

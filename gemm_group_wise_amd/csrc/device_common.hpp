@@ -61,29 +61,76 @@ template <> struct Slot<UQ_NF4> {
   static __host__ __device__ constexpr float inv_cls(int) { return 1.0f; }
 };
 
-template <int S> __device__ __forceinline__ void unpack_pairs(uint32_t w, f16x2 (&p)[Fmt<S>::PPD]);
-
-template <> __device__ __forceinline__ void unpack_pairs<UQ_INT4>(uint32_t w, f16x2 (&p)[4]) {
-  const uint32_t w8 = w >> 8;
-  p[0] = as_h2((w & 0x000F000Fu) | kMagic2);
-  p[1] = as_h2((w8 & 0x000F000Fu) | kMagic2);
-  p[2] = as_h2((w & 0x00F000F0u) | kMagic2);
-  p[3] = as_h2((w8 & 0x00F000F0u) | kMagic2);
+// (a & mask) | orv in one v_and_or_b32.  gfx9 VOP3 encodings take no literal
+// and at most one SGPR, so left to itself the compiler splits this into an
+// AND and an OR with literals; here the mask rides in an SGPR and the magic
+// constant in a VGPR.
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t orv) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(mask), "v"(orv));
+  return r;
 }
 
-template <> __device__ __forceinline__ void unpack_pairs<UQ_INT2>(uint32_t w, f16x2 (&p)[8]) {
+template <int S> __device__ __forceinline__ void unpack_pairs(uint32_t w, uint32_t magic, f16x2 (&p)[Fmt<S>::PPD]);
+
+template <> __device__ __forceinline__ void unpack_pairs<UQ_INT4>(uint32_t w, uint32_t magic, f16x2 (&p)[4]) {
+  const uint32_t w8 = w >> 8;
+  p[0] = as_h2(and_or(w, 0x000F000Fu, magic));
+  p[1] = as_h2(and_or(w8, 0x000F000Fu, magic));
+  p[2] = as_h2(and_or(w, 0x00F000F0u, magic));
+  p[3] = as_h2(and_or(w8, 0x00F000F0u, magic));
+}
+
+template <> __device__ __forceinline__ void unpack_pairs<UQ_INT2>(uint32_t w, uint32_t magic, f16x2 (&p)[8]) {
   const uint32_t w8 = w >> 8;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    p[j] = as_h2((w & (0x00030003u << (2 * j))) | kMagic2);
-    p[4 + j] = as_h2((w8 & (0x00030003u << (2 * j))) | kMagic2);
+    p[j] = as_h2(and_or(w, 0x00030003u << (2 * j), magic));
+    p[4 + j] = as_h2(and_or(w8, 0x00030003u << (2 * j), magic));
   }
 }
 
-template <> __device__ __forceinline__ void unpack_pairs<UQ_INT8>(uint32_t w, f16x2 (&p)[2]) {
-  // v_perm_b32 picks bytes of {0x64646464 : w}: (b0, 0x64, b1, 0x64), (b2, 0x64, b3, 0x64)
-  p[0] = as_h2(__builtin_amdgcn_perm(0x64646464u, w, 0x04010400u));
-  p[1] = as_h2(__builtin_amdgcn_perm(0x64646464u, w, 0x04030402u));
+template <> __device__ __forceinline__ void unpack_pairs<UQ_INT8>(uint32_t w, uint32_t magic, f16x2 (&p)[2]) {
+  // v_perm_b32 selects bytes of {magic : w} (selector 0-3 = w, 4-7 = magic;
+  // magic byte 5 is 0x64): (b0, 0x64, b1, 0x64) and (b2, 0x64, b3, 0x64)
+  p[0] = as_h2(__builtin_amdgcn_perm(magic, w, 0x05010500u));
+  p[1] = as_h2(__builtin_amdgcn_perm(magic, w, 0x05030502u));
+}
+
+// Activation pairing for the staged layout.  `d` holds WPD activations of one
+// code dword in natural order as fp16 pairs d[j] = (x_{2j}, x_{2j+1}); the
+// result is the PPD pairs the unpacker's output multiplies, pre-divided by the
+// pair's class (see Slot<S>).  v_perm_b32 selector 0x05040100 takes the low
+// halves of {S0 : S1}, 0x07060302 the high halves.
+template <int S> __device__ __forceinline__ void pair_activations(const uint32_t (&d)[Fmt<S>::WPD / 2],
+                                                                 f16x2 (&p)[Fmt<S>::PPD]);
+
+template <> __device__ __forceinline__ void pair_activations<UQ_INT4>(const uint32_t (&d)[4], f16x2 (&p)[4]) {
+  const f16x2 sixteenth = {_Float16(0.0625f), _Float16(0.0625f)};
+  p[0] = as_h2(__builtin_amdgcn_perm(d[2], d[0], 0x05040100u));              // (x0, x4)
+  p[1] = as_h2(__builtin_amdgcn_perm(d[3], d[1], 0x05040100u));              // (x2, x6)
+  p[2] = as_h2(__builtin_amdgcn_perm(d[2], d[0], 0x07060302u)) * sixteenth;  // (x1, x5)/16
+  p[3] = as_h2(__builtin_amdgcn_perm(d[3], d[1], 0x07060302u)) * sixteenth;  // (x3, x7)/16
+}
+
+template <> __device__ __forceinline__ void pair_activations<UQ_INT2>(const uint32_t (&d)[8], f16x2 (&p)[8]) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    // (x_j, x_{j+8}) / 4^(j mod 4)
+    const f16x2 v = as_h2(__builtin_amdgcn_perm(d[4 + j / 2], d[j / 2], (j & 1) ? 0x07060302u : 0x05040100u));
+    const _Float16 c = _Float16(Slot<UQ_INT2>::inv_cls(j));
+    p[j] = (j & 3) ? v * f16x2{c, c} : v;
+  }
+}
+
+template <> __device__ __forceinline__ void pair_activations<UQ_INT8>(const uint32_t (&d)[2], f16x2 (&p)[2]) {
+  p[0] = as_h2(d[0]);
+  p[1] = as_h2(d[1]);
+}
+
+template <> __device__ __forceinline__ void pair_activations<UQ_NF4>(const uint32_t (&d)[4], f16x2 (&p)[4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) p[j] = as_h2(d[j]);
 }
 
 // DPP lane moves (gfx9 encodings).
@@ -100,6 +147,40 @@ __device__ __forceinline__ float wave_sum(float v) {
   v += dpp_mov<0x140>(v);  // row_mirror
   v += __shfl_xor(v, 16, 64);
   v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
+// Sum of each of four per-lane values over the 64 lanes of a wave, using the
+// gfx950 lane-swap instructions as a transpose-reduction.  v_permlane32_swap
+// exchanges the upper 32 lanes of its first operand with the lower 32 lanes of
+// its second; v_permlane16_swap exchanges the odd 16-lane rows of the first
+// with the even rows of the second.  Two levels of swap-and-add leave one
+// register whose 16-lane rows hold partial sums of a, c, b, d (rows 0..3);
+// DPP mirrors finish each row.  Result: lane 0 = sum(a), lane 16 = sum(c),
+// lane 32 = sum(b), lane 48 = sum(d).
+// The swaps are issued as inline asm with both registers in/out: the compiler
+// builtins return the two swapped registers as a pair, and adding the pair's
+// elements was compiled as the first element added to itself.  The compiler
+// cannot see into the asm to pad its hazards, so the wait states around the
+// cross-lane read and write are spelled out (generously).
+__device__ __forceinline__ void permlane32_swap(float& x, float& y) {
+  asm("s_nop 4\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 4" : "+v"(x), "+v"(y));
+}
+__device__ __forceinline__ void permlane16_swap(float& x, float& y) {
+  asm("s_nop 4\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 4" : "+v"(x), "+v"(y));
+}
+
+__device__ __forceinline__ float wave_sum4(float a, float b, float c, float d) {
+  permlane32_swap(a, b);  // a = [a.lo32, b.lo32], b = [a.hi32, b.hi32]
+  permlane32_swap(c, d);
+  float s1 = a + b;       // lanes 0-31: a halves, lanes 32-63: b halves
+  float s2 = c + d;
+  permlane16_swap(s1, s2);
+  float v = s1 + s2;      // 16-lane rows: a, c, b, d
+  v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_mov<0x141>(v);  // row_half_mirror
+  v += dpp_mov<0x140>(v);  // row_mirror
   return v;
 }
 

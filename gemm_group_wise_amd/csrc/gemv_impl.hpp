@@ -1,0 +1,449 @@
+// Fused group-wise dequant + GEMV for decode, M <= 8 activation rows
+// ("Ultra LLM Engine", Core Components > Fused Kernels: dequantized-weight
+// GEMV during single-token decode).
+//
+// Work split (gfx950, wave64):
+//   * A workgroup is 4 waves.  Each wave owns R consecutive weight rows for
+//     the whole K range; its 64 lanes split each row into 16-byte code
+//     chunks (lane l takes chunks l, l+64, ...), so every 128-bit load
+//     instruction of a wave reads 1 KB of one row contiguously from HBM.
+//   * Per K block, each lane first issues the loads of the activations it
+//     stages, then every weight-chunk load it will need (U chunks x R rows,
+//     plus their group parameters), so the block's HBM traffic is in
+//     flight while the activations are paired, pre-scaled and written to
+//     LDS.  Only then the workgroup synchronises and computes.
+//   * The activations sit in LDS paired for the unpacked code layout (see
+//     device_common.hpp), with two sums per group part: SX = sum x and
+//     C = 1024 * sum x'.  The lane forms t = sum (1024 + cls*q) * x/cls - C
+//     = sum q*x with packed fp16 dot products (fp32 accumulation) and adds
+//     s*t + z*SX, which is sum x*(q*s + z).  NF4: a * sum C16[q]*x.
+//   * Lane partials are summed across the wave with DPP and lane swizzles.
+#pragma once
+
+#include "device_common.hpp"
+
+namespace uq {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr int kXBlock = 16384;  // activations staged per LDS block (all rows of x together)
+
+template <int S, int G, int MT = 1>
+struct Geo {
+  using F = Fmt<S>;
+  static constexpr int CW = F::CW, WPD = F::WPD, PPD = F::PPD;
+  static constexpr int GP = G < CW ? G : CW;  // codes per group part
+  static constexpr int PPC = CW / GP;         // group parts per chunk
+  static constexpr int DPG = GP / WPD;        // dwords per group part
+  static constexpr int XV = GP / 8;           // 128-bit activation loads per part
+  // chunks per lane per group: up to 4096 codes of K, but no more than one
+  // LDS block of activations holds
+  static constexpr int U0 = (kXBlock / MT) / (64 * CW);
+  static constexpr int U = U0 < 1 ? 1 : (U0 < 64 / CW ? U0 : 64 / CW);
+  static constexpr bool NF = (S == UQ_NF4);
+};
+
+template <int S, int G, int R>
+struct ChunkRegs {
+  uint4 code[R];
+  uint32_t par[R][Geo<S, G>::PPC];  // INT: (s | z << 16) per part; NF4: absmax bits
+};
+
+// Load 16-byte code chunk `chunk` of each of the wave's R rows, plus the
+// parameters of the groups it touches.  cbase/pbase point at the wave's first
+// row and roff/poff are the (clamped) row offsets -- all wave-uniform -- so
+// only the chunk offset is per lane.
+template <int S, int G, int R>
+__device__ __forceinline__ void load_chunk(ChunkRegs<S, G, R>& cr, const uint8_t* __restrict__ cbase,
+                                           const uint8_t* __restrict__ pbase, const int64_t (&roff)[R],
+                                           const int64_t (&poff)[R], int chunk) {
+  using Gm = Geo<S, G>;
+  constexpr int PB = Gm::NF ? 2 : 4;  // bytes of one group's parameters
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    cr.code[r] = *reinterpret_cast<const uint4*>(cbase + roff[r] + uint32_t(chunk) * 16u);
+  const uint32_t gb = uint32_t(chunk) * Gm::CW / G * PB;  // first group of the chunk, in bytes
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const uint8_t* p = pbase + poff[r] + gb;
+    if constexpr (Gm::NF) {
+      cr.par[r][0] = *reinterpret_cast<const uint16_t*>(p);
+    } else if constexpr (Gm::PPC == 1) {
+      cr.par[r][0] = *reinterpret_cast<const uint32_t*>(p);
+    } else if constexpr (Gm::PPC == 2) {
+      const uint2 v = *reinterpret_cast<const uint2*>(p);
+      cr.par[r][0] = v.x;
+      cr.par[r][1] = v.y;
+    } else {
+      const uint4 v = *reinterpret_cast<const uint4*>(p);
+      cr.par[r][0] = v.x;
+      cr.par[r][1] = v.y;
+      cr.par[r][2] = v.z;
+      cr.par[r][3] = v.w;
+    }
+  }
+}
+
+__device__ __forceinline__ uint32_t dword_of(const uint4& v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+__device__ __forceinline__ _Float16 half_of(const uint4& v, int e) {
+  const uint32_t d = dword_of(v, e >> 1);
+  return __builtin_bit_cast(_Float16, uint16_t((e & 1) ? (d >> 16) : (d & 0xFFFFu)));
+}
+
+template <int PPD>
+__device__ __forceinline__ void load_pairs(const uint32_t* src, f16x2 (&xp)[PPD]) {
+  if constexpr (PPD >= 4) {
+#pragma unroll
+    for (int q = 0; q < PPD / 4; ++q) {
+      const uint4 v = reinterpret_cast<const uint4*>(src)[q];
+      xp[4 * q] = as_h2(v.x);
+      xp[4 * q + 1] = as_h2(v.y);
+      xp[4 * q + 2] = as_h2(v.z);
+      xp[4 * q + 3] = as_h2(v.w);
+    }
+  } else {
+    const uint2 v = reinterpret_cast<const uint2*>(src)[0];
+    xp[0] = as_h2(v.x);
+    xp[1] = as_h2(v.y);
+  }
+}
+
+template <int S>
+__device__ __forceinline__ void unpack_dword(uint32_t w, uint32_t magic, const uint32_t* lut,
+                                             f16x2 (&hp)[Fmt<S>::PPD]) {
+  if constexpr (S == UQ_NF4) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) hp[j] = as_h2(lut[(w >> (8 * j)) & 0xFFu]);
+  } else {
+    unpack_pairs<S>(w, magic, hp);
+  }
+}
+
+// y += s * t + z * SX for one group part (t = the accumulator, which started
+// at -C); NF4: y += a * t.
+template <bool NF, int MT, int PPC>
+__device__ __forceinline__ void apply_group(uint32_t par, const float (&acc)[MT], const float2 (&cv)[MT][PPC],
+                                            int pp, float (&acc_y)[MT]) {
+  if constexpr (NF) {
+    const float a = h2f(uint16_t(par));
+#pragma unroll
+    for (int mm = 0; mm < MT; ++mm) acc_y[mm] = __builtin_fmaf(a, acc[mm], acc_y[mm]);
+  } else {
+    const float s = h2f(uint16_t(par & 0xFFFFu));
+    const float z = h2f(uint16_t(par >> 16));
+#pragma unroll
+    for (int mm = 0; mm < MT; ++mm) {
+      acc_y[mm] = __builtin_fmaf(s, acc[mm], acc_y[mm]);
+      acc_y[mm] = __builtin_fmaf(z, cv[mm][pp].y, acc_y[mm]);
+    }
+  }
+}
+
+// ONE: the whole K range fits one LDS block of activations and one group of
+// 64*U chunks per lane, so the kernel body is loop-free.  (With a loop, the
+// compiler must assume loads from the previous trip may still be landing in
+// the registers it is about to reuse, and it waits for them at the loop head,
+// which stalls the first trip's weight loads behind the activation loads.)
+template <int S, int G, int MT, int R, bool ONE, int IPT>
+__global__ __launch_bounds__(kThreads) void gemv_kernel(
+    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ params,
+    const uint16_t* __restrict__ x, float* __restrict__ y, int n, int k, int m,
+    int kb_max) {
+  using Gm = Geo<S, G, MT>;
+  constexpr int CW = Gm::CW, WPD = Gm::WPD, PPD = Gm::PPD, GP = Gm::GP;
+  constexpr int PPC = Gm::PPC, DPG = Gm::DPG, XV = Gm::XV, U = Gm::U;
+  constexpr bool NF = Gm::NF;
+  // Each thread stages IPT activation group parts per K block (IPT * 256
+  // covers the block; chosen at launch).
+  constexpr int kIPT = IPT;
+
+  extern __shared__ uint4 lds4[];
+  uint32_t* lds = reinterpret_cast<uint32_t*>(lds4);
+  uint32_t* lut = lds;                              // NF4: 256 fp16 pairs
+  uint32_t* xs = lds + (NF ? 256 : 0);              // [MT][kb_max/2] fp16 pairs
+  float2* cs = reinterpret_cast<float2*>(xs + MT * (kb_max / 2));  // [MT][kb_max/GP]
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int64_t row0 = (int64_t(blockIdx.x) * kWaves + wave) * R;
+  const size_t rowb = size_t(k) * Fmt<S>::bits / 8;
+  const int ng = k / G;
+  // Wave-uniform addressing: base pointers at the wave's first row, clamped
+  // row offsets (rows past n re-read row n-1 and are not stored).
+  const uint8_t* cbase = codes + size_t(row0) * rowb;
+  const uint8_t* pbase = params + size_t(row0) * size_t(ng) * (NF ? 2 : 4);
+  int64_t roff[R], poff[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t rr = row0 + r < n ? r : int64_t(n) - 1 - row0;
+    roff[r] = rr * int64_t(rowb);
+    poff[r] = rr * int64_t(ng) * (NF ? 2 : 4);
+  }
+  const uint32_t magic = kMagic2;
+
+  if constexpr (NF) {
+    // byte b -> (fp16(C[b & 15]), fp16(C[b >> 4]))
+    const _Float16 lo = _Float16(nf4_value(tid & 15)), hi = _Float16(nf4_value(tid >> 4));
+    lut[tid] = as_u32(f16x2{lo, hi});
+  }
+
+  float acc_y[R][MT];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int mm = 0; mm < MT; ++mm) acc_y[r][mm] = 0.0f;
+
+  // One K block: stage its activations, stream its weight chunks, accumulate.
+  auto k_block = [&](const int kb0) __attribute__((always_inline)) {
+    const int kb = ONE ? k : (k - kb0 < kb_max ? k - kb0 : kb_max);
+    const int nch = kb / CW;
+    const int64_t ch0 = kb0 / CW;
+    const int n_items = MT * nch * PPC;
+
+    // (1) activation loads for the parts this thread stages (L2 hits; issued
+    //     first so they return first)
+    //     Loads are never predicated: out-of-range items and chunks load a
+    //     clamped, valid address and are ignored later.  (Conditionally issued
+    //     loads leave the compiler unsure how many loads follow a given one,
+    //     and it then waits for all of them.)
+    uint4 xr[kIPT][XV];
+#pragma unroll
+    for (int s = 0; s < kIPT; ++s) {
+      const int it0 = tid + s * kThreads;
+      const int it = it0 < n_items ? it0 : n_items - 1;
+      const int mm = it / (nch * PPC);
+      const int rem = it - mm * (nch * PPC);
+      const int c = rem / PPC, pp = rem - c * PPC;
+      const uint4* src = reinterpret_cast<const uint4*>(
+          x + size_t(mm < m ? mm : 0) * size_t(k) + kb0 + c * CW + pp * GP);
+#pragma unroll
+      for (int v = 0; v < XV; ++v) xr[s][v] = src[v];
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep the activation loads ahead of the weight loads
+    // (2) every weight chunk of the first 64*U columns, for all R rows
+    ChunkRegs<S, G, R> cur[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = lane + 64 * u;
+      load_chunk<S, G, R>(cur[u], cbase, pbase, roff, poff, int(ch0) + (c < nch ? c : nch - 1));
+    }
+    __builtin_amdgcn_sched_barrier(0);  // and all weight loads ahead of the staging work
+
+    // (3) stage: pair, pre-scale, sum; write LDS
+    __syncthreads();  // LDS free (previous K block done)
+    // Threads past the last item redo the last one (same values, same LDS
+    // words), so the staging has no branch for the loads to sink into.
+#pragma unroll
+    for (int s = 0; s < kIPT; ++s) {
+      {
+        const int it0 = tid + s * kThreads;
+        const int it = it0 < n_items ? it0 : n_items - 1;
+        const int mm = it / (nch * PPC);
+        const int rem = it - mm * (nch * PPC);
+        const int c = rem / PPC, pp = rem - c * PPC;
+        const bool live = mm < m;
+        const f16x2 one2 = {_Float16(1.0f), _Float16(1.0f)};
+        float sx = 0.0f, sxp = 0.0f;
+#pragma unroll
+        for (int dl = 0; dl < DPG; ++dl) {
+          const int dd = pp * DPG + dl;
+          uint32_t d[WPD / 2];  // this code dword's activations, natural fp16 pairs
+#pragma unroll
+          for (int j = 0; j < WPD / 2; ++j) d[j] = live ? dword_of(xr[s][(dl * WPD / 2 + j) >> 2], (dl * WPD / 2 + j) & 3) : 0u;
+          f16x2 pr[PPD];
+          pair_activations<S>(d, pr);
+          if constexpr (!NF) {
+#pragma unroll
+            for (int j = 0; j < WPD / 2; ++j) sx = __builtin_amdgcn_fdot2(as_h2(d[j]), one2, sx, false);
+#pragma unroll
+            for (int j = 0; j < PPD; ++j) sxp = __builtin_amdgcn_fdot2(pr[j], one2, sxp, false);
+          }
+          uint32_t* dst = xs + mm * (kb_max / 2) + (dd * nch + c) * PPD;
+          if constexpr (PPD == 8) {
+            reinterpret_cast<uint4*>(dst)[0] = make_uint4(as_u32(pr[0]), as_u32(pr[1]), as_u32(pr[2]), as_u32(pr[3]));
+            reinterpret_cast<uint4*>(dst)[1] = make_uint4(as_u32(pr[4]), as_u32(pr[5]), as_u32(pr[6]), as_u32(pr[7]));
+          } else if constexpr (PPD == 4) {
+            reinterpret_cast<uint4*>(dst)[0] = make_uint4(as_u32(pr[0]), as_u32(pr[1]), as_u32(pr[2]), as_u32(pr[3]));
+          } else {
+            reinterpret_cast<uint2*>(dst)[0] = make_uint2(as_u32(pr[0]), as_u32(pr[1]));
+          }
+        }
+        if constexpr (!NF) cs[mm * (kb_max / GP) + pp * nch + c] = make_float2(-1024.0f * sxp, sx);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);  // no weight-dependent math above the barrier
+    __syncthreads();
+
+    // (4) compute; K blocks wider than 64*U chunks load each further group
+    //     just before using it (many waves per SIMD cover that latency)
+    // one group of 64*U chunks per lane; further groups (long K) reload `cur`
+    auto chunk_group = [&](const int cg) __attribute__((always_inline)) {
+      if (cg > 0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int c = cg + lane + 64 * u;
+          load_chunk<S, G, R>(cur[u], cbase, pbase, roff, poff, int(ch0) + (c < nch ? c : nch - 1));
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        // One chunk at a time: keep the scheduler from interleaving chunks,
+        // which would hold every chunk's temporaries live at once.
+        __builtin_amdgcn_sched_barrier(0);
+        // No branch around the math either (it would invite the compiler to
+        // sink the weight loads into it): a lane past the last chunk works
+        // on its clamped chunk and adds it with scale and zero set to 0.
+        const int c0 = cg + lane + 64 * u;
+        const bool valid = c0 < nch;
+        const int c = valid ? c0 : nch - 1;
+        if constexpr (MT <= 2) {
+          // Row-inner: the chunk's activation pairs stay in registers and each
+          // row's math waits only for that row's own load.
+          f16x2 xp[MT][4][PPD];
+#pragma unroll
+          for (int mm = 0; mm < MT; ++mm)
+#pragma unroll
+            for (int dd = 0; dd < 4; ++dd) load_pairs<PPD>(xs + mm * (kb_max / 2) + (dd * nch + c) * PPD, xp[mm][dd]);
+          float2 cv[MT][PPC];
+          if constexpr (!NF) {
+#pragma unroll
+            for (int mm = 0; mm < MT; ++mm)
+#pragma unroll
+              for (int pp = 0; pp < PPC; ++pp) cv[mm][pp] = cs[mm * (kb_max / GP) + pp * nch + c];
+          }
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+#pragma unroll
+            for (int pp = 0; pp < PPC; ++pp) {
+              float acc[MT];
+#pragma unroll
+              for (int mm = 0; mm < MT; ++mm) acc[mm] = NF ? 0.0f : cv[mm][pp].x;  // starts at -C
+#pragma unroll
+              for (int dl = 0; dl < DPG; ++dl) {
+                const int dd = pp * DPG + dl;
+                f16x2 hp[PPD];
+                unpack_dword<S>(dword_of(cur[u].code[r], dd), magic, lut, hp);
+#pragma unroll
+                for (int mm = 0; mm < MT; ++mm)
+#pragma unroll
+                  for (int j = 0; j < PPD; ++j) acc[mm] = __builtin_amdgcn_fdot2(hp[j], xp[mm][dd][j], acc[mm], false);
+              }
+              apply_group<NF>(valid ? cur[u].par[r][pp] : 0u, acc, cv, pp, acc_y[r]);
+            }
+          }
+        } else {
+          // Dword-outer: each activation pair read from LDS serves all R rows.
+#pragma unroll
+          for (int pp = 0; pp < PPC; ++pp) {
+            float2 cv[MT][PPC];
+            if constexpr (!NF) {
+#pragma unroll
+              for (int mm = 0; mm < MT; ++mm) cv[mm][pp] = cs[mm * (kb_max / GP) + pp * nch + c];
+            }
+            float acc[R][MT];
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+              for (int mm = 0; mm < MT; ++mm) acc[r][mm] = NF ? 0.0f : cv[mm][pp].x;  // starts at -C
+#pragma unroll
+            for (int dl = 0; dl < DPG; ++dl) {
+              const int dd = pp * DPG + dl;
+              f16x2 hp[R][PPD];
+#pragma unroll
+              for (int r = 0; r < R; ++r) unpack_dword<S>(dword_of(cur[u].code[r], dd), magic, lut, hp[r]);
+#pragma unroll
+              for (int mm = 0; mm < MT; ++mm) {
+                f16x2 xq[PPD];
+                load_pairs<PPD>(xs + mm * (kb_max / 2) + (dd * nch + c) * PPD, xq);
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+#pragma unroll
+                  for (int j = 0; j < PPD; ++j)
+                    acc[r][mm] = __builtin_amdgcn_fdot2(hp[r][j], xq[j], acc[r][mm], false);
+              }
+            }
+#pragma unroll
+            for (int r = 0; r < R; ++r) apply_group<NF>(valid ? cur[u].par[r][pp] : 0u, acc[r], cv, pp, acc_y[r]);
+          }
+        }
+      }
+    };
+    if constexpr (ONE) {
+      chunk_group(0);
+    } else {
+      for (int cg = 0; cg < nch; cg += 64 * U) chunk_group(cg);
+    }
+  };
+  if constexpr (ONE) {
+    k_block(0);
+  } else {
+    for (int kb0 = 0; kb0 < k; kb0 += kb_max) k_block(kb0);
+  }
+
+  // Reduce lane partials and store: four (row, m) outputs per swap-reduction.
+  constexpr int NV = R * MT;
+  float* yv = &acc_y[0][0];
+#pragma unroll
+  for (int q = 0; q + 4 <= NV; q += 4) {
+    const float v = wave_sum4(yv[q], yv[q + 1], yv[q + 2], yv[q + 3]);
+    const int slot = q + ((lane >> 4) == 1 ? 2 : (lane >> 4) == 2 ? 1 : (lane >> 4));  // a, c, b, d
+    const int r = slot / MT, mm = slot - r * MT;
+    if ((lane & 15) == 0 && row0 + r < n && mm < m) y[size_t(mm) * size_t(n) + size_t(row0 + r)] = v;
+  }
+#pragma unroll
+  for (int q = NV - NV % 4; q < NV; ++q) {
+    const float v = wave_sum(yv[q]);
+    const int r = q / MT, mm = q - r * MT;
+    if (lane == 0 && row0 + r < n && mm < m) y[size_t(mm) * size_t(n) + size_t(row0 + r)] = v;
+  }
+}
+
+#ifndef UQ_GEMV_ROWS_PER_WAVE
+#define UQ_GEMV_ROWS_PER_WAVE 4
+#endif
+
+template <int S, int G, int MT, int R, bool ONE>
+hipError_t launch_ipt(int ipt, dim3 grid, void** args, size_t shmem, hipStream_t stream) {
+  const void* fn = ipt == 1   ? reinterpret_cast<const void*>(&gemv_kernel<S, G, MT, R, ONE, 1>)
+                   : ipt == 2 ? reinterpret_cast<const void*>(&gemv_kernel<S, G, MT, R, ONE, 2>)
+                              : reinterpret_cast<const void*>(&gemv_kernel<S, G, MT, R, ONE, 4>);
+  return hipLaunchKernel(fn, grid, dim3(kThreads), args, shmem, stream);
+}
+
+template <int S, int G, int MT, int R>
+hipError_t launch(const uq_layout* L, const void* codes, const void* params, const uint16_t* x,
+                  float* y, int m, hipStream_t stream) {
+  using Gm = Geo<S, G, MT>;
+  const int k = int(L->k), n = int(L->n);
+  int kb_max = kXBlock / MT;
+  if (kb_max > k) kb_max = k;
+  const size_t shmem = (Gm::NF ? 1024 : 0) + size_t(MT) * kb_max * 2 +
+                       (Gm::NF ? 0 : size_t(MT) * (kb_max / Gm::GP) * 8);
+  const int rows_per_block = kWaves * R;
+  const dim3 grid(unsigned((n + rows_per_block - 1) / rows_per_block));
+  const uint8_t* c8 = static_cast<const uint8_t*>(codes);
+  const uint8_t* p8 = static_cast<const uint8_t*>(params);
+  void* args[] = {&c8, &p8, (void*)&x, &y, (void*)&n, (void*)&k, &m, &kb_max};
+  const int items = MT * (kb_max / Gm::GP);  // staged activation parts per K block
+  const int ipt = items <= kThreads ? 1 : items <= 2 * kThreads ? 2 : 4;
+  const bool one = kb_max == k && k <= 64 * Gm::U * Gm::CW;
+  return one ? launch_ipt<S, G, MT, R, true>(ipt, grid, args, shmem, stream)
+             : launch_ipt<S, G, MT, R, false>(ipt, grid, args, shmem, stream);
+}
+
+template <int S, int G>
+hipError_t launch_m(const uq_layout* L, const void* codes, const void* params, const uint16_t* x,
+                    float* y, int m, hipStream_t stream) {
+  constexpr int R = UQ_GEMV_ROWS_PER_WAVE;
+  if (m == 1) return launch<S, G, 1, R>(L, codes, params, x, y, m, stream);
+  if (m == 2) return launch<S, G, 2, R>(L, codes, params, x, y, m, stream);
+  if (m <= 4) return launch<S, G, 4, R>(L, codes, params, x, y, m, stream);
+  return launch<S, G, 8, R>(L, codes, params, x, y, m, stream);
+}
+
+}  // namespace
+}  // namespace uq

@@ -1,0 +1,14 @@
+// NF4 instantiations of the fused dequant + GEMV kernel (gemv_impl.hpp).
+#include "gemv_impl.hpp"
+
+namespace uq {
+
+hipError_t launch_gemv_nf4(const uq_layout* L, const void* codes, const void* params,
+                         const uint16_t* x, float* y, int m, hipStream_t stream) {
+  switch (L->group) {
+    case 64: return launch_m<UQ_NF4, 64>(L, codes, params, x, y, m, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace uq
