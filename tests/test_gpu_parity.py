@@ -203,20 +203,22 @@ def test_gemm_k_tail(lib, k):
 
 
 def test_gemm_batched_equivalence(lib):
-    """Row i of an M-row GEMM equals the single-row GEMM of x[i], bit for bit.
+    """Row i of an M-row GEMM equals the single-row GEMM of x[i].
 
-    (GEMM and GEMV rows are not compared under the gate: the bf16 rounding of
-    w' alone moves the GEMM by ~2e-3 relative to the fp16 GEMV, which is why
-    the GEMM's oracle applies the same bf16 casts.)
+    The GEMM splits K across workgroups and adds the partial sums with fp32
+    atomics in no fixed order, so rows agree to fp32 reassociation (a few
+    ulps), not bit for bit.  (GEMM and GEMV rows are not compared under the
+    gate: the bf16 rounding of w' alone moves the GEMM by ~2e-3 relative to
+    the fp16 GEMV, which is why the GEMM's oracle applies the same casts.)
     """
-    w, x = workloads.make_random(200, 1024, 40, seed=15)
+    w, x = workloads.make_random(300, 2048, 130, seed=15)
     lay, codes, params = packed_on_device(lib, "int4", 128, w)
-    ys = [run_gemm(lib, lay, codes, params, x[i:i + 1], 1)[0] for i in range(40)]
-    for m in (16, 40):
+    ys = np.stack([run_gemm(lib, lay, codes, params, x[i:i + 1], 1)[0] for i in range(130)])
+    for m in (16, 40, 130):
         note(f"gemm batched equivalence m={m}")
         y = run_gemm(lib, lay, codes, params, x, m)
-        for i in range(m):
-            assert np.array_equal(y[i], ys[i]), (m, i)
+        scale = np.abs(ys[:m]).max()
+        assert np.abs(y - ys[:m]).max() <= 1e-5 * scale, m
 
 
 # ---------------------------------------------------------------------------
