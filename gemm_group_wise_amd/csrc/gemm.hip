@@ -6,27 +6,35 @@
 // w' = fma(q, s, z) (INT-N) or C[q] * a (NF4) is the exact fp32 dequant and
 // both casts round to nearest even.
 //
-// Work split (gfx950):
-//   * v_mfma_f32_32x32x16_bf16.  A workgroup is 4 waves and covers BM rows of
-//     x by 256 weight rows; wave w owns weight rows [64w, 64w + 64) of the
-//     tile (two 32-column MFMA tiles), so every activation fragment read
-//     from LDS feeds two MFMAs per M tile.
-//   * Weights never pass through LDS: each wave loads its own 64 rows'
-//     codes and dequantizes them straight into MFMA B registers, 8 codes per
-//     lane per MFMA, exactly once per M tile.
-//   * Activations are converted fp16 -> bf16 into a double-buffered LDS
-//     tile (BM x 128); the next K step's activation and code loads are in
-//     flight while the current one multiplies.
-//   * With only ~43 column tiles for a 7B-sized N, K is split across
-//     workgroups (so about 256 run at once) and the partial products are
-//     added with hardware fp32 atomics into y, which a fill kernel zeroes
-//     first; the order of those additions is not fixed, so y can differ from
-//     run to run in the last bits when K is split.
+// Two launches on the caller's stream:
+//   1. x (fp16) -> bf16 into an activation workspace, once per call, so the
+//      conversion is not repeated by every column tile.
+//   2. The GEMM.  A workgroup is 8 waves (two per SIMD, so one wave's
+//      dequant VALU work and LDS reads run under the other's MFMAs; on gfx950
+//      a single wave does not overlap them well).  The workgroup owns BM rows
+//      of x by BN = 64 * WGN weight rows; wave (wn, wk) owns weight rows
+//      [64 wn, 64 wn + 64) of the tile and the KW-wide K slice wk of every
+//      K step of KW * WGK.  Each wave keeps a BM x 64 fp32 accumulator
+//      (v_mfma_f32_32x32x16_bf16 tiles) and the K slices are summed through
+//      LDS at the end, so no partial sums go to memory.
+//   * Activations: the bf16 tile of a K step (BM x KW*WGK, 32 KB) is copied
+//     HBM -> LDS by global_load_lds_dwordx4 (no VGPR staging) into a ring of
+//     four buffers, three steps ahead of use, XOR-swizzled on 16-byte chunks
+//     so the MFMA fragment reads are free of bank conflicts.  (An L2-to-LDS
+//     copy takes about 1.5 us to land; one step ahead does not hide that.)
+//   * Weights never pass through LDS: each lane loads the codes of its weight
+//     row and K slice three steps ahead into a ring of registers and
+//     dequantizes them straight into MFMA B registers, 8 codes per MFMA,
+//     exactly once per M tile.
 //
-// Lane layout of one K step of 128: lane l works on row (l % 32) of its
-// 32-row tile and on the 64-code half kh = l / 32 of the step; MFMA sub-step
-// s (0..7) takes codes [64*kh + 8*s, +8) on both the A and the B side.  (Any
-// consistent order of k within an MFMA gives the same dot product.)
+// Lane layout of one wave's K slice of KW: lane l works on row (l % 32) of
+// each 32-row tile and on codes [KW/2 * kh, KW/2 * (kh + 1)) with kh = l / 32;
+// MFMA sub-step s (0 .. KW/16 - 1) takes codes 8s..8s+7 of that half on both
+// the A and the B side (any consistent assignment of k within an MFMA gives
+// the same dot product).
+#include <mutex>
+#include <vector>
+
 #include "device_common.hpp"
 
 namespace uq {
@@ -34,53 +42,67 @@ namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kThreads = 256;
-constexpr int kWaves = 4;
-constexpr int kWN = 64;             // weight rows per wave
-constexpr int kBN = kWaves * kWN;   // weight rows per workgroup
-constexpr int kBK = 128;            // K per step
-constexpr int kLdA = kBK + 8;       // bf16 per LDS row of activations (16-byte pad)
+constexpr int kThreads = 512;
+constexpr int kWaves = 8;
+#ifndef UQ_GEMM_NB
+#define UQ_GEMM_NB 2
+#endif
+constexpr int kNB = UQ_GEMM_NB;  // activation buffers = code register sets = prefetch distance + 1
+static_assert(kNB == 2 || kNB == 4, "ring of two or four");
 
-// Raw codes of one lane for one 32-row tile and one K step: 64 consecutive
-// codes of one weight row, and the parameters of the groups they span.
-template <int S, int G>
-struct BRegs {
-  static constexpr int bits = Fmt<S>::bits;
-  static constexpr int NV = 64 * bits / 128;            // uint4 of codes (1, 2 or 4)
-  static constexpr int NGRP = G >= 64 ? 1 : 64 / G;     // groups among the 64 codes
-  uint4 code[NV];
-  uint32_t par[NGRP];
+template <int BM, int WGN>
+struct Tile {
+  static constexpr int WGK = kWaves / WGN;              // K slices per step
+  static constexpr int KW = (kNB == 2 || BM == 32) ? 64 : 32;  // k per wave per step
+  static constexpr int SUB = KW / 16;                   // MFMA sub-steps per step
+  static constexpr int KS = KW * WGK;                   // k per step
+  static constexpr int BN = 64 * WGN;                   // weight rows per workgroup
+  static constexpr int TM = BM / 32;                    // 32-row MFMA tiles of x
+  static constexpr int CPR = KS / 8;                    // 16-byte chunks per activation row
+  static constexpr int BYTES = BM * KS * 2;             // one activation buffer
+  static constexpr int LOADS = BYTES / (kThreads * 16); // 16-byte copies per thread per step
+  static constexpr int RPI = kThreads / CPR;            // activation rows per copy round
+  static_assert(kNB * BYTES <= 131072, "activation ring fits in LDS");
+  static_assert(RPI % 8 == 0, "swizzle period");
+  static_assert((WGK / 2) * WGN * TM * 2 * 16 * 64 * 4 <= kNB * BYTES, "K-slice reduction fits in LDS");
 };
 
-template <int S, int G>
-__device__ __forceinline__ void load_b(BRegs<S, G>& b, const uint8_t* __restrict__ codes,
-                                       const uint8_t* __restrict__ params, int row, int k0,
-                                       int k, size_t rowb, int ng) {
-  constexpr int bits = Fmt<S>::bits;
-  constexpr int NV = BRegs<S, G>::NV, NGRP = BRegs<S, G>::NGRP;
-  const uint8_t* cr = codes + size_t(row) * rowb;
+// The KW/2 codes of one lane for one weight row and K slice.
+template <int S, int KW>
+struct Codes {
+  static constexpr int BYTES = KW / 2 * Fmt<S>::bits / 8;  // 4 .. 32
+  static constexpr int W = BYTES / 4;
+  uint32_t d[W];
+};
+
+// One load instruction per 16 bytes (or fewer): the count is part of the
+// wait-count arithmetic in the kernel.
+template <int S, int KW>
+__device__ __forceinline__ void load_codes(Codes<S, KW>& c, const uint8_t* __restrict__ p) {
+  constexpr int B = Codes<S, KW>::BYTES;
+  if constexpr (B == 4) {
+    c.d[0] = *reinterpret_cast<const uint32_t*>(p);
+  } else if constexpr (B == 8) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    c.d[0] = v.x;
+    c.d[1] = v.y;
+  } else {
 #pragma unroll
-  for (int v = 0; v < NV; ++v) {
-    int kv = k0 + v * (128 / bits);                 // first code of this 16-byte piece
-    kv = kv < k ? kv : 0;                           // past K: any valid piece (its x is 0)
-    b.code[v] = *reinterpret_cast<const uint4*>(cr + size_t(kv) * bits / 8);
-  }
-  const int kg = k0 < k ? k0 : 0;
-#pragma unroll
-  for (int j = 0; j < NGRP; ++j) {
-    int g = kg / G + j;
-    g = g < ng ? g : ng - 1;  // groups past K (short last step): any valid one (its x is 0)
-    const int64_t gi = int64_t(row) * ng + g;
-    if constexpr (S == UQ_NF4) b.par[j] = *reinterpret_cast<const uint16_t*>(params + gi * 2);
-    else b.par[j] = *reinterpret_cast<const uint32_t*>(params + gi * 4);
+    for (int h = 0; h < B / 16; ++h) {
+      const uint4 v = *reinterpret_cast<const uint4*>(p + 16 * h);
+      c.d[4 * h] = v.x;
+      c.d[4 * h + 1] = v.y;
+      c.d[4 * h + 2] = v.z;
+      c.d[4 * h + 3] = v.w;
+    }
   }
 }
-
-__device__ __forceinline__ uint32_t dword_of(const uint4& v, int i) {
-  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+template <int S, int KW>
+constexpr int code_loads() {
+  return Codes<S, KW>::BYTES <= 16 ? 1 : Codes<S, KW>::BYTES / 16;
 }
 
-// Byte i of a dword to fp32 in one instruction.  (Written as shift-and-mask,
+// Byte I of a dword to fp32 in one instruction.  (Written as shift-and-mask,
 // the compiler emits a bit-field extract plus a byte-0 conversion: two.)
 template <int I>
 __device__ __forceinline__ float ubyte_f32(uint32_t v) {
@@ -92,46 +114,39 @@ __device__ __forceinline__ float ubyte_f32(uint32_t v) {
   return r;
 }
 
-template <int I>
-__device__ __forceinline__ void bytes_to_f32(uint32_t v, float (&f)[4]) {
-  f[0] = ubyte_f32<0>(v);
-  f[1] = ubyte_f32<1>(v);
-  f[2] = ubyte_f32<2>(v);
-  f[3] = ubyte_f32<3>(v);
-}
-
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   const bf16x2 v = {__bf16(a), __bf16(b)};
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// Dequantize codes [8s, 8s+8) of the lane's 64 to bf16 (exact fp32 dequant,
-// then round to nearest even), as an MFMA operand.
-template <int S, int G>
-__device__ __forceinline__ bf16x8 dequant8(const BRegs<S, G>& b, int s, const float* nf4) {
+// Group parameters of a lane's K slice, as fp32: (s, z), or (a, 0) for NF4.
+// The lane's KW/2 codes span NGRP groups (two only for INT2 G16 with KW 64).
+template <int S, int G, int KW>
+struct Params {
+  static constexpr int NGRP = G < KW / 2 ? KW / 2 / G : 1;
+  float s[NGRP], z[NGRP];
+};
+
+// Codes 8s..8s+7 of the lane's KW/2 -> bf16(w') as an MFMA operand.
+template <int S, int G, int KW>
+__device__ __forceinline__ bf16x8 dequant8(const Codes<S, KW>& c, const Params<S, G, KW>& p, int s,
+                                           const float* nf4) {
   constexpr int bits = Fmt<S>::bits;
+  const int grp = G < KW / 2 ? (8 * s) / G : 0;
+  const float sc = p.s[grp], zc = p.z[grp];
   float w[8];
-  const int grp = G >= 64 ? 0 : (8 * s) / G;
-  float sc, zc;
-  if constexpr (S == UQ_NF4) {
-    sc = h2f(uint16_t(b.par[0]));
-    zc = 0.0f;
-  } else {
-    sc = h2f(uint16_t(b.par[grp] & 0xFFFFu));
-    zc = h2f(uint16_t(b.par[grp] >> 16));
-  }
   if constexpr (bits == 8) {
-    const uint32_t d0 = dword_of(b.code[s >> 1], (s & 1) * 2), d1 = dword_of(b.code[s >> 1], (s & 1) * 2 + 1);
-    float q0[4], q1[4];
-    bytes_to_f32<0>(d0, q0);
-    bytes_to_f32<0>(d1, q1);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      w[i] = __builtin_fmaf(q0[i], sc, zc);
-      w[4 + i] = __builtin_fmaf(q1[i], sc, zc);
-    }
+    const uint32_t d0 = c.d[2 * s], d1 = c.d[2 * s + 1];
+    w[0] = __builtin_fmaf(ubyte_f32<0>(d0), sc, zc);
+    w[1] = __builtin_fmaf(ubyte_f32<1>(d0), sc, zc);
+    w[2] = __builtin_fmaf(ubyte_f32<2>(d0), sc, zc);
+    w[3] = __builtin_fmaf(ubyte_f32<3>(d0), sc, zc);
+    w[4] = __builtin_fmaf(ubyte_f32<0>(d1), sc, zc);
+    w[5] = __builtin_fmaf(ubyte_f32<1>(d1), sc, zc);
+    w[6] = __builtin_fmaf(ubyte_f32<2>(d1), sc, zc);
+    w[7] = __builtin_fmaf(ubyte_f32<3>(d1), sc, zc);
   } else if constexpr (bits == 4) {
-    const uint32_t d = dword_of(b.code[s >> 2], s & 3);
+    const uint32_t d = c.d[s];
     const uint32_t lo = d & 0x0F0F0F0Fu, hi = (d >> 4) & 0x0F0F0F0Fu;  // codes 0,2,4,6 | 1,3,5,7
     if constexpr (S == UQ_NF4) {
 #pragma unroll
@@ -140,252 +155,402 @@ __device__ __forceinline__ bf16x8 dequant8(const BRegs<S, G>& b, int s, const fl
         w[2 * i + 1] = nf4[(hi >> (8 * i)) & 0xFu] * sc;
       }
     } else {
-      float qe[4], qo[4];
-      bytes_to_f32<0>(lo, qe);
-      bytes_to_f32<0>(hi, qo);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        w[2 * i] = __builtin_fmaf(qe[i], sc, zc);
-        w[2 * i + 1] = __builtin_fmaf(qo[i], sc, zc);
-      }
+      w[0] = __builtin_fmaf(ubyte_f32<0>(lo), sc, zc);
+      w[1] = __builtin_fmaf(ubyte_f32<0>(hi), sc, zc);
+      w[2] = __builtin_fmaf(ubyte_f32<1>(lo), sc, zc);
+      w[3] = __builtin_fmaf(ubyte_f32<1>(hi), sc, zc);
+      w[4] = __builtin_fmaf(ubyte_f32<2>(lo), sc, zc);
+      w[5] = __builtin_fmaf(ubyte_f32<2>(hi), sc, zc);
+      w[6] = __builtin_fmaf(ubyte_f32<3>(lo), sc, zc);
+      w[7] = __builtin_fmaf(ubyte_f32<3>(hi), sc, zc);
     }
   } else {  // 2 bits: codes 8s..8s+7 are 16 bits of one dword
-    const uint32_t d = dword_of(b.code[0], s >> 1) >> (16 * (s & 1));
+    const uint32_t d = c.d[s >> 1] >> (16 * (s & 1));
 #pragma unroll
     for (int i = 0; i < 8; ++i) w[i] = __builtin_fmaf(float((d >> (2 * i)) & 3u), sc, zc);
   }
-  const uint4 p = make_uint4(pack_bf16(w[0], w[1]), pack_bf16(w[2], w[3]), pack_bf16(w[4], w[5]),
+  const uint4 v = make_uint4(pack_bf16(w[0], w[1]), pack_bf16(w[2], w[3]), pack_bf16(w[4], w[5]),
                              pack_bf16(w[6], w[7]));
-  return __builtin_bit_cast(bf16x8, p);
+  return __builtin_bit_cast(bf16x8, v);
 }
 
-// Activations: BM rows x 128 columns per K step.  Thread t converts
-// PER = BM * 128 / 256 consecutive values of one row.
-template <int BM>
-struct AStage {
-  static constexpr int PER = BM * kBK / kThreads;  // 16, 32 or 64 values
-  static constexpr int NV = PER / 8;               // uint4 loads
-  uint4 v[NV];
-};
-
-template <int BM>
-__device__ __forceinline__ void load_a(AStage<BM>& a, const uint16_t* __restrict__ x, int tid, int bm,
-                                       int k0, int m, int k) {
-  constexpr int PER = AStage<BM>::PER, NV = AStage<BM>::NV;
-  constexpr int TPR = kBK / PER;                   // threads per row
-  const int r = tid / TPR, c = (tid % TPR) * PER;
-  const int row = bm + r < m ? bm + r : m - 1;
-#pragma unroll
-  for (int v = 0; v < NV; ++v) {
-    int kv = k0 + c + 8 * v;
-    kv = kv < k ? kv : 0;
-    a.v[v] = *reinterpret_cast<const uint4*>(x + size_t(row) * size_t(k) + kv);
-  }
+// Workgroup order: the dispatcher deals workgroups to the 8 XCDs in turn
+// (workgroup b to XCD b % 8); renumber them so that each XCD gets a contiguous
+// run of tiles, and the M tiles that share a weight tile share an L2.
+__device__ __forceinline__ int xcd_order(int b, int nb) {
+  const int q = nb >> 3, r = nb & 7, x = b & 7;
+  return x * q + (x < r ? x : r) + (b >> 3);
 }
 
-template <int BM>
-__device__ __forceinline__ void store_a(const AStage<BM>& a, __bf16* As, int tid, int bm, int k0, int m,
-                                        int k) {
-  constexpr int PER = AStage<BM>::PER, NV = AStage<BM>::NV;
-  constexpr int TPR = kBK / PER;
-  const int r = tid / TPR, c = (tid % TPR) * PER;
-  const bool live_row = bm + r < m;
-#pragma unroll
-  for (int v = 0; v < NV; ++v) {
-    const bool live = live_row && k0 + c + 8 * v < k;  // k is a multiple of 32: whole pieces
-    uint4 o = make_uint4(0, 0, 0, 0);
-    if (live) {
-      const uint4 h = a.v[v];
-      o.x = pack_bf16(h2f(uint16_t(h.x)), h2f(uint16_t(h.x >> 16)));
-      o.y = pack_bf16(h2f(uint16_t(h.y)), h2f(uint16_t(h.y >> 16)));
-      o.z = pack_bf16(h2f(uint16_t(h.z)), h2f(uint16_t(h.z >> 16)));
-      o.w = pack_bf16(h2f(uint16_t(h.w)), h2f(uint16_t(h.w >> 16)));
-    }
-    *reinterpret_cast<uint4*>(As + r * kLdA + c + 8 * v) = o;
-  }
-}
-
-template <int S, int G, int BM>
+template <int S, int G, int BM, int WGN>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint8_t* __restrict__ codes,
                                                         const uint8_t* __restrict__ params,
-                                                        const uint16_t* __restrict__ x,
+                                                        const uint16_t* __restrict__ xb,
                                                         float* __restrict__ y, int n, int k, int m,
-                                                        int tiles_m, int splits, int steps_per_split) {
-  constexpr int TM = BM / 32;  // 32-row MFMA tiles
-  __shared__ __attribute__((aligned(16))) __bf16 As[2][BM * kLdA];
+                                                        int tiles_m, int nblocks) {
+  using T = Tile<BM, WGN>;
+  constexpr int KW = T::KW;
+  constexpr int bits = Fmt<S>::bits;
+  constexpr int PB = param_bytes_per_group(S);
+  constexpr int NGRP = Params<S, G, KW>::NGRP;
+  // The activation buffers are separate LDS objects, so the compiler can tell
+  // the copies into one from the fragment reads of another.
+  constexpr int B23 = kNB == 4 ? T::BYTES : 16;
+  __shared__ __attribute__((aligned(16))) uint8_t lds0[T::BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t lds1[T::BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t lds2[B23];
+  __shared__ __attribute__((aligned(16))) uint8_t lds3[B23];
   __shared__ float nf4[16];
+  auto buffer = [&](int i) __attribute__((always_inline)) {
+    return i == 0 ? lds0 : i == 1 ? lds1 : i == 2 ? lds2 : lds3;
+  };
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // blockIdx.x: (split, tile_m, tile_n) with the split fastest, so the K
-  // pieces of one output tile run side by side
-  const int b = blockIdx.x;
-  const int split = b % splits, tile = b / splits;
-  const int tile_m = tile % tiles_m, tile_n = tile / tiles_m;
+  const int wn = wave % WGN, wk = wave / WGN;
+  const int b = xcd_order(blockIdx.x, nblocks);
+  const int tile_m = b % tiles_m, tile_n = b / tiles_m;
   const int bm = tile_m * BM;
-  const int steps = (k + kBK - 1) / kBK;
-  const int st0 = split * steps_per_split;
-  const int st1 = st0 + steps_per_split < steps ? st0 + steps_per_split : steps;
-  if (st0 >= st1) return;
-  const size_t rowb = size_t(k) * Fmt<S>::bits / 8;
+  const int steps = (k + T::KS - 1) / T::KS;
+  const size_t rowb = size_t(k) * bits / 8;
   const int ng = k / G;
   if constexpr (S == UQ_NF4) {
     if (tid < 16) nf4[tid] = nf4_value(tid);
   }
 
-  const int kh = lane >> 5, r32 = lane & 31;
-  int brow[2];
+  // Activation copy: thread tid moves 16-byte slot q = i * 512 + tid of the
+  // step's tile (row q / CPR, physical chunk q % CPR, which holds logical
+  // chunk (q % CPR) ^ (row & 7)).  RPI is a multiple of 8, so the logical
+  // chunk is the same for every i.
+  const int r0 = tid / T::CPR;
+  const int cl = (tid % T::CPR) ^ (r0 & 7);
+  const uint16_t* arow[T::LOADS];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int rr = tile_n * kBN + wave * kWN + t * 32 + r32;
-    brow[t] = rr < n ? rr : n - 1;
+  for (int i = 0; i < T::LOADS; ++i) {
+    int r = bm + i * T::RPI + r0;
+    r = r < m ? r : m - 1;  // rows past M: any valid row (their outputs are not stored)
+    arow[i] = xb + size_t(r) * size_t(k);
   }
 
-  f32x16 acc[TM][2];
+  // Weight rows of the lane's two 32-row tiles.
+  const int kh = lane >> 5, r32 = lane & 31;
+  const uint8_t* crow[2];
+  const uint8_t* prow[2];
 #pragma unroll
-  for (int a = 0; a < TM; ++a)
+  for (int t = 0; t < 2; ++t) {
+    int row = tile_n * T::BN + wn * 64 + t * 32 + r32;
+    row = row < n ? row : n - 1;  // rows past N: computed, not stored
+    crow[t] = codes + size_t(row) * rowb;
+    prow[t] = params + size_t(row) * size_t(ng) * PB;
+  }
+
+  f32x16 acc[T::TM][2];
+#pragma unroll
+  for (int a = 0; a < T::TM; ++a)
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int j = 0; j < 16; ++j) acc[a][t][j] = 0.0f;
 
-  // prologue: step st0 into buffer 0
-  AStage<BM> an;
-  BRegs<S, G> bn[2];
-  load_a<BM>(an, x, tid, bm, st0 * kBK, m, k);
-#pragma unroll
-  for (int t = 0; t < 2; ++t) load_b<S, G>(bn[t], codes, params, brow[t], st0 * kBK + 64 * kh, k, rowb, ng);
-  store_a<BM>(an, As[0], tid, bm, st0 * kBK, m, k);
-  __syncthreads();
+  // Prefetch: step st's activation tile goes to buffer st % kNB and its codes
+  // to register set st % kNB, issued kNB - 1 steps ahead (the step loop is
+  // unrolled by kNB, so nothing is copied).  Each step issues the tile's
+  // copies and then the codes, always (clamped to valid addresses past the
+  // last step: loads under a branch make the compiler wait for every load
+  // where the paths join).  Waiting for step st then means waiting until at
+  // most the kNB - 2 later steps' loads are outstanding.
+  constexpr int NT = T::LOADS;                         // copies per step
+  constexpr int NC = 2 * (code_loads<S, KW>() + 1);    // code + parameter loads per step
+  constexpr int NWAIT = (kNB - 2) * (NT + NC);
+  static_assert(NWAIT < 64, "vmcnt field");
+  Codes<S, KW> cs[kNB][2];        // [set][tile]
+  uint32_t ps[kNB][2][NGRP];      // [set][tile][group]
+  bool live[kNB] = {};
 
-  for (int st = st0; st < st1; ++st) {
-    const int buf = (st - st0) & 1;
-    BRegs<S, G> bc[2] = {bn[0], bn[1]};
-    const bool more = st + 1 < st1;
-    if (more) {  // next step's loads in flight during this step's MFMAs
-      load_a<BM>(an, x, tid, bm, (st + 1) * kBK, m, k);
+  auto issue = [&](int st, int set) __attribute__((always_inline)) {
+    int col = st * T::KS + 8 * cl;
+    col = col < k ? col : 0;  // past K: any valid chunk (the weights there are zeroed)
+    uint8_t* dst = buffer(set) + wave * 1024;
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
-        load_b<S, G>(bn[t], codes, params, brow[t], (st + 1) * kBK + 64 * kh, k, rowb, ng);
+    for (int i = 0; i < T::LOADS; ++i)
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(arow[i] + col),
+                                       (__attribute__((address_space(3))) void*)(dst + i * kThreads * 16), 16, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    const int k0 = st * T::KS + KW * wk + KW / 2 * kh;
+    live[set] = k0 < k;
+    const int kc = live[set] ? k0 : 0;  // past K: any valid slice (its weights are zeroed)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      load_codes<S, KW>(cs[set][t], crow[t] + size_t(kc) * bits / 8);
+      const uint8_t* pp = prow[t] + size_t(kc / G) * PB;
+      static_assert(NGRP <= 2 && (NGRP == 1 || PB == 4), "parameter load");
+      if constexpr (NGRP == 2) {
+        const uint2 v = *reinterpret_cast<const uint2*>(pp);  // kc / G is even: 8-byte aligned
+        ps[set][t][0] = v.x;
+        ps[set][t][1] = v.y;
+      } else if constexpr (PB == 4) {
+        ps[set][t][0] = *reinterpret_cast<const uint32_t*>(pp);
+      } else {
+        ps[set][t][0] = *reinterpret_cast<const uint16_t*>(pp);
+      }
     }
-    // Sub-steps are software-pipelined: while sub-step s's MFMAs run, the
-    // wave dequantizes sub-step s+1's weights and reads its activation
-    // fragments; the scheduling hints interleave one MFMA with a few VALU
-    // instructions so the matrix core and the VALU work at the same time.
-    const __bf16* Ab = As[buf];
-    bf16x8 bcur[2], acur[TM];
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // One K step from buffer and register set `set` = st % 4.  Sub-steps are
+  // software-pipelined: while sub-step s's MFMAs run, the wave reads sub-step
+  // s+1's activation fragments and dequantizes its weights; the scheduling
+  // hints interleave each MFMA with a share of that VALU work.
+  auto step = [&](int st, int set) __attribute__((always_inline)) {
+    // A plain s_barrier, not __syncthreads(): the fences of the latter wait for
+    // every outstanding load (vmcnt(0)), the prefetched steps included.  The
+    // waits go through the builtin so that the compiler's wait-count tracking
+    // sees them (it then knows the tile's copies are done and adds no wait of
+    // its own before the fragment reads).  The ds_reads of the previous step
+    // have all been consumed by its MFMAs, so lgkmcnt(0) is immediate.
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (NWAIT & 15) | ((NWAIT >> 4) << 14));  // vmcnt(NWAIT), gfx9 encoding
+    __builtin_amdgcn_s_waitcnt(0xC07F);                                         // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();  // step st's tile is in LDS for every wave; buffer (st-1) % kNB is free
+    asm volatile("" ::: "memory");
+    Params<S, G, KW> pc[2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) bcur[t] = dequant8<S, G>(bc[t], 0, nf4);
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int a = 0; a < TM; ++a)
-      acur[a] = *reinterpret_cast<const bf16x8*>(Ab + (a * 32 + r32) * kLdA + 64 * kh);
+      for (int j = 0; j < NGRP; ++j) {
+        const uint32_t v = live[set] ? ps[set][t][j] : 0u;  // K slice past K: w' = 0
+        if constexpr (S == UQ_NF4) {
+          pc[t].s[j] = h2f(uint16_t(v));
+          pc[t].z[j] = 0.0f;
+        } else {
+          pc[t].s[j] = h2f(uint16_t(v & 0xFFFFu));
+          pc[t].z[j] = h2f(uint16_t(v >> 16));
+        }
+      }
+    const Codes<S, KW> cc[2] = {cs[set][0], cs[set][1]};
+    issue(st + kNB - 1, (set + kNB - 1) % kNB);
+
+    const uint8_t* Ab = buffer(set) + r32 * T::CPR * 16;
+    auto afrag = [&](int a, int s) __attribute__((always_inline)) {
+      const int chunk = ((KW / 8) * wk + (KW / 16) * kh + s) ^ (r32 & 7);
+      return *reinterpret_cast<const bf16x8*>(Ab + (a * 32 * T::CPR + chunk) * 16);
+    };
+    bf16x8 acur[T::TM], bcur[2];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      bf16x8 bnxt[2], anxt[TM];
-      if (s < 7) {
+    for (int a = 0; a < T::TM; ++a) acur[a] = afrag(a, 0);
 #pragma unroll
-        for (int a = 0; a < TM; ++a)
-          anxt[a] = *reinterpret_cast<const bf16x8*>(Ab + (a * 32 + r32) * kLdA + 64 * kh + 8 * (s + 1));
+    for (int t = 0; t < 2; ++t) bcur[t] = dequant8<S, G, KW>(cc[t], pc[t], 0, nf4);
 #pragma unroll
-        for (int t = 0; t < 2; ++t) bnxt[t] = dequant8<S, G>(bc[t], s + 1, nf4);
+    for (int s = 0; s < T::SUB; ++s) {
+      bf16x8 anxt[T::TM], bnxt[2];
+      if (s + 1 < T::SUB) {
+#pragma unroll
+        for (int a = 0; a < T::TM; ++a) anxt[a] = afrag(a, s + 1);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) bnxt[t] = dequant8<S, G, KW>(cc[t], pc[t], s + 1, nf4);
       }
 #pragma unroll
-      for (int a = 0; a < TM; ++a)
+      for (int a = 0; a < T::TM; ++a)
 #pragma unroll
         for (int t = 0; t < 2; ++t)
           acc[a][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(acur[a], bcur[t], acc[a][t], 0, 0, 0);
-      if (s < 7) {
+      if (s + 1 < T::SUB) {
 #pragma unroll
-        for (int q = 0; q < 2 * TM; ++q) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);            // one MFMA
-          __builtin_amdgcn_sched_group_barrier(0x002, 48 / (2 * TM), 0); // then some VALU
-          if (q < TM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); // and an LDS read
+        for (int q = 0; q < 2 * T::TM; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                    // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 48 / (2 * T::TM), 0);     // a share of the VALU
+          if (q < T::TM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // and an LDS read
         }
 #pragma unroll
-        for (int t = 0; t < 2; ++t) bcur[t] = bnxt[t];
+        for (int a = 0; a < T::TM; ++a) acur[a] = anxt[a];
 #pragma unroll
-        for (int a = 0; a < TM; ++a) acur[a] = anxt[a];
+        for (int t = 0; t < 2; ++t) bcur[t] = bnxt[t];
       }
     }
-    if (more) store_a<BM>(an, As[buf ^ 1], tid, bm, (st + 1) * kBK, m, k);
-    __syncthreads();
+  };
+
+#pragma unroll
+  for (int j = 0; j < kNB - 1; ++j) issue(j, j);
+  // Whole rounds of kNB steps; the steps past K multiply by w' = 0.
+  for (int st = 0; st < steps; st += kNB) {
+#pragma unroll
+    for (int u = 0; u < kNB; ++u) step(st + u, u);
   }
 
-  // D layout of a 32x32 tile: lane l, element j -> row 8*(j/4) + 4*(l/32) + j%4,
-  // column l % 32.
-  const bool atomic = splits > 1;
+  // Sum the K slices: a halving tree through LDS (float4 per lane and
+  // element group, lane-major so the partner wave reads what it wrote).
+  constexpr int E4 = T::TM * 2 * 4;  // float4 per lane
+  constexpr int SB = E4 * 64 * 16;    // bytes of one wave's partial sums
+  static_assert(T::BYTES % SB == 0, "partial sums do not straddle the buffers");
+  auto slot = [&](int sl) __attribute__((always_inline)) {
+    const int off = sl * SB;
+    return reinterpret_cast<float4*>(buffer(off / T::BYTES) + off % T::BYTES) + lane;
+  };
+  __syncthreads();
 #pragma unroll
-  for (int a = 0; a < TM; ++a)
+  for (int half = T::WGK / 2; half >= 1; half /= 2) {
+    if (wk >= half && wk < 2 * half) {
+      float4* dst = slot((wk - half) * WGN + wn);
+#pragma unroll
+      for (int a = 0; a < T::TM; ++a)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int j4 = 0; j4 < 4; ++j4)
+            dst[((a * 2 + t) * 4 + j4) * 64] = make_float4(acc[a][t][4 * j4], acc[a][t][4 * j4 + 1],
+                                                           acc[a][t][4 * j4 + 2], acc[a][t][4 * j4 + 3]);
+    }
+    __syncthreads();
+    if (wk < half) {
+      const float4* src = slot(wk * WGN + wn);
+#pragma unroll
+      for (int a = 0; a < T::TM; ++a)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int j4 = 0; j4 < 4; ++j4) {
+            const float4 v = src[((a * 2 + t) * 4 + j4) * 64];
+            acc[a][t][4 * j4] += v.x;
+            acc[a][t][4 * j4 + 1] += v.y;
+            acc[a][t][4 * j4 + 2] += v.z;
+            acc[a][t][4 * j4 + 3] += v.w;
+          }
+    }
+    __syncthreads();
+  }
+  if (wk != 0) return;
+
+  // D layout of a 32x32 tile: lane l, element j -> row 8*(j/4) + 4*(l/32) + j%4
+  // (an x row), column l % 32 (a weight row).
+#pragma unroll
+  for (int a = 0; a < T::TM; ++a)
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const int col = tile_n * kBN + wave * kWN + t * 32 + r32;
+      const int col = tile_n * T::BN + wn * 64 + t * 32 + r32;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int row = bm + a * 32 + 8 * (j / 4) + 4 * kh + (j % 4);
-        if (row < m && col < n) {
-          float* dst = y + size_t(row) * size_t(n) + col;
-          if (atomic) unsafeAtomicAdd(dst, acc[a][t][j]);
-          else *dst = acc[a][t][j];
-        }
+        if (row < m && col < n) y[size_t(row) * size_t(n) + col] = acc[a][t][j];
       }
     }
 }
 
-__global__ __launch_bounds__(256) void zero_kernel(float* __restrict__ y, int64_t count) {
+// x (fp16) -> bf16, round to nearest even; 8 values per thread and pass.
+__global__ __launch_bounds__(256) void to_bf16_kernel(const uint16_t* __restrict__ x,
+                                                      uint16_t* __restrict__ xb, int64_t count8) {
   const int64_t stride = int64_t(gridDim.x) * 256;
-  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < count; i += stride) y[i] = 0.0f;
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < count8; i += stride) {
+    const uint4 h = reinterpret_cast<const uint4*>(x)[i];
+    uint4 o;
+    o.x = pack_bf16(h2f(uint16_t(h.x)), h2f(uint16_t(h.x >> 16)));
+    o.y = pack_bf16(h2f(uint16_t(h.y)), h2f(uint16_t(h.y >> 16)));
+    o.z = pack_bf16(h2f(uint16_t(h.z)), h2f(uint16_t(h.z >> 16)));
+    o.w = pack_bf16(h2f(uint16_t(h.w)), h2f(uint16_t(h.w >> 16)));
+    reinterpret_cast<uint4*>(xb)[i] = o;
+  }
 }
 
-template <int S, int G, int BM>
-hipError_t launch(const uq_layout* L, const void* codes, const void* params, const uint16_t* x,
-                  float* y, int m, hipStream_t stream) {
-  int n = int(L->n), k = int(L->k);
-  int tiles_m = (m + BM - 1) / BM, tiles_n = (n + kBN - 1) / kBN;
-  const int tiles = tiles_m * tiles_n;
-  const int steps = (k + kBK - 1) / kBK;
-  // Split K so that about 256 workgroups (one per CU) share the work.
-  int splits = (256 + tiles - 1) / tiles;
-  if (splits > steps) splits = steps;
-  if (splits < 1) splits = 1;
-  int steps_per_split = (steps + splits - 1) / splits;
-  splits = (steps + steps_per_split - 1) / steps_per_split;
-  if (splits > 1) {
-    int64_t count = int64_t(m) * n;
-    void* zargs[] = {&y, &count};
-    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&zero_kernel), dim3(1024), dim3(256),
-                                         zargs, 0, stream);
-    if (e != hipSuccess) return e;
+// Activation workspace, one per (device, stream) so calls on different
+// streams never share it; calls on one stream are ordered by the stream.  A
+// buffer that is outgrown stays allocated (a captured graph may still name
+// it) until the process ends; growth is at least 2x, so the retired buffers
+// add up to less than the live one.
+struct Workspace {
+  int device;
+  hipStream_t stream;
+  void* ptr;
+  size_t bytes;
+};
+std::mutex g_ws_mutex;
+std::vector<Workspace> g_ws;
+std::vector<void*> g_ws_retired;
+
+hipError_t activation_workspace(hipStream_t stream, size_t bytes, void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  Workspace* w = nullptr;
+  for (auto& it : g_ws)
+    if (it.device == dev && it.stream == stream) w = &it;
+  if (w && w->bytes >= bytes) {
+    *out = w->ptr;
+    return hipSuccess;
   }
+  // No allocation while the stream is being captured into a graph.
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  e = hipStreamIsCapturing(stream, &cap);
+  if (e != hipSuccess) return e;
+  if (cap != hipStreamCaptureStatusNone) return hipErrorStreamCaptureUnsupported;
+  size_t want = bytes < (size_t(1) << 20) ? (size_t(1) << 20) : bytes;
+  if (w && want < 2 * w->bytes) want = 2 * w->bytes;
+  void* p = nullptr;
+  e = hipMalloc(&p, want);
+  if (e != hipSuccess) return e;
+  if (w) {
+    g_ws_retired.push_back(w->ptr);
+    w->ptr = p;
+    w->bytes = want;
+  } else {
+    g_ws.push_back(Workspace{dev, stream, p, want});
+  }
+  *out = p;
+  return hipSuccess;
+}
+
+template <int S, int G, int BM, int WGN>
+hipError_t launch(const uq_layout* L, const void* codes, const void* params, const uint16_t* xb,
+                  float* y, int m, hipStream_t stream) {
+  using T = Tile<BM, WGN>;
+  int n = int(L->n), k = int(L->k);
+  int tiles_m = (m + BM - 1) / BM;
+  const int64_t tiles_n = (int64_t(n) + T::BN - 1) / T::BN;
+  const int64_t nb = int64_t(tiles_m) * tiles_n;
+  if (nb > 0x7fffffff) return hipErrorInvalidValue;
+  int nblocks = int(nb);
   const uint8_t* c8 = static_cast<const uint8_t*>(codes);
   const uint8_t* p8 = static_cast<const uint8_t*>(params);
-  void* args[] = {&c8, &p8, (void*)&x, &y, &n, &k, &m, &tiles_m, &splits, &steps_per_split};
-  const dim3 grid(unsigned(tiles * splits)), block(kThreads);
-  return hipLaunchKernel(reinterpret_cast<const void*>(&gemm_kernel<S, G, BM>), grid, block, args, 0, stream);
+  void* args[] = {&c8, &p8, (void*)&xb, &y, &n, &k, &m, &tiles_m, &nblocks};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&gemm_kernel<S, G, BM, WGN>), dim3(unsigned(nblocks)),
+                         dim3(kThreads), args, 0, stream);
 }
 
 template <int S, int G>
-hipError_t launch_bm(const uq_layout* L, const void* codes, const void* params, const uint16_t* x,
-                     float* y, int m, hipStream_t stream) {
-  if (m <= 32) return launch<S, G, 32>(L, codes, params, x, y, m, stream);
-  if (m <= 64) return launch<S, G, 64>(L, codes, params, x, y, m, stream);
-  return launch<S, G, 128>(L, codes, params, x, y, m, stream);
+hipError_t launch_tiles(const uq_layout* L, const void* codes, const void* params, const uint16_t* xb,
+                        float* y, int m, hipStream_t stream) {
+  if (m <= 32) return launch<S, G, 32, 1>(L, codes, params, xb, y, m, stream);
+  if (m <= 64) return launch<S, G, 64, 1>(L, codes, params, xb, y, m, stream);
+  return launch<S, G, 128, 2>(L, codes, params, xb, y, m, stream);
 }
 
 }  // namespace
 
 hipError_t launch_gemm(const uq_layout* L, const void* codes, const void* params, const uint16_t* x,
                        float* y, int m, hipStream_t stream) {
+  const int64_t count = int64_t(m) * L->k;  // k % 32 == 0: whole 8-value pieces
+  void* ws = nullptr;
+  hipError_t e = activation_workspace(stream, size_t(count) * 2, &ws);
+  if (e != hipSuccess) return e;
+  uint16_t* xb = static_cast<uint16_t*>(ws);
+  {
+    int64_t count8 = count / 8;
+    const int64_t want = (count8 + 255) / 256;
+    const unsigned grid = unsigned(want < 1024 ? want : 1024);
+    void* args[] = {(void*)&x, &xb, &count8};
+    e = hipLaunchKernel(reinterpret_cast<const void*>(&to_bf16_kernel), dim3(grid), dim3(256), args, 0, stream);
+    if (e != hipSuccess) return e;
+  }
   switch (L->scheme * 1000 + L->group) {
-    case UQ_INT2 * 1000 + 16: return launch_bm<UQ_INT2, 16>(L, codes, params, x, y, m, stream);
-    case UQ_INT2 * 1000 + 32: return launch_bm<UQ_INT2, 32>(L, codes, params, x, y, m, stream);
-    case UQ_INT2 * 1000 + 64: return launch_bm<UQ_INT2, 64>(L, codes, params, x, y, m, stream);
-    case UQ_INT2 * 1000 + 128: return launch_bm<UQ_INT2, 128>(L, codes, params, x, y, m, stream);
-    case UQ_INT4 * 1000 + 32: return launch_bm<UQ_INT4, 32>(L, codes, params, x, y, m, stream);
-    case UQ_INT4 * 1000 + 64: return launch_bm<UQ_INT4, 64>(L, codes, params, x, y, m, stream);
-    case UQ_INT4 * 1000 + 128: return launch_bm<UQ_INT4, 128>(L, codes, params, x, y, m, stream);
-    case UQ_INT8 * 1000 + 64: return launch_bm<UQ_INT8, 64>(L, codes, params, x, y, m, stream);
-    case UQ_INT8 * 1000 + 128: return launch_bm<UQ_INT8, 128>(L, codes, params, x, y, m, stream);
-    case UQ_NF4 * 1000 + 64: return launch_bm<UQ_NF4, 64>(L, codes, params, x, y, m, stream);
+    case UQ_INT2 * 1000 + 16: return launch_tiles<UQ_INT2, 16>(L, codes, params, xb, y, m, stream);
+    case UQ_INT2 * 1000 + 32: return launch_tiles<UQ_INT2, 32>(L, codes, params, xb, y, m, stream);
+    case UQ_INT2 * 1000 + 64: return launch_tiles<UQ_INT2, 64>(L, codes, params, xb, y, m, stream);
+    case UQ_INT2 * 1000 + 128: return launch_tiles<UQ_INT2, 128>(L, codes, params, xb, y, m, stream);
+    case UQ_INT4 * 1000 + 32: return launch_tiles<UQ_INT4, 32>(L, codes, params, xb, y, m, stream);
+    case UQ_INT4 * 1000 + 64: return launch_tiles<UQ_INT4, 64>(L, codes, params, xb, y, m, stream);
+    case UQ_INT4 * 1000 + 128: return launch_tiles<UQ_INT4, 128>(L, codes, params, xb, y, m, stream);
+    case UQ_INT8 * 1000 + 64: return launch_tiles<UQ_INT8, 64>(L, codes, params, xb, y, m, stream);
+    case UQ_INT8 * 1000 + 128: return launch_tiles<UQ_INT8, 128>(L, codes, params, xb, y, m, stream);
+    case UQ_NF4 * 1000 + 64: return launch_tiles<UQ_NF4, 64>(L, codes, params, xb, y, m, stream);
     default: return hipErrorInvalidValue;
   }
 }
