@@ -1,7 +1,7 @@
 // C ABI of libuq (declared in include/uq.h): argument validation, kernel
 // selection and launch on the caller's stream.  Validation always precedes
-// the first HIP call, and no entry point allocates, synchronizes or keeps
-// state.
+// the first HIP call; no entry point synchronizes, and only uq_gemm allocates
+// (its activation workspace, kept per device and stream).
 #include <hip/hip_runtime.h>
 
 #include <cstring>

@@ -36,13 +36,13 @@
  * Conventions for every call:
  *   - Validation runs before any HIP call.  On any status other than UQ_OK
  *     nothing was launched and no output was written.
- *   - The caller owns every buffer.  The library allocates no memory, keeps
- *     no mutable state, and never synchronizes: device calls are enqueued on
- *     `stream` (a hipStream_t; NULL means the null stream) and return at
- *     once.  Faults inside a kernel surface at the caller's next
- *     synchronization.
+ *   - The caller owns every buffer it passes.  Calls never synchronize:
+ *     device work is enqueued on `stream` (a hipStream_t; NULL means the null
+ *     stream) and the call returns at once.  Faults inside a kernel surface
+ *     at the caller's next synchronization.  Only uq_gemm allocates (see
+ *     there); every other call allocates nothing and keeps no state.
  *   - Outputs are overwritten, never accumulated into.
- *   - All functions are thread-safe (no shared state).
+ *   - All functions are thread-safe.
  */
 #ifndef UQ_H
 #define UQ_H
@@ -115,8 +115,17 @@ uq_status uq_gemv(const uq_layout* layout, const void* codes,
 /* Fused dequant + GEMM on the bf16 matrix cores for batched decode and
  * prefill (Core Components > Fused Kernels, GEMM during batched decode):
  *   y[m][n] = sum_k bf16(x[m][k]) * bf16(w'[n][k])  for 1 <= m <= UQ_GEMM_MAX_M
- * Both casts round to nearest even; products accumulate in fp32.
- * Arguments as for uq_gemv. */
+ * Both casts round to nearest even; products accumulate in fp32, in an order
+ * fixed by (layout, m), so repeated calls give identical bits.
+ * Arguments as for uq_gemv.
+ * Workspace: bf16(x) is staged in device memory the library owns, one buffer
+ * per (device, stream), m * k * 2 bytes, allocated with hipMalloc by the first
+ * call that needs it to be larger (at least doubling) and kept until the
+ * process ends.  Calls on one stream are ordered by the stream; calls on
+ * different streams use different buffers.  A call that would have to grow
+ * the buffer while `stream` is being captured into a graph returns
+ * UQ_ERR_HIP without launching: make one call of the largest m * k on that
+ * stream before capturing. */
 uq_status uq_gemm(const uq_layout* layout, const void* codes,
                   const void* params, const uint16_t* x, float* y, int64_t m,
                   void* stream);
