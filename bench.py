@@ -32,8 +32,13 @@ import workloads  # noqa: E402
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix cores, published
 METRIC = "dequant-GEMV weight GB/s & % HBM peak, INT4 g64 K=4096 N=11008 M=1"
-KERNEL_SOURCES = ("gemm_group_wise_amd/csrc/gemv_impl.hpp", "gemm_group_wise_amd/csrc/gemm.hip",
-                  "gemm_group_wise_amd/csrc/device_common.hpp")
+_CSRC = "gemm_group_wise_amd/csrc/"
+KERNEL_SOURCES = {  # what the timed kernel of each path is built from
+    "gemv": [_CSRC + f for f in ("gemv_impl.hpp", "device_common.hpp", "gemv.hip", "gemv_int2.hip",
+                                 "gemv_int4.hip", "gemv_int8.hip", "gemv_nf4.hip")],
+    "gemm": [_CSRC + f for f in ("gemm.hip", "device_common.hpp")],
+}
+CALIBRATION_MIB = 512          # plain copy used to scale the HBM byte counters
 
 
 def log(msg: str) -> None:
@@ -46,9 +51,9 @@ def weight_bytes(wl: workloads.Workload) -> int:
     return wl.n * wl.k * bits // 8 + wl.n * (wl.k // wl.group) * per_group
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(path: str) -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in KERNEL_SOURCES[path]:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -181,16 +186,95 @@ def cpu_baseline(wl: workloads.Workload, m: int, nbytes: int) -> dict:
                        f"elementwise steps single-threaded, product on {blas} BLAS threads")}
 
 
-def traffic_for(name: str, m: int):
+def traffic_path(name: str, m: int, ext: str) -> str:
+    return os.path.join(ROOT, "profiles", f"traffic_{name}_m{m}.{ext}")
+
+
+def traffic_for(wl: workloads.Workload, m: int):
     """HBM bytes per launch from committed rocprofv3 counter runs, if the kernel is unchanged."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{name}_m{m}.json")
+    path = traffic_path(wl.name, m, "json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_source_hash") != kernel_source_hash():
+    if t.get("kernel_source_hash") != kernel_source_hash(wl.path):
         return None
     return t.get("hbm_bytes_per_launch")
+
+
+def traffic_run(uq, wl: workloads.Workload, m: int, launches: int) -> None:
+    """The workload's kernel `launches` times (eager, rotated weights), then a plain
+    copy of CALIBRATION_MIB MiB five times; run under rocprofv3 --pmc."""
+    import torch
+    st = Setup(uq, wl, m, None)
+    sp = torch.cuda.current_stream().cuda_stream
+    for i in range(launches):
+        st.launch(i, sp)
+    torch.cuda.synchronize()
+    n = CALIBRATION_MIB * 2**20 // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        torch.mul(src, 1.0, out=dst)   # reads and writes CALIBRATION_MIB MiB
+    torch.cuda.synchronize()
+    log(f"traffic run: {launches} launches of {wl.name} m={m}, 5 calibration copies")
+
+
+def _counter_rows(directory: str, counter: str):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {directory}")
+    rows = []
+    with open(files[0]) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter:
+                rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    return rows
+
+
+def traffic_parse(wl: workloads.Workload, m: int, fetch_dir: str, write_dir: str, cmds: list[str]) -> dict:
+    """Scale the kernel's FETCH_SIZE / WRITE_SIZE (KiB per dispatch) by what the
+    same counters read for the calibration copy, and store the result."""
+    kernel = "gemv_kernel" if wl.path == "gemv" else "gemm_kernel"
+    known = CALIBRATION_MIB * 2**20
+    out = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _counter_rows(d, counter)
+        kv = [v for name, v in rows if kernel in name]
+        cv = [v for name, v in rows if "elementwise" in name and "MulFunctor" in name]
+        if not kv or not cv:
+            raise SystemExit(f"{counter}: kernel or calibration dispatches missing in {d}")
+        kib, cal = statistics.median(kv), statistics.median(cv)
+        factor = known / (cal * 1024.0)
+        out[counter] = {"kernel_kib_per_dispatch": kib, "dispatches": len(kv),
+                        "calibration_kib": cal, "calibration_bytes": known, "scale": round(factor, 4),
+                        "bytes_per_launch": round(kib * 1024.0 * factor)}
+    alg = weight_bytes(wl)
+    total = out["FETCH_SIZE"]["bytes_per_launch"] + out["WRITE_SIZE"]["bytes_per_launch"]
+    t = {"workload": wl.name, "m": m, "kernel": kernel, "kernel_source_hash": kernel_source_hash(wl.path),
+         "hbm_bytes_per_launch": total, "algorithmic_weight_bytes": alg,
+         "traffic_over_algorithmic": round(total / alg, 4), "counters": out, "commands": cmds}
+    with open(traffic_path(wl.name, m, "json"), "w") as f:
+        json.dump(t, f, indent=1)
+    f_, w_ = out["FETCH_SIZE"], out["WRITE_SIZE"]
+    md = [f"# HBM traffic of {kernel}: {wl.name}, M={m}", "",
+          "Commands (GPU box, repository root), one counter per run:", ""] + [f"    {c}" for c in cmds] + [
+          "", "| counter | kernel KiB/dispatch (median) | dispatches | calibration copy KiB | scale | bytes/launch |",
+          "|---|---|---|---|---|---|",
+          f"| FETCH_SIZE | {f_['kernel_kib_per_dispatch']:.1f} | {f_['dispatches']} | {f_['calibration_kib']:.0f} | "
+          f"{f_['scale']} | {f_['bytes_per_launch']:,} |",
+          f"| WRITE_SIZE | {w_['kernel_kib_per_dispatch']:.1f} | {w_['dispatches']} | {w_['calibration_kib']:.0f} | "
+          f"{w_['scale']} | {w_['bytes_per_launch']:,} |", "",
+          f"The calibration copy is torch.mul(src, 1.0, out=dst) over {CALIBRATION_MIB} MiB (reads and writes "
+          f"{known:,} bytes); scale = known bytes / counter bytes for that copy.  HBM traffic per launch "
+          f"{total:,} bytes against {alg:,} algorithmic weight bytes ({total / alg:.3f}x).", ""]
+    with open(traffic_path(wl.name, m, "md"), "w") as f:
+        f.write("\n".join(md))
+    log("\n".join(md))
+    return t
 
 
 def report_all(uq, steps: int, warmup: int, path: str | None) -> None:
@@ -226,18 +310,29 @@ def main() -> None:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--all", action="store_true", help="also time every workload (markdown)")
     ap.add_argument("--report", default=None)
+    ap.add_argument("--traffic-run", type=int, default=0, metavar="LAUNCHES",
+                    help="only launch the kernel LAUNCHES times plus a calibration copy (for rocprofv3 --pmc)")
+    ap.add_argument("--traffic-parse", nargs=2, default=None, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two rocprofv3 --pmc outputs (FETCH_SIZE, WRITE_SIZE) into profiles/traffic_*")
+    ap.add_argument("--traffic-cmd", action="append", default=[], help="command lines recorded with the result")
     args = ap.parse_args()
 
     if args.gpus != 1:
         raise SystemExit("bench.py measures one GPU: this build has no multi-GPU path "
                          "(the sharding plan is documented, not built); run with --gpus 1")
+    wl = workloads.WORKLOADS[args.workload]
+    m = args.m or wl.ms[0]
+    if args.traffic_parse:
+        traffic_parse(wl, m, args.traffic_parse[0], args.traffic_parse[1], args.traffic_cmd)
+        return
     import torch
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a ROCm GPU")
     import gemm_group_wise_amd as uq
 
-    wl = workloads.WORKLOADS[args.workload]
-    m = args.m or wl.ms[0]
+    if args.traffic_run:
+        traffic_run(uq, wl, m, args.traffic_run)
+        return
     st = Setup(uq, wl, m, args.rotate)
     torch.cuda.synchronize()
     ms, eager_ms = st.time(args.steps, args.warmup)
@@ -267,12 +362,12 @@ def main() -> None:
     }
     if wl.path == "gemv":
         out["roofline"] = {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                           "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic_for(wl.name, m)}
+                           "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic_for(wl, m)}
     else:
         tfl = 2.0 * m * wl.k * wl.n / (ms * 1e-3) / 1e12
         out["roofline"] = {"bound": "mfma", "achieved": round(tfl, 3), "peak": BF16_PEAK_TFLOPS,
                            "unit": "TFLOP/s", "frac": round(tfl / BF16_PEAK_TFLOPS, 4),
-                           "traffic": traffic_for(wl.name, m)}
+                           "traffic": traffic_for(wl, m)}
     if not args.no_cpu_baseline:
         log("timing the oracle on the host (cpu_baseline) ...")
         out["cpu_baseline"] = cpu_baseline(wl, m, st.bytes)
