@@ -184,6 +184,25 @@ __device__ __forceinline__ float wave_sum4(float a, float b, float c, float d) {
   return v;
 }
 
+// Loads of bytes a launch reads once (weight codes and group parameters):
+// the non-temporal hint marks the lines for early eviction, so the stream
+// does not push reused data (the activations) out of the caches.  Measured on
+// the INT4 GEMV: about 5 % less time per launch.
+template <typename T>
+__device__ __forceinline__ T load_stream(const void* p) {
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  if constexpr (sizeof(T) == 16) {
+    const u32x4 v = __builtin_nontemporal_load(static_cast<const u32x4*>(p));
+    return T{v.x, v.y, v.z, v.w};
+  } else if constexpr (sizeof(T) == 8) {
+    const u32x2 v = __builtin_nontemporal_load(static_cast<const u32x2*>(p));
+    return T{v.x, v.y};
+  } else {
+    return __builtin_nontemporal_load(static_cast<const T*>(p));
+  }
+}
+
 // Device copy of the NF4 codebook (one per code object).
 static __constant__ uint32_t kNf4Dev[16] = {
     kNf4Bits[0], kNf4Bits[1], kNf4Bits[2],  kNf4Bits[3],  kNf4Bits[4],  kNf4Bits[5],

@@ -61,22 +61,21 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<S, G, R>& cr, const uint8_t
   using Gm = Geo<S, G>;
   constexpr int PB = Gm::NF ? 2 : 4;  // bytes of one group's parameters
 #pragma unroll
-  for (int r = 0; r < R; ++r)
-    cr.code[r] = *reinterpret_cast<const uint4*>(cbase + roff[r] + uint32_t(chunk) * 16u);
+  for (int r = 0; r < R; ++r) cr.code[r] = load_stream<uint4>(cbase + roff[r] + uint32_t(chunk) * 16u);
   const uint32_t gb = uint32_t(chunk) * Gm::CW / G * PB;  // first group of the chunk, in bytes
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const uint8_t* p = pbase + poff[r] + gb;
     if constexpr (Gm::NF) {
-      cr.par[r][0] = *reinterpret_cast<const uint16_t*>(p);
+      cr.par[r][0] = load_stream<uint16_t>(p);
     } else if constexpr (Gm::PPC == 1) {
-      cr.par[r][0] = *reinterpret_cast<const uint32_t*>(p);
+      cr.par[r][0] = load_stream<uint32_t>(p);
     } else if constexpr (Gm::PPC == 2) {
-      const uint2 v = *reinterpret_cast<const uint2*>(p);
+      const uint2 v = load_stream<uint2>(p);
       cr.par[r][0] = v.x;
       cr.par[r][1] = v.y;
     } else {
-      const uint4 v = *reinterpret_cast<const uint4*>(p);
+      const uint4 v = load_stream<uint4>(p);
       cr.par[r][0] = v.x;
       cr.par[r][1] = v.y;
       cr.par[r][2] = v.z;
