@@ -37,7 +37,7 @@ class Workload:
         return max(self.ms)
 
 
-# The five workloads (names say what they are).
+# The workloads (names say what they are).
 WORKLOADS = {
     "int4_g32_k256_n768": Workload(
         "int4_g32_k256_n768", "int4", 32, 256, 768, (1,),
@@ -57,6 +57,16 @@ WORKLOADS = {
     "int4_g128_k4096_n11008_gemm": Workload(
         "int4_g128_k4096_n11008_gemm", "int4", 128, 4096, 11008, (16, 64, 256),
         path="gemm", note="batched decode / prefill"),
+    # The same GEMM for the other schemes, on the GEMV workloads' matrices.
+    "int8_g128_k4096_n4096_gemm": Workload(
+        "int8_g128_k4096_n4096_gemm", "int8", 128, 4096, 4096, (64, 256), seed=1,
+        path="gemm", note="attention q/o projection, batched"),
+    "int2_g16_k4096_n4096_gemm": Workload(
+        "int2_g16_k4096_n4096_gemm", "int2", 16, 4096, 4096, (64, 256), seed=2,
+        path="gemm", note="attention q/o projection, batched"),
+    "nf4_g64_k4096_n14336_gemm": Workload(
+        "nf4_g64_k4096_n14336_gemm", "nf4", 64, 4096, 14336, (64, 256), seed=3,
+        path="gemm", note="wide MLP projection, batched"),
 }
 
 # The workload the headline throughput figure is quoted on.
