@@ -1,9 +1,13 @@
-"""Reference oracle for group-wise weight quantization and dequant-GEMV/GEMM.
+"""Reference oracle for group-wise weight quantization, dequant-GEMV/GEMM and
+the fused RMSNorm + RoPE step.
 
 TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
 CPU-baseline leg of the benchmark may import this package.  The product path
 (the HIP library and its Python binding) never imports it, and this package
 imports nothing from the product path.
 """
+from . import norm_rope, uq_oracle
+from .norm_rope import *  # noqa: F401,F403
 from .uq_oracle import *  # noqa: F401,F403
-from .uq_oracle import __all__  # noqa: F401
+
+__all__ = list(uq_oracle.__all__) + list(norm_rope.__all__)

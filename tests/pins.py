@@ -291,3 +291,100 @@ def check_fp16_conversion(seed=0):
     # hand values: 1 + 2^-11 is halfway -> 1.0; 1 + 3*2^-11 -> 1 + 2^-9
     hv = np.array([1 + 2 ** -11, 1 + 3 * 2 ** -11, 2 ** -4], dtype=np.float32)
     assert hv.astype(np.float16).view(np.uint16).tolist() == [0x3C00, 0x3C02, 0x2C00]
+
+
+# ---------------------------------------------------------------------------
+# RMSNorm + RoPE (oracle/norm_rope.py): closed forms and brute force
+# ---------------------------------------------------------------------------
+COS1, SIN1 = 0.5403023058681398, 0.8414709848078965      # cos 1, sin 1 (radians)
+COS2, SIN2 = -0.4161468365471424, 0.9092974268256817     # cos 2, sin 2
+
+
+def check_rope_table(o):
+    """Row 0 is the identity; known angles give the textbook cosines and sines."""
+    cos, sin = o.rope_table(10000.0, 8, 201)
+    assert cos.shape == (201, 4) and cos.dtype == np.float32 and sin.dtype == np.float32
+    assert (cos[0] == 1).all() and (sin[0] == 0).all()
+    # pair 0 turns by p radians; pair 2 of 4 (d = 8) by p / 100
+    assert cos[1, 0] == np.float32(COS1) and sin[1, 0] == np.float32(SIN1)
+    assert cos[100, 2] == np.float32(COS1) and sin[100, 2] == np.float32(SIN1)
+    assert cos[200, 2] == np.float32(COS2) and sin[200, 2] == np.float32(SIN2)
+    assert cos[2, 0] == np.float32(COS2) and sin[2, 0] == np.float32(SIN2)
+    unit = cos.astype(np.float64) ** 2 + sin.astype(np.float64) ** 2
+    assert np.abs(unit - 1).max() <= 2.0 ** -22
+
+
+def check_rmsnorm_identity(o, seed=0):
+    """At position 0 the rotation is the identity, so y is the RMSNorm alone."""
+    rng = np.random.default_rng(seed)
+    d = 16
+    cos, sin = o.rope_table(10000.0, d, 4)
+    x = rng.standard_normal((5, 3, d)).astype(np.float16)
+    pos = np.zeros(5, dtype=np.int64)
+    y = o.rmsnorm_rope(x, np.ones(d, np.float32), pos, cos, sin, 0.0)
+    assert np.abs(np.sqrt(np.mean(y * y, axis=-1)) - 1).max() <= 1e-12
+    y2 = o.rmsnorm_rope((x.astype(np.float32) * 2).astype(np.float16), np.ones(d, np.float32), pos, cos, sin, 0.0)
+    assert np.abs(y2 - y).max() <= 1e-12                       # scale invariance
+    eps = np.float32(0.25)
+    ye = o.rmsnorm_rope(x, np.ones(d, np.float32), pos, cos, sin, eps)
+    xf = x.astype(np.float64)
+    ms = np.mean(xf * xf, axis=-1)
+    want = np.sqrt(ms / (ms + np.float64(eps)))                # rms of the output, closed form
+    assert np.abs(np.sqrt(np.mean(ye * ye, axis=-1)) - want).max() <= 1e-12
+    g = rng.uniform(0.5, 1.5, d).astype(np.float32)
+    yg = o.rmsnorm_rope(x, g, pos, cos, sin, 0.0)
+    assert np.abs(yg - y * g.astype(np.float64)).max() <= 1e-12
+
+
+def check_rope_pair_norms(o, seed=1):
+    """(a c - b s)^2 + (b c + a s)^2 = (a^2 + b^2)(c^2 + s^2) for every pair (i, i + D/2)."""
+    rng = np.random.default_rng(seed)
+    d, h = 32, 16
+    cos, sin = o.rope_table(10000.0, d, 512)
+    x = rng.standard_normal((7, 4, d)).astype(np.float16)
+    g = rng.uniform(0.5, 1.5, d).astype(np.float32)
+    pos = rng.integers(0, 512, 7)
+    y = o.rmsnorm_rope(x, g, pos, cos, sin, 1e-5)
+    u = o.rmsnorm_rope(x, g, np.zeros(7, dtype=np.int64), cos, sin, 1e-5)
+    c = cos[pos].astype(np.float64)[:, None, :]
+    s = sin[pos].astype(np.float64)[:, None, :]
+    lhs = y[..., :h] ** 2 + y[..., h:] ** 2
+    rhs = (u[..., :h] ** 2 + u[..., h:] ** 2) * (c * c + s * s)
+    assert np.abs(lhs - rhs).max() <= 1e-12 * rhs.max()
+
+
+def check_rope_composition(o, seed=2):
+    """Turning by p1 and then by p2 equals turning by p1 + p2 (angle addition)."""
+    rng = np.random.default_rng(seed)
+    d = 16
+    cos, sin = o.rope_table(10000.0, d, 300)
+    x = rng.standard_normal((6, 2, d)).astype(np.float16)
+    one = np.ones(d, np.float32)
+    p1, p2 = rng.integers(0, 150, 6), rng.integers(0, 150, 6)
+    y1 = o.rmsnorm_rope(x, one, p1, cos, sin, 0.0)              # rms 1 afterwards
+    y12 = o.rmsnorm_rope(y1, one, p2, cos, sin, 0.0)
+    y3 = o.rmsnorm_rope(x, one, p1 + p2, cos, sin, 0.0)
+    assert np.abs(y12 - y3).max() <= 2e-6                      # fp32 table entries
+
+
+def check_rope_bruteforce(o, seed=3):
+    """Scalar loops with explicit 2x2 rotations from math.cos / math.sin."""
+    import math
+    rng = np.random.default_rng(seed)
+    d, h, theta, eps = 6, 3, 10000.0, 1e-3
+    cos, sin = o.rope_table(theta, d, 64)
+    x = rng.standard_normal((4, 2, d)).astype(np.float16)
+    g = rng.uniform(0.5, 1.5, d).astype(np.float32)
+    pos = rng.integers(0, 64, 4)
+    y = o.rmsnorm_rope(x, g, pos, cos, sin, eps)
+    for t in range(4):
+        for hh in range(2):
+            v = [float(a) for a in x[t, hh]]
+            r = 1.0 / math.sqrt(sum(a * a for a in v) / d + float(np.float32(eps)))
+            u = [v[i] * r * float(g[i]) for i in range(d)]
+            for i in range(h):
+                ang = float(pos[t]) * theta ** (-2.0 * i / d)
+                c, s = math.cos(ang), math.sin(ang)
+                ya = u[i] * c - u[i + h] * s
+                yb = u[i + h] * c + u[i] * s
+                assert abs(y[t, hh, i] - ya) <= 1e-6 and abs(y[t, hh, i + h] - yb) <= 1e-6, (t, hh, i)

@@ -99,3 +99,34 @@ def test_roundtrip_bound_nf4_full():
 def test_roundtrip_nf4_small():
     w, _ = workloads.make_random(64, 512, 1, seed=3, outliers=True)
     pins.check_roundtrip_nf4(o, w, 64)
+
+
+# ---------------------------------------------------------------------------
+# RMSNorm + RoPE
+# ---------------------------------------------------------------------------
+def test_rope_table():
+    pins.check_rope_table(o)
+
+
+def test_rmsnorm_identity():
+    pins.check_rmsnorm_identity(o)
+
+
+def test_rope_pair_norms():
+    pins.check_rope_pair_norms(o)
+
+
+def test_rope_composition():
+    pins.check_rope_composition(o)
+
+
+def test_rope_bruteforce():
+    pins.check_rope_bruteforce(o)
+
+
+def test_fp16_spacing():
+    import torch
+    v = np.array([1.0, 1.5, 2.0, 3.0e-3, 1.0e-6, 60000.0, 6.1e-5])
+    t = torch.tensor(v, dtype=torch.float16)
+    nxt = torch.nextafter(t, torch.tensor(np.inf, dtype=torch.float16)).double().numpy()
+    assert np.array_equal(o.fp16_spacing(v), nxt - t.double().numpy())

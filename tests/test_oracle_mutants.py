@@ -91,6 +91,45 @@ def bf16_truncate(a):
     return (u & np.uint32(0xFFFF0000)).view(np.float32)
 
 
+def rope_interleaved(x16, gamma, pos, cos, sin, eps):
+    # pairs (2i, 2i+1) instead of (i, i + D/2)
+    y = o.rmsnorm_rope(x16, gamma, np.zeros_like(pos), cos, sin, eps)
+    c = cos[pos].astype(np.float64)[:, None, :]
+    s = sin[pos].astype(np.float64)[:, None, :]
+    a, b = y[..., 0::2], y[..., 1::2]
+    out = np.empty_like(y)
+    out[..., 0::2], out[..., 1::2] = a * c - b * s, b * c + a * s
+    return out
+
+
+def rope_sin_flipped(x16, gamma, pos, cos, sin, eps):
+    return o.rmsnorm_rope(x16, gamma, pos, cos, -sin, eps)
+
+
+def rmsnorm_sum(x16, gamma, pos, cos, sin, eps):
+    # sum of squares instead of the mean
+    d = x16.shape[-1]
+    return o.rmsnorm_rope(x16, gamma, pos, cos, sin, eps) / np.sqrt(d)
+
+
+def rmsnorm_eps_outside(x16, gamma, pos, cos, sin, eps):
+    x = x16.astype(np.float64)
+    r = np.sqrt(np.mean(x * x, axis=-1, keepdims=True))
+    xr = x / (r + np.float64(np.float32(eps))) * r / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + 0.0)
+    return o.rmsnorm_rope(xr, gamma, pos, cos, sin, 0.0) * (r / (r + np.float64(np.float32(eps))))
+
+
+def rope_gamma_after(x16, gamma, pos, cos, sin, eps):
+    y = o.rmsnorm_rope(x16, np.ones_like(gamma), pos, cos, sin, eps)
+    return y * np.asarray(gamma, np.float64)
+
+
+def rope_table_wrong_exponent(theta, d, max_pos):
+    i = np.arange(d // 2, dtype=np.float64)
+    ang = np.arange(max_pos, dtype=np.float64)[:, None] * (theta ** (-i / d))[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
 CASES = [
     ("dequant drops the zero term", dict(dequant_int=dequant_drop_zero),
      lambda ns: pins.check_grid_recovery(ns, 4, 64)),
@@ -115,6 +154,18 @@ CASES = [
      lambda ns: pins.check_products_exact(ns)),
     ("bf16 truncates", dict(bf16_rne=bf16_truncate),
      lambda ns: pins.check_bf16(ns)),
+    ("RoPE pairs neighbours", dict(rmsnorm_rope=rope_interleaved),
+     lambda ns: pins.check_rope_bruteforce(ns)),
+    ("RoPE turns the wrong way", dict(rmsnorm_rope=rope_sin_flipped),
+     lambda ns: pins.check_rope_bruteforce(ns)),
+    ("RMSNorm uses the sum", dict(rmsnorm_rope=rmsnorm_sum),
+     lambda ns: pins.check_rmsnorm_identity(ns)),
+    ("RMSNorm adds eps outside the root", dict(rmsnorm_rope=rmsnorm_eps_outside),
+     lambda ns: pins.check_rmsnorm_identity(ns)),
+    ("RMSNorm gain applied after RoPE", dict(rmsnorm_rope=rope_gamma_after),
+     lambda ns: pins.check_rope_bruteforce(ns)),
+    ("RoPE frequencies theta^(-i/D)", dict(rope_table=rope_table_wrong_exponent),
+     lambda ns: pins.check_rope_table(ns)),
 ]
 
 
