@@ -277,6 +277,47 @@ def traffic_parse(wl: workloads.Workload, m: int, fetch_dir: str, write_dir: str
     return t
 
 
+class NormRopeSetup:
+    """Fused RMSNorm + RoPE inputs (rotated device copies of x and y) for one workload."""
+
+    def __init__(self, uq, wl: workloads.NormRopeWorkload):
+        import torch
+        self.uq, self.wl = uq, wl
+        x, gamma, pos = workloads.make_norm_rope(wl)
+        self.x_host, self.gamma_host, self.pos_host = x, gamma, pos
+        cos, sin = uq.uq_rope_table(wl.theta, wl.head_dim, wl.max_pos)
+        vec_bytes = x.nbytes
+        # x read + y written + the table rows and positions of every token + gamma
+        self.bytes = 2 * vec_bytes + wl.tokens * (wl.head_dim // 2) * 8 + wl.tokens * 4 + wl.head_dim * 4
+        self.rotate = min(256, max(4, math.ceil(320e6 / (2 * vec_bytes))))
+        xd = torch.from_numpy(x.view(np.int16)).cuda()
+        self.x = [xd] + [xd.clone() for _ in range(self.rotate - 1)]
+        self.y = [torch.empty_like(xd) for _ in range(self.rotate)]
+        self.gamma = torch.from_numpy(gamma).cuda()
+        self.pos = torch.from_numpy(pos).cuda()
+        self.cos, self.sin = torch.from_numpy(cos).cuda(), torch.from_numpy(sin).cuda()
+        torch.cuda.synchronize()
+
+    def launch(self, i: int, stream: int) -> None:
+        j = i % self.rotate
+        wl = self.wl
+        self.uq.uq_rmsnorm_rope(self.x[j], self.y[j], self.gamma, self.pos, self.cos, self.sin, wl.tokens,
+                                wl.heads, wl.head_dim, wl.max_pos, wl.eps, stream=stream)
+
+    graph = Setup.graph
+    time = Setup.time
+
+    def check_sample(self) -> float:
+        """The whole output of the first copy against the oracle, within one fp16 spacing."""
+        import oracle as o
+        y = self.y[0].cpu().numpy().view(np.float16).astype(np.float64)
+        cos, sin = o.rope_table(self.wl.theta, self.wl.head_dim, self.wl.max_pos)
+        ref = o.rmsnorm_rope(self.x_host, self.gamma_host, self.pos_host, cos, sin, self.wl.eps)
+        if not o.within_gate(y.reshape(ref.shape), ref).all():
+            raise SystemExit(f"bench output of {self.wl.name} fails parity")
+        return float(np.linalg.norm(y - ref) / np.linalg.norm(ref))
+
+
 def report_all(uq, steps: int, warmup: int, path: str | None) -> None:
     rows = ["| workload | path | M | weight MB | us/launch | weight GB/s | % HBM | TFLOP/s | % bf16 MFMA |",
             "|---|---|---|---|---|---|---|---|---|"]
@@ -292,6 +333,17 @@ def report_all(uq, steps: int, warmup: int, path: str | None) -> None:
                         f"{gbs:.0f} | {100 * gbs / HBM_PEAK_GBS:.1f} | {tfl:.2f} | {mfma} |")
             log(rows[-1])
             del st
+    rows += ["", "| fused RMSNorm + RoPE | tokens | heads | head_dim | MB moved | us/launch | GB/s | % HBM |",
+             "|---|---|---|---|---|---|---|---|"]
+    for name, wl in workloads.NORM_ROPE.items():
+        st = NormRopeSetup(uq, wl)
+        ms, _ = st.time(steps, warmup)
+        st.check_sample()
+        gbs = st.bytes / (ms * 1e-3) / 1e9
+        rows.append(f"| {name} | {wl.tokens} | {wl.heads} | {wl.head_dim} | {st.bytes / 1e6:.2f} | "
+                    f"{ms * 1e3:.2f} | {gbs:.0f} | {100 * gbs / HBM_PEAK_GBS:.1f} |")
+        log(rows[-1])
+        del st
     text = "\n".join(rows) + "\n"
     log(text)
     if path:

@@ -1,4 +1,5 @@
-"""gemm_group_wise_amd -- fused group-wise dequant + GEMV/GEMM for MI355X (gfx950).
+"""gemm_group_wise_amd -- fused group-wise dequant + GEMV/GEMM (and the fused
+RMSNorm + RoPE step) for MI355X (gfx950).
 
 The compute lives in ``libuq.so`` (HIP kernels behind the C ABI of
 ``include/uq.h``); this package is its thin Python binding.  Importing it
@@ -7,5 +8,5 @@ without a built library raises ImportError.
 from ._binding import (  # noqa: F401
     BITS, EXPORTS, GEMM_MAX_M, GEMV_MAX_M, LIB_PATH, SCHEMES, Layout, UQError,
     layout, raw_call, uq_dequant, uq_gemm, uq_gemv, uq_nf4_codebook, uq_pack_weights,
-    uq_packed_size, uq_status_str,
+    uq_packed_size, uq_rmsnorm_rope, uq_rope_table, uq_status_str,
 )

@@ -63,14 +63,17 @@ _lib.uq_gemv.argtypes = [_L, _P, _P, _P, _P, ctypes.c_int64, _P]
 _lib.uq_gemm.argtypes = [_L, _P, _P, _P, _P, ctypes.c_int64, _P]
 _lib.uq_dequant.argtypes = [_L, _P, _P, _P, _P]
 _lib.uq_nf4_codebook.argtypes = [_P]
+_lib.uq_rope_table.argtypes = [ctypes.c_double, ctypes.c_int32, ctypes.c_int64, _P, _P]
+_lib.uq_rmsnorm_rope.argtypes = [_P, _P, _P, _P, _P, _P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                 ctypes.c_int64, ctypes.c_float, _P]
 _lib.uq_status_str.argtypes = [ctypes.c_int]
 _lib.uq_status_str.restype = ctypes.c_char_p
 for _fn in ("uq_packed_size", "uq_pack_weights", "uq_gemv", "uq_gemm", "uq_dequant",
-            "uq_nf4_codebook"):
+            "uq_nf4_codebook", "uq_rope_table", "uq_rmsnorm_rope"):
     getattr(_lib, _fn).restype = ctypes.c_int
 
 EXPORTS = ("uq_packed_size", "uq_pack_weights", "uq_gemv", "uq_gemm", "uq_dequant",
-           "uq_nf4_codebook", "uq_status_str")
+           "uq_nf4_codebook", "uq_rope_table", "uq_rmsnorm_rope", "uq_status_str")
 
 
 def _check(fn: str, status: int):
@@ -134,6 +137,23 @@ def uq_gemm(lay: Layout, codes, params, x, y, m: int, stream=None) -> None:
 def uq_dequant(lay: Layout, codes, params, w, stream=None) -> None:
     _check("uq_dequant", _lib.uq_dequant(ctypes.byref(lay), _ptr(codes), _ptr(params), _ptr(w),
                                          _stream(stream)))
+
+
+def uq_rope_table(theta: float, head_dim: int, max_pos: int) -> tuple[np.ndarray, np.ndarray]:
+    """Host rotary table: (cos, sin), each fp32 [max_pos, head_dim // 2]."""
+    cos = np.empty((max_pos, head_dim // 2), dtype=np.float32)
+    sin = np.empty_like(cos)
+    _check("uq_rope_table", _lib.uq_rope_table(float(theta), int(head_dim), int(max_pos),
+                                               cos.ctypes.data, sin.ctypes.data))
+    return cos, sin
+
+
+def uq_rmsnorm_rope(x, y, gamma, pos, cos, sin, tokens: int, heads: int, head_dim: int, max_pos: int,
+                    eps: float, stream=None) -> None:
+    """Fused RMSNorm + RoPE on device buffers (x, y fp16 [tokens, heads, head_dim]; y may be x)."""
+    _check("uq_rmsnorm_rope", _lib.uq_rmsnorm_rope(_ptr(x), _ptr(y), _ptr(gamma), _ptr(pos), _ptr(cos),
+                                                   _ptr(sin), int(tokens), int(heads), int(head_dim),
+                                                   int(max_pos), float(eps), _stream(stream)))
 
 
 def uq_nf4_codebook() -> np.ndarray:

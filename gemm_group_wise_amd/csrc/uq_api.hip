@@ -15,6 +15,9 @@ hipError_t launch_gemm(const uq_layout* L, const void* codes, const void* params
                        float* y, int m, hipStream_t stream);
 hipError_t launch_dequant(const uq_layout* L, const void* codes, const void* params, float* w,
                           hipStream_t stream);
+hipError_t launch_rmsnorm_rope(const uint16_t* x, uint16_t* y, const float* gamma, const int32_t* pos,
+                               const float* cos_tab, const float* sin_tab, int64_t tokens, int32_t heads,
+                               int32_t head_dim, int64_t max_pos, float eps, hipStream_t stream);
 
 namespace {
 
@@ -74,6 +77,27 @@ uq_status uq_dequant(const uq_layout* layout, const void* codes, const void* par
   if (!codes || !params || !w) return UQ_ERR_NULL;
   if (!uq::aligned16(codes) || !uq::aligned16(params) || !uq::aligned16(w)) return UQ_ERR_ALIGN;
   const hipError_t e = uq::launch_dequant(layout, codes, params, w, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? UQ_OK : UQ_ERR_HIP;
+}
+
+uq_status uq_rope_table(double theta, int32_t head_dim, int64_t max_pos, float* cos, float* sin) {
+  return uq::rope_table(theta, head_dim, max_pos, cos, sin);
+}
+
+uq_status uq_rmsnorm_rope(const uint16_t* x, uint16_t* y, const float* gamma, const int32_t* pos,
+                          const float* cos, const float* sin, int64_t tokens, int32_t heads,
+                          int32_t head_dim, int64_t max_pos, float eps, void* stream) {
+  if (!x || !y || !gamma || !pos || !cos || !sin) return UQ_ERR_NULL;
+  if (!uq::rope_head_dim_supported(head_dim)) return UQ_ERR_UNSUPPORTED;
+  if (tokens < 0 || heads < 1 || max_pos < 1 || max_pos > (int64_t(1) << 24)) return UQ_ERR_SHAPE;
+  if (tokens > (int64_t(1) << 40) / (int64_t(heads) * head_dim)) return UQ_ERR_SHAPE;
+  if (!(eps >= 0.0f) || !(eps <= 3.4e38f)) return UQ_ERR_RANGE;  // also rejects NaN
+  if (!uq::aligned16(x) || !uq::aligned16(y) || !uq::aligned16(gamma) || !uq::aligned16(cos) ||
+      !uq::aligned16(sin) || (reinterpret_cast<uintptr_t>(pos) & 3u))
+    return UQ_ERR_ALIGN;
+  if (tokens == 0) return UQ_OK;
+  const hipError_t e = uq::launch_rmsnorm_rope(x, y, gamma, pos, cos, sin, tokens, heads, head_dim, max_pos, eps,
+                                               static_cast<hipStream_t>(stream));
   return e == hipSuccess ? UQ_OK : UQ_ERR_HIP;
 }
 

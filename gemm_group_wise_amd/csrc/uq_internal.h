@@ -66,4 +66,10 @@ inline size_t param_row_bytes(const uq_layout* L) {
 uq_status pack_weights(const uq_layout* L, const float* w, uint8_t* codes,
                        uint16_t* params);
 
+// Host rotary table (rope_table.cpp).
+uq_status rope_table(double theta, int32_t head_dim, int64_t max_pos, float* cos_out, float* sin_out);
+
+// Head dimensions the fused RMSNorm + RoPE kernel serves.
+constexpr bool rope_head_dim_supported(int32_t d) { return d == 64 || d == 128 || d == 256 || d == 512; }
+
 }  // namespace uq

@@ -139,6 +139,39 @@ uq_status uq_dequant(const uq_layout* layout, const void* codes,
 /* The 16 NF4 codebook entries (fp32) the library uses; host call. */
 uq_status uq_nf4_codebook(float out[16]);
 
+/* ---- RMSNorm followed by RoPE (Core Components > Fused Kernels, third
+ * bullet; the Architecture diagram's "RMSNorm + RoPE" step of each layer). ----
+ *
+ * Rotary table for uq_rmsnorm_rope, host call:
+ *   cos[p][i] = fp32(cos(p * theta^(-2i/head_dim))), sin likewise, for
+ *   0 <= p < max_pos, 0 <= i < head_dim/2; the angle is formed in fp64 and
+ *   rounded once.  cos, sin: host fp32 [max_pos][head_dim/2], written.
+ * UQ_ERR_SHAPE unless head_dim is even and >= 2, 1 <= max_pos <= 2^24 and
+ * theta > 0 is finite. */
+uq_status uq_rope_table(double theta, int32_t head_dim, int64_t max_pos,
+                        float* cos, float* sin);
+
+/* Fused RMSNorm + RoPE over vectors of head_dim values:
+ *   u = x / sqrt(mean(x^2) + eps) * gamma           (over the head_dim values)
+ *   y[i] = u[i] c - u[i+h] s,  y[i+h] = u[i+h] c + u[i] s,  i < h = head_dim/2,
+ *   with c = cos[pos[t]][i], s = sin[pos[t]][i] for token t.
+ *   x     : device fp16 [tokens][heads][head_dim] (uint16 bit patterns), 16-byte aligned
+ *   y     : device fp16, same shape; may be x itself (in place)
+ *   gamma : device fp32 [head_dim], 16-byte aligned
+ *   pos   : device int32 [tokens], each in [0, max_pos)
+ *   cos, sin : device fp32 [max_pos][head_dim/2] (e.g. from uq_rope_table), 16-byte aligned
+ *   head_dim in {64, 128, 256, 512}; tokens >= 0 (0 launches nothing); heads >= 1;
+ *   eps finite and >= 0.
+ * Computed in fp32, rounded to fp16 (nearest even) once: within one fp16
+ * spacing of the exact result, plus fp32 rounding at the vector's scale
+ * (2^-18 of its largest output) where cancellation makes a value tiny.  A token whose position lies outside
+ * [0, max_pos) gets NaN in every output value (the host cannot see device
+ * positions; the kernel never reads outside the table). */
+uq_status uq_rmsnorm_rope(const uint16_t* x, uint16_t* y, const float* gamma,
+                          const int32_t* pos, const float* cos, const float* sin,
+                          int64_t tokens, int32_t heads, int32_t head_dim,
+                          int64_t max_pos, float eps, void* stream);
+
 /* Static, NUL-terminated name of a status code ("UQ_OK", ...). */
 const char* uq_status_str(uq_status status);
 

@@ -21,14 +21,16 @@ steps and fixes none of their arithmetic, so each step below is a reading:
         built once: each entry is the fp32 rounding (to nearest even) of the
         cosine / sine of the angle formed exactly (fp64).  Kernel and oracle
         read the same table; the table builder is checked against closed forms.
-  R-RO  x and y are fp16, gamma fp32; the reference below is exact (fp64) and
-        the kernel's output must lie within one fp16 spacing of it.
+  R-RO  x and y are fp16, gamma fp32; the reference below is exact (fp64).  A
+        kernel computing in fp32 and rounding to fp16 once must land within
+        one fp16 spacing of it, plus the fp32 rounding of the vector's scale
+        (2^-18 of its largest value) where cancellation makes a value tiny.
 """
 from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["rope_table", "rmsnorm_rope", "fp16_spacing"]
+__all__ = ["rope_table", "rmsnorm_rope", "fp16_spacing", "within_gate"]
 
 
 def rope_table(theta: float, d: int, max_pos: int):
@@ -59,6 +61,17 @@ def rmsnorm_rope(x16: np.ndarray, gamma: np.ndarray, pos: np.ndarray, cos: np.nd
     s = np.asarray(sin, dtype=np.float32)[np.asarray(pos)].astype(np.float64)[:, None, :]
     a, b = u[..., :h], u[..., h:]
     return np.concatenate([a * c - b * s, b * c + a * s], axis=-1)
+
+
+def within_gate(y: np.ndarray, ref: np.ndarray) -> np.ndarray:
+    """R-RO gate: |y - ref| <= one fp16 spacing at |ref| + 2^-18 * max |ref| of the vector.
+
+    The second term is the fp32 arithmetic on values of the vector's scale
+    (a few roundings of 2^-24 each, with headroom), which dominates only where
+    a rotated value lands near zero by cancellation."""
+    ref = np.asarray(ref, dtype=np.float64)
+    scale = np.abs(ref).max(axis=-1, keepdims=True)
+    return np.abs(np.asarray(y, dtype=np.float64) - ref) <= fp16_spacing(ref) + 2.0 ** -18 * scale
 
 
 def fp16_spacing(y: np.ndarray) -> np.ndarray:

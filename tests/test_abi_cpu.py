@@ -184,3 +184,42 @@ def test_single_hip_runtime_in_process():
             "print(len(hip), len(hsa))\n")
     out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, check=True)
     assert out.stdout.split() == ["1", "1"], out.stdout
+
+
+# ---------------------------------------------------------------------------
+# RMSNorm + RoPE: host table and validation
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("theta,d,max_pos", [(10000.0, 128, 4096), (10000.0, 64, 300), (500000.0, 256, 1000),
+                                             (10000.0, 512, 64), (1e6, 6, 17)])
+def test_rope_table_matches_oracle(lib, theta, d, max_pos):
+    c, s = lib.uq_rope_table(theta, d, max_pos)
+    oc, os_ = o.rope_table(theta, d, max_pos)
+    for got, want in ((c, oc), (s, os_)):
+        ulps = np.abs(got.view(np.int32).astype(np.int64) - want.view(np.int32).astype(np.int64))
+        assert ulps.max() <= 1 and (ulps == 0).mean() >= 0.999
+
+
+def test_rope_table_errors(lib):
+    A = np.empty(64, np.float32)
+    call = lambda th, d, p, c, s: lib.raw_call("uq_rope_table", ctypes.c_double(th), d, p, c, s)  # noqa: E731
+    assert call(1e4, 8, 4, None, A.ctypes.data) == 1
+    assert call(1e4, 7, 4, A.ctypes.data, A.ctypes.data) == 2          # odd head_dim
+    assert call(1e4, 8, 0, A.ctypes.data, A.ctypes.data) == 2          # no positions
+    assert call(0.0, 8, 4, A.ctypes.data, A.ctypes.data) == 2          # theta <= 0
+    assert call(float("nan"), 8, 4, A.ctypes.data, A.ctypes.data) == 2
+
+
+def test_rmsnorm_rope_validation(lib):
+    A = 1 << 20  # fake, 16-byte aligned addresses: never dereferenced
+    f = lambda *a: lib.raw_call("uq_rmsnorm_rope", *a)  # noqa: E731
+    ok = (A, A, A, A, A, A, 4, 2, 128, 64, ctypes.c_float(1e-6), None)
+    def v(i, val):
+        a = list(ok)
+        a[i] = val
+        return f(*a)
+    assert v(0, None) == 1 and v(3, None) == 1 and v(5, None) == 1     # null pointers
+    assert v(8, 96) == 3 and v(8, 1024) == 3                             # head_dim not served
+    assert v(6, -1) == 2 and v(7, 0) == 2 and v(9, 0) == 2              # tokens, heads, max_pos
+    assert v(10, ctypes.c_float(float("nan"))) == 5 and v(10, ctypes.c_float(-1.0)) == 5
+    assert v(0, A + 8) == 4 and v(1, A + 2) == 4 and v(3, A + 2) == 4   # alignment
+    assert v(6, 0) == 0                                                  # no tokens: nothing launched

@@ -130,3 +130,17 @@ def test_fp16_spacing():
     t = torch.tensor(v, dtype=torch.float16)
     nxt = torch.nextafter(t, torch.tensor(np.inf, dtype=torch.float16)).double().numpy()
     assert np.array_equal(o.fp16_spacing(v), nxt - t.double().numpy())
+
+
+def test_norm_rope_gate():
+    """The gate accepts the fp16 rounding of the exact result and rejects a
+    one-spacing-plus error on an ordinary value."""
+    rng = np.random.default_rng(4)
+    cos, sin = o.rope_table(10000.0, 64, 128)
+    x = rng.standard_normal((9, 2, 64)).astype(np.float16)
+    ref = o.rmsnorm_rope(x, np.ones(64, np.float32), rng.integers(0, 128, 9), cos, sin, 1e-6)
+    assert o.within_gate(ref.astype(np.float16), ref).all()
+    bad = ref.astype(np.float16).astype(np.float64)
+    i = np.unravel_index(np.argmax(np.abs(ref)), ref.shape)
+    bad[i] += 3 * o.fp16_spacing(ref[i])
+    assert not o.within_gate(bad, ref).all()

@@ -69,6 +69,46 @@ WORKLOADS = {
         path="gemm", note="wide MLP projection, batched"),
 }
 
+@dataclass(frozen=True)
+class NormRopeWorkload:
+    """Fused RMSNorm + RoPE over [tokens, heads, head_dim] fp16 vectors."""
+    name: str
+    tokens: int
+    heads: int
+    head_dim: int
+    max_pos: int
+    sequence: bool = True     # positions 0 .. tokens-1 (prefill) or random (a decode batch)
+    theta: float = 10000.0
+    eps: float = 1e-6
+    seed: int = 0
+    note: str = field(default="", compare=False)
+
+
+NORM_ROPE = {
+    "rmsnorm_rope_t4096_h32_d128": NormRopeWorkload(
+        "rmsnorm_rope_t4096_h32_d128", 4096, 32, 128, 4096,
+        note="prefill of a 4096-wide model, 32 heads of 128"),
+    "rmsnorm_rope_t64_h32_d128": NormRopeWorkload(
+        "rmsnorm_rope_t64_h32_d128", 64, 32, 128, 4096, sequence=False, seed=1,
+        note="one batched decode step, 64 sequences"),
+    "rmsnorm_rope_t256_h1_d256": NormRopeWorkload(
+        "rmsnorm_rope_t256_h1_d256", 256, 1, 256, 256, seed=2,
+        note="small decoder, hidden 256 as one vector"),
+}
+
+
+def make_norm_rope(wl: NormRopeWorkload):
+    """x fp16 [T, H, D] ~ N(0, 1); gamma fp32 ~ 1 + 0.1 N(0, 1); positions int32 [T]."""
+    rng = np.random.default_rng(wl.seed)
+    x = rng.standard_normal((wl.tokens, wl.heads, wl.head_dim)).astype(np.float16)
+    gamma = (1.0 + 0.1 * rng.standard_normal(wl.head_dim)).astype(np.float32)
+    if wl.sequence:
+        pos = np.arange(wl.tokens, dtype=np.int32) % wl.max_pos
+    else:
+        pos = rng.integers(0, wl.max_pos, wl.tokens).astype(np.int32)
+    return x, gamma, pos
+
+
 # The workload the headline throughput figure is quoted on.
 HEADLINE = "int4_g64_k4096_n11008"
 
