@@ -351,12 +351,36 @@ def report_all(uq, steps: int, warmup: int, path: str | None) -> None:
             f.write(text)
 
 
+def norm_rope_line(args) -> None:
+    """One JSON line for a fused RMSNorm + RoPE workload (not the headline metric)."""
+    import torch
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a ROCm GPU")
+    import gemm_group_wise_amd as uq
+    wl = workloads.NORM_ROPE[args.workload]
+    st = NormRopeSetup(uq, wl)
+    ms, eager_ms = st.time(args.steps, args.warmup)
+    rel = st.check_sample()
+    gbs = st.bytes / (ms * 1e-3) / 1e9
+    log(f"{wl.name}: {ms * 1e3:.3f} us/launch (graph), {eager_ms * 1e3:.3f} us (eager), {gbs:.1f} GB/s, "
+        f"rel-L2 {rel:.2e}")
+    print(json.dumps({
+        "metric": "fused RMSNorm + RoPE GB/s (x read + y written + table rows)", "value": round(gbs, 2),
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": wl.name, "tokens": wl.tokens, "heads": wl.heads, "head_dim": wl.head_dim,
+                   "bytes": st.bytes, "rotated_copies": st.rotate},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None}}), flush=True)
+
+
 def main() -> None:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--workload", default=workloads.HEADLINE, choices=list(workloads.WORKLOADS))
+    ap.add_argument("--workload", default=workloads.HEADLINE,
+                    choices=list(workloads.WORKLOADS) + list(workloads.NORM_ROPE))
     ap.add_argument("--m", type=int, default=None)
     ap.add_argument("--rotate", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -372,6 +396,9 @@ def main() -> None:
     if args.gpus != 1:
         raise SystemExit("bench.py measures one GPU: this build has no multi-GPU path "
                          "(the sharding plan is documented, not built); run with --gpus 1")
+    if args.workload in workloads.NORM_ROPE:
+        norm_rope_line(args)
+        return
     wl = workloads.WORKLOADS[args.workload]
     m = args.m or wl.ms[0]
     if args.traffic_parse:
