@@ -261,7 +261,7 @@ def traffic_parse(wl: workloads.Workload, m: int, fetch_dir: str, write_dir: str
         json.dump(t, f, indent=1)
     f_, w_ = out["FETCH_SIZE"], out["WRITE_SIZE"]
     md = [f"# HBM traffic of {kernel}: {wl.name}, M={m}", "",
-          "Commands (GPU box, repository root), one counter per run:", ""] + [f"    {c}" for c in cmds] + [
+          "Commands (MI355X host, repository root), one counter per run:", ""] + [f"    {c}" for c in cmds] + [
           "", "| counter | kernel KiB/dispatch (median) | dispatches | calibration copy KiB | scale | bytes/launch |",
           "|---|---|---|---|---|---|",
           f"| FETCH_SIZE | {f_['kernel_kib_per_dispatch']:.1f} | {f_['dispatches']} | {f_['calibration_kib']:.0f} | "
@@ -394,7 +394,7 @@ def main() -> None:
     args = ap.parse_args()
 
     if args.gpus != 1:
-        raise SystemExit("bench.py measures one GPU: this build has no multi-GPU path "
+        raise SystemExit("bench.py measures one GPU: the library has no multi-GPU path "
                          "(the sharding plan is documented, not built); run with --gpus 1")
     if args.workload in workloads.NORM_ROPE:
         norm_rope_line(args)
