@@ -17,15 +17,19 @@
 //      K step of KW * WGK.  Each wave keeps a BM x 64 fp32 accumulator
 //      (v_mfma_f32_32x32x16_bf16 tiles) and the K slices are summed through
 //      LDS at the end, so no partial sums go to memory.
-//   * Activations: the bf16 tile of a K step (BM x KW*WGK, 32 KB) is copied
+//   * Activations: the bf16 tile of a K step (BM x KW*WGK) is copied
 //     HBM -> LDS by global_load_lds_dwordx4 (no VGPR staging) into a ring of
-//     four buffers, three steps ahead of use, XOR-swizzled on 16-byte chunks
-//     so the MFMA fragment reads are free of bank conflicts.  (An L2-to-LDS
-//     copy takes about 1.5 us to land; one step ahead does not hide that.)
+//     kNB buffers (two by default: one step ahead), XOR-swizzled on 16-byte
+//     chunks so the MFMA fragment reads are free of bank conflicts.
 //   * Weights never pass through LDS: each lane loads the codes of its weight
-//     row and K slice three steps ahead into a ring of registers and
-//     dequantizes them straight into MFMA B registers, 8 codes per MFMA,
-//     exactly once per M tile.
+//     row and K slice one step ahead into a ring of registers and dequantizes
+//     them straight into MFMA B registers, 8 codes per MFMA, exactly once per
+//     M tile.
+//   * The cost of the loads goes by the number of cache lines they touch
+//     more than by their bytes, and a burst of them stalls the issuing waves:
+//     a step's loads go out in shares, one per MFMA sub-step of the step
+//     before, and where one group covers the wave's whole K slice the group
+//     parameters of both weight tiles come in one load.
 //
 // Lane layout of one wave's K slice of KW: lane l works on row (l % 32) of
 // each 32-row tile and on codes [KW/2 * kh, KW/2 * (kh + 1)) with kh = l / 32;
@@ -55,6 +59,7 @@ struct Tile {
   static constexpr int WGK = kWaves / WGN;              // K slices per step
   static constexpr int KW = (kNB == 2 || BM == 32) ? 64 : 32;  // k per wave per step
   static constexpr int SUB = KW / 16;                   // MFMA sub-steps per step
+  static_assert(SUB >= 2, "the two weight tiles' loads go out in separate sub-steps");
   static constexpr int KS = KW * WGK;                   // k per step
   static constexpr int BN = 64 * WGN;                   // weight rows per workgroup
   static constexpr int TM = BM / 32;                    // 32-row MFMA tiles of x
@@ -243,6 +248,11 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint8_t* __restric
     crow[t] = codes + size_t(row) * rowb;
     prow[t] = params + size_t(row) * size_t(ng) * PB;
   }
+  // When a group spans the wave's whole K slice (G >= KW), both halves of the
+  // wave need the same group of both tiles' rows: one load fetches it (lanes
+  // of half h take tile h) and a swap of the halves gives every lane both.
+  constexpr bool kOneParamLoad = G >= KW;
+  const uint8_t* prow_h = kh ? prow[1] : prow[0];
 
   f32x16 acc[T::TM][2];
 #pragma unroll
@@ -260,44 +270,61 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint8_t* __restric
   // where the paths join).  Waiting for step st then means waiting until at
   // most the kNB - 2 later steps' loads are outstanding.
   constexpr int NT = T::LOADS;                         // copies per step
-  constexpr int NC = 2 * (code_loads<S, KW>() + 1);    // code + parameter loads per step
+  constexpr int NC = 2 * code_loads<S, KW>() + (kOneParamLoad ? 1 : 2);  // code + parameter loads per step
   constexpr int NWAIT = (kNB - 2) * (NT + NC);
   static_assert(NWAIT < 64, "vmcnt field");
   Codes<S, KW> cs[kNB][2];        // [set][tile]
   uint32_t ps[kNB][2][NGRP];      // [set][tile][group]
   bool live[kNB] = {};
 
-  auto issue = [&](int st, int set) __attribute__((always_inline)) {
+  // The loads of step st into set `set`, in SUB shares: share `part` holds the
+  // tile copies i with i % SUB == part and, for part < 2, the codes (and
+  // parameters) of weight tile `part`.  The shares are issued one per MFMA
+  // sub-step, so the loads of a step reach the memory pipeline spread over the
+  // previous step instead of in one burst after its barrier.
+  auto issue = [&](int st, int set, int part) __attribute__((always_inline)) {
     int col = st * T::KS + 8 * cl;
     col = col < k ? col : 0;  // past K: any valid chunk (the weights there are zeroed)
     uint8_t* dst = buffer(set) + wave * 1024;
 #pragma unroll
     for (int i = 0; i < T::LOADS; ++i)
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(arow[i] + col),
-                                       (__attribute__((address_space(3))) void*)(dst + i * kThreads * 16), 16, 0, 0);
+      if (i % T::SUB == part)
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(arow[i] + col),
+                                         (__attribute__((address_space(3))) void*)(dst + i * kThreads * 16), 16, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
-    const int k0 = st * T::KS + KW * wk + KW / 2 * kh;
-    live[set] = k0 < k;
-    const int kc = live[set] ? k0 : 0;  // past K: any valid slice (its weights are zeroed)
+    const int kb = st * T::KS + KW * wk;  // the wave's K slice
+    const int k0 = kb + KW / 2 * kh;      // the lane's half of it
+    if (part == 0) live[set] = k0 < k;
+    const int kc = k0 < k ? k0 : 0;       // past K: any valid slice (its weights are zeroed)
+    static_assert(NGRP <= 2 && (NGRP == 1 || PB == 4), "parameter load");
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
+      if (t != part) continue;
       load_codes<S, KW>(cs[set][t], crow[t] + size_t(kc) * bits / 8);
-      const uint8_t* pp = prow[t] + size_t(kc / G) * PB;
-      static_assert(NGRP <= 2 && (NGRP == 1 || PB == 4), "parameter load");
-      if constexpr (NGRP == 2) {
-        const uint2 v = *reinterpret_cast<const uint2*>(pp);  // kc / G is even: 8-byte aligned
-        ps[set][t][0] = v.x;
-        ps[set][t][1] = v.y;
-      } else if constexpr (PB == 4) {
-        ps[set][t][0] = *reinterpret_cast<const uint32_t*>(pp);
+      if constexpr (kOneParamLoad) {
+        if (t == 0) {
+          const int kq = kb < k ? kb : 0;
+          const uint8_t* pp = prow_h + size_t(kq / G) * PB;
+          if constexpr (PB == 4) ps[set][0][0] = *reinterpret_cast<const uint32_t*>(pp);
+          else ps[set][0][0] = *reinterpret_cast<const uint16_t*>(pp);
+        }
       } else {
-        ps[set][t][0] = *reinterpret_cast<const uint16_t*>(pp);
+        const uint8_t* pp = prow[t] + size_t(kc / G) * PB;
+        if constexpr (NGRP == 2) {
+          const uint2 v = *reinterpret_cast<const uint2*>(pp);  // kc / G is even: 8-byte aligned
+          ps[set][t][0] = v.x;
+          ps[set][t][1] = v.y;
+        } else if constexpr (PB == 4) {
+          ps[set][t][0] = *reinterpret_cast<const uint32_t*>(pp);
+        } else {
+          ps[set][t][0] = *reinterpret_cast<const uint16_t*>(pp);
+        }
       }
     }
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // One K step from buffer and register set `set` = st % 4.  Sub-steps are
+  // One K step from buffer and register set `set` = st % kNB.  Sub-steps are
   // software-pipelined: while sub-step s's MFMAs run, the wave reads sub-step
   // s+1's activation fragments and dequantizes its weights; the scheduling
   // hints interleave each MFMA with a share of that VALU work.
@@ -313,12 +340,23 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint8_t* __restric
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();  // step st's tile is in LDS for every wave; buffer (st-1) % kNB is free
     asm volatile("" ::: "memory");
+    uint32_t praw[2][NGRP];
+    if constexpr (kOneParamLoad) {
+      const auto sw = __builtin_amdgcn_permlane32_swap(ps[set][0][0], ps[set][0][0], false, false);
+      praw[0][0] = sw[0];  // tile 0's row (loaded by the lower half)
+      praw[1][0] = sw[1];  // tile 1's row (loaded by the upper half)
+    } else {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int j = 0; j < NGRP; ++j) praw[t][j] = ps[set][t][j];
+    }
     Params<S, G, KW> pc[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int j = 0; j < NGRP; ++j) {
-        const uint32_t v = live[set] ? ps[set][t][j] : 0u;  // K slice past K: w' = 0
+        const uint32_t v = live[set] ? praw[t][j] : 0u;  // K slice past K: w' = 0
         if constexpr (S == UQ_NF4) {
           pc[t].s[j] = h2f(uint16_t(v));
           pc[t].z[j] = 0.0f;
@@ -328,7 +366,6 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint8_t* __restric
         }
       }
     const Codes<S, KW> cc[2] = {cs[set][0], cs[set][1]};
-    issue(st + kNB - 1, (set + kNB - 1) % kNB);
 
     const uint8_t* Ab = buffer(set) + r32 * T::CPR * 16;
     auto afrag = [&](int a, int s) __attribute__((always_inline)) {
@@ -342,6 +379,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint8_t* __restric
     for (int t = 0; t < 2; ++t) bcur[t] = dequant8<S, G, KW>(cc[t], pc[t], 0, nf4);
 #pragma unroll
     for (int s = 0; s < T::SUB; ++s) {
+      issue(st + kNB - 1, (set + kNB - 1) % kNB, s);
       bf16x8 anxt[T::TM], bnxt[2];
       if (s + 1 < T::SUB) {
 #pragma unroll
@@ -370,7 +408,9 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint8_t* __restric
   };
 
 #pragma unroll
-  for (int j = 0; j < kNB - 1; ++j) issue(j, j);
+  for (int j = 0; j < kNB - 1; ++j)
+#pragma unroll
+    for (int p = 0; p < T::SUB; ++p) issue(j, j, p);
   // Whole rounds of kNB steps; the steps past K multiply by w' = 0.
   for (int st = 0; st < steps; st += kNB) {
 #pragma unroll
