@@ -13,29 +13,30 @@
 //      dequant VALU work and LDS reads run under the other's MFMAs; on gfx950
 //      a single wave does not overlap them well).  The workgroup owns BM rows
 //      of x by BN = 64 * WGN weight rows; wave (wn, wk) owns weight rows
-//      [64 wn, 64 wn + 64) of the tile and the KW-wide K slice wk of every
-//      K step of KW * WGK.  Each wave keeps a BM x 64 fp32 accumulator
+//      [64 wn, 64 wn + 64) of the tile and the 32-wide K slice wk of every
+//      K step of 32 * WGK.  Each wave keeps a BM x 64 fp32 accumulator
 //      (v_mfma_f32_32x32x16_bf16 tiles) and the K slices are summed through
 //      LDS at the end, so no partial sums go to memory.
-//   * Activations: the bf16 tile of a K step (BM x KW*WGK) is copied
-//     HBM -> LDS by global_load_lds_dwordx4 (no VGPR staging) into a ring of
-//     kNB buffers (two by default: one step ahead), XOR-swizzled on 16-byte
-//     chunks so the MFMA fragment reads are free of bank conflicts.
-//   * Weights never pass through LDS: each lane loads the codes of its weight
-//     row and K slice one step ahead into a ring of registers and dequantizes
-//     them straight into MFMA B registers, 8 codes per MFMA, exactly once per
-//     M tile.
-//   * The cost of the loads goes by the number of cache lines they touch
-//     more than by their bytes, and a burst of them stalls the issuing waves:
-//     a step's loads go out in shares, one per MFMA sub-step of the step
-//     before, and where one group covers the wave's whole K slice the group
-//     parameters of both weight tiles come in one load.
+//   * Everything a step needs is copied into LDS by global_load_lds (no VGPR
+//     staging): the bf16 activation tile (BM x KS, from L2) one step ahead
+//     into the other of two buffers; the packed codes of the BN weight rows
+//     for the step (from HBM, so with a longer wait) three steps ahead into a
+//     ring of four; and a window of 16 or more groups of parameters per
+//     weight row, at least three steps ahead into the other of two.  The vector memory pipeline charges about a
+//     cycle per four adjacent lanes and cache line touched, so every copy is
+//     laid out for four or more adjacent lanes to read one line: a per-lane
+//     load of each lane's own codes (32 rows per instruction) costs 3-4x as
+//     much for the same bytes.  Each lane then reads its 16 codes and its
+//     group's parameters back from LDS (swizzled layouts, few bank
+//     conflicts) and dequantizes them straight into MFMA B registers, exactly
+//     once per M tile.  The copies of a step go out in two shares, one per
+//     MFMA sub-step of the step before, not in one burst after its barrier.
 //
-// Lane layout of one wave's K slice of KW: lane l works on row (l % 32) of
-// each 32-row tile and on codes [KW/2 * kh, KW/2 * (kh + 1)) with kh = l / 32;
-// MFMA sub-step s (0 .. KW/16 - 1) takes codes 8s..8s+7 of that half on both
-// the A and the B side (any consistent assignment of k within an MFMA gives
-// the same dot product).
+// Lane layout of one wave's K slice of 32: lane l works on row (l % 32) of
+// each 32-row weight tile and on codes [16 kh, 16 kh + 16) with kh = l / 32;
+// MFMA sub-step s (0, 1) takes codes 8s..8s+7 of that half on both the A and
+// the B side (any consistent assignment of k within an MFMA gives the same
+// dot product).
 #include <mutex>
 #include <vector>
 
@@ -48,64 +49,52 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kThreads = 512;
 constexpr int kWaves = 8;
-#ifndef UQ_GEMM_NB
-#define UQ_GEMM_NB 2
-#endif
-constexpr int kNB = UQ_GEMM_NB;  // activation buffers = code register sets = prefetch distance + 1
-static_assert(kNB == 2 || kNB == 4, "ring of two or four");
+constexpr int kKW = 32;          // k per wave per step: 16 codes per lane, two MFMA sub-steps
+constexpr int kSUB = kKW / 16;
+constexpr int kDC = 3;           // codes are copied this many steps ahead (from HBM: long latency)
+constexpr int kNC = kDC + 1;     // code buffers
+
+// Groups per parameter window: at least 16, and enough that a window spans
+// kDC or more steps (the next window is copied kDC steps before it is used,
+// into the buffer of the window before the current one).
+constexpr int param_window(int G, int KS) {
+  int w = 16;
+  while (w * G < kDC * KS) w *= 2;
+  return w;
+}
 
 template <int BM, int WGN>
 struct Tile {
   static constexpr int WGK = kWaves / WGN;              // K slices per step
-  static constexpr int KW = (kNB == 2 || BM == 32) ? 64 : 32;  // k per wave per step
-  static constexpr int SUB = KW / 16;                   // MFMA sub-steps per step
-  static_assert(SUB >= 2, "the two weight tiles' loads go out in separate sub-steps");
-  static constexpr int KS = KW * WGK;                   // k per step
+  static constexpr int KS = kKW * WGK;                  // k per step (256 or 128)
   static constexpr int BN = 64 * WGN;                   // weight rows per workgroup
   static constexpr int TM = BM / 32;                    // 32-row MFMA tiles of x
   static constexpr int CPR = KS / 8;                    // 16-byte chunks per activation row
-  static constexpr int BYTES = BM * KS * 2;             // one activation buffer
-  static constexpr int LOADS = BYTES / (kThreads * 16); // 16-byte copies per thread per step
+  static constexpr int ABYTES = BM * KS * 2;            // one activation buffer
+  static constexpr int ALOADS = ABYTES / (kThreads * 16);  // 16-byte copies per thread per step
   static constexpr int RPI = kThreads / CPR;            // activation rows per copy round
-  static_assert(kNB * BYTES <= 131072, "activation ring fits in LDS");
-  static_assert(RPI % 8 == 0, "swizzle period");
-  static_assert((WGK / 2) * WGN * TM * 2 * 16 * 64 * 4 <= kNB * BYTES, "K-slice reduction fits in LDS");
+  static_assert(ALOADS >= 1 && ALOADS % kSUB == 0 || ALOADS == 1, "copies split over the sub-steps");
+  static_assert(RPI % 16 == 0 && CPR >= 16, "swizzle period");
 };
 
-// The KW/2 codes of one lane for one weight row and K slice.
-template <int S, int KW>
-struct Codes {
-  static constexpr int BYTES = KW / 2 * Fmt<S>::bits / 8;  // 4 .. 32
-  static constexpr int W = BYTES / 4;
-  uint32_t d[W];
+// The weight codes of one step in LDS: BN rows of RB bytes, in 16-byte pieces;
+// piece p of row r sits at position p ^ swz(r) so that the 16 rows read
+// together by a half-wave land on different banks.  Copied with 16-byte lanes
+// (INT4, INT8; rows are 16-byte aligned) or 4-byte lanes (INT2, whose rows are
+// only 8-byte aligned), eight or more lanes per 128-byte line.
+template <int S, int KS, int BN>
+struct CodeTile {
+  static constexpr int bits = Fmt<S>::bits;
+  static constexpr int RB = KS * bits / 8;              // bytes of one weight row per step
+  static constexpr int PPR = RB / 16;                   // 16-byte pieces per row
+  static constexpr int BYTES = BN * RB;
+  static constexpr int EL = bits == 2 ? 4 : 16;         // bytes per lane per copy
+  static constexpr int PER_WAVE = BYTES / (EL * 64 * kWaves);  // copies per wave per step
+  static constexpr int SWZ_DIV = 16 / PPR;
+  static constexpr int LANE_BYTES = kKW / 2 * bits / 8;  // codes of one lane: 4, 8 or 16 bytes
+  static_assert(PPR >= 2 && PPR <= 16 && PER_WAVE >= 1, "code tile shape");
+  __device__ static int swz(int r) { return (r / SWZ_DIV) & (PPR - 1); }
 };
-
-// One load instruction per 16 bytes (or fewer): the count is part of the
-// wait-count arithmetic in the kernel.
-template <int S, int KW>
-__device__ __forceinline__ void load_codes(Codes<S, KW>& c, const uint8_t* __restrict__ p) {
-  constexpr int B = Codes<S, KW>::BYTES;
-  if constexpr (B == 4) {
-    c.d[0] = *reinterpret_cast<const uint32_t*>(p);
-  } else if constexpr (B == 8) {
-    const uint2 v = *reinterpret_cast<const uint2*>(p);
-    c.d[0] = v.x;
-    c.d[1] = v.y;
-  } else {
-#pragma unroll
-    for (int h = 0; h < B / 16; ++h) {
-      const uint4 v = *reinterpret_cast<const uint4*>(p + 16 * h);
-      c.d[4 * h] = v.x;
-      c.d[4 * h + 1] = v.y;
-      c.d[4 * h + 2] = v.z;
-      c.d[4 * h + 3] = v.w;
-    }
-  }
-}
-template <int S, int KW>
-constexpr int code_loads() {
-  return Codes<S, KW>::BYTES <= 16 ? 1 : Codes<S, KW>::BYTES / 16;
-}
 
 // Byte I of a dword to fp32 in one instruction.  (Written as shift-and-mask,
 // the compiler emits a bit-field extract plus a byte-0 conversion: two.)
@@ -124,21 +113,37 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// Group parameters of a lane's K slice, as fp32: (s, z), or (a, 0) for NF4.
-// The lane's KW/2 codes span NGRP groups (two only for INT2 G16 with KW 64).
-template <int S, int G, int KW>
-struct Params {
-  static constexpr int NGRP = G < KW / 2 ? KW / 2 / G : 1;
-  float s[NGRP], z[NGRP];
+// The 16 codes of one lane (one weight row, one half of the wave's K slice).
+template <int S>
+struct Codes {
+  static constexpr int W = kKW / 2 * Fmt<S>::bits / 8 / 4;  // 1, 2 or 4 dwords
+  uint32_t d[W];
 };
 
-// Codes 8s..8s+7 of the lane's KW/2 -> bf16(w') as an MFMA operand.
-template <int S, int G, int KW>
-__device__ __forceinline__ bf16x8 dequant8(const Codes<S, KW>& c, const Params<S, G, KW>& p, int s,
-                                           const float* nf4) {
+template <int S>
+__device__ __forceinline__ Codes<S> lds_codes(const uint8_t* p) {
+  Codes<S> c;
+  if constexpr (Codes<S>::W == 1) {
+    c.d[0] = *reinterpret_cast<const uint32_t*>(p);
+  } else if constexpr (Codes<S>::W == 2) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    c.d[0] = v.x;
+    c.d[1] = v.y;
+  } else {
+    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    c.d[0] = v.x;
+    c.d[1] = v.y;
+    c.d[2] = v.z;
+    c.d[3] = v.w;
+  }
+  return c;
+}
+
+// Codes 8s..8s+7 of the lane's 16 -> bf16(w') as an MFMA operand, with the
+// lane's group parameters (s, z) -- (a, 0) for NF4 -- in fp32.
+template <int S>
+__device__ __forceinline__ bf16x8 dequant8(const Codes<S>& c, float sc, float zc, int s, const float* nf4) {
   constexpr int bits = Fmt<S>::bits;
-  const int grp = G < KW / 2 ? (8 * s) / G : 0;
-  const float sc = p.s[grp], zc = p.z[grp];
   float w[8];
   if constexpr (bits == 8) {
     const uint32_t d0 = c.d[2 * s], d1 = c.d[2 * s + 1];
@@ -169,8 +174,8 @@ __device__ __forceinline__ bf16x8 dequant8(const Codes<S, KW>& c, const Params<S
       w[6] = __builtin_fmaf(ubyte_f32<3>(lo), sc, zc);
       w[7] = __builtin_fmaf(ubyte_f32<3>(hi), sc, zc);
     }
-  } else {  // 2 bits: codes 8s..8s+7 are 16 bits of one dword
-    const uint32_t d = c.d[s >> 1] >> (16 * (s & 1));
+  } else {  // 2 bits: codes 8s..8s+7 are 16 bits of the lane's dword
+    const uint32_t d = c.d[0] >> (16 * s);
 #pragma unroll
     for (int i = 0; i < 8; ++i) w[i] = __builtin_fmaf(float((d >> (2 * i)) & 3u), sc, zc);
   }
@@ -194,65 +199,107 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint8_t* __restric
                                                         float* __restrict__ y, int n, int k, int m,
                                                         int tiles_m, int nblocks) {
   using T = Tile<BM, WGN>;
-  constexpr int KW = T::KW;
+  using C = CodeTile<S, T::KS, T::BN>;
   constexpr int bits = Fmt<S>::bits;
   constexpr int PB = param_bytes_per_group(S);
-  constexpr int NGRP = Params<S, G, KW>::NGRP;
-  // The activation buffers are separate LDS objects, so the compiler can tell
-  // the copies into one from the fragment reads of another.
-  constexpr int B23 = kNB == 4 ? T::BYTES : 16;
-  __shared__ __attribute__((aligned(16))) uint8_t lds0[T::BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t lds1[T::BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t lds2[B23];
-  __shared__ __attribute__((aligned(16))) uint8_t lds3[B23];
+  constexpr int WIN = param_window(G, T::KS);     // groups per parameter window
+  constexpr int SPW = WIN * G / T::KS;            // steps per parameter window
+  constexpr int PPW = T::BN * WIN / (64 * kWaves);  // parameter copies per wave per window
+  constexpr int PBYTES = T::BN * WIN * 4;         // one window: a dword slot per group
+  static_assert(SPW >= kDC && PPW >= 1, "parameter window shape");
+  static_assert(G >= kKW / 2, "a lane's 16 codes lie in one group");
+  // Every buffer is its own LDS object and the step loop is unrolled by kNC,
+  // so the compiler can tell the copies into one buffer from the reads of
+  // another and adds no waits of its own.
+  __shared__ __attribute__((aligned(16))) uint8_t act0[T::ABYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t act1[T::ABYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t cod0[C::BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t cod1[C::BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t cod2[C::BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t cod3[C::BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t par0[PBYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t par1[PBYTES];
   __shared__ float nf4[16];
-  auto buffer = [&](int i) __attribute__((always_inline)) {
-    return i == 0 ? lds0 : i == 1 ? lds1 : i == 2 ? lds2 : lds3;
+  static_assert(kNC == 4, "four code buffers");
+  auto abuf = [&](int i) __attribute__((always_inline)) { return i ? act1 : act0; };
+  auto cbuf = [&](int i) __attribute__((always_inline)) {
+    return i == 0 ? cod0 : i == 1 ? cod1 : i == 2 ? cod2 : cod3;
   };
+  auto pbuf = [&](int i) __attribute__((always_inline)) { return i ? par1 : par0; };
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wn = wave % WGN, wk = wave / WGN;
   const int b = xcd_order(blockIdx.x, nblocks);
   const int tile_m = b % tiles_m, tile_n = b / tiles_m;
-  const int bm = tile_m * BM;
+  const int bm = tile_m * BM, bn = tile_n * T::BN;
   const int steps = (k + T::KS - 1) / T::KS;
   const size_t rowb = size_t(k) * bits / 8;
   const int ng = k / G;
   if constexpr (S == UQ_NF4) {
     if (tid < 16) nf4[tid] = nf4_value(tid);
   }
+  auto grow = [&](int r) __attribute__((always_inline)) {
+    const int row = bn + r;
+    return row < n ? row : n - 1;  // rows past N: computed, not stored
+  };
 
   // Activation copy: thread tid moves 16-byte slot q = i * 512 + tid of the
   // step's tile (row q / CPR, physical chunk q % CPR, which holds logical
-  // chunk (q % CPR) ^ (row & 7)).  RPI is a multiple of 8, so the logical
+  // chunk (q % CPR) ^ (row & 15)).  RPI is a multiple of 16, so the logical
   // chunk is the same for every i.
   const int r0 = tid / T::CPR;
-  const int cl = (tid % T::CPR) ^ (r0 & 7);
-  const uint16_t* arow[T::LOADS];
+  const int cl = (tid % T::CPR) ^ (r0 & 15);
+  // Sources are a base common to the workgroup plus a 32-bit lane offset
+  // (the tile spans at most 128 rows of at most 2^16 elements).
+  const uint16_t* abase = xb + size_t(bm) * size_t(k);
+  uint32_t aoff[T::ALOADS];
 #pragma unroll
-  for (int i = 0; i < T::LOADS; ++i) {
+  for (int i = 0; i < T::ALOADS; ++i) {
     int r = bm + i * T::RPI + r0;
     r = r < m ? r : m - 1;  // rows past M: any valid row (their outputs are not stored)
-    arow[i] = xb + size_t(r) * size_t(k);
+    aoff[i] = uint32_t(r - bm) * uint32_t(k);
   }
 
-  // Weight rows of the lane's two 32-row tiles.
+  // Code copy j of this wave: lane slot q -> row r = piece / PPR, logical
+  // piece p = (piece % PPR) ^ swz(r); 4-byte lanes take dword q % 4 of it.
+  const uint8_t* cbase = codes + size_t(bn) * rowb;
+  uint32_t crow[C::PER_WAVE], cbyte[C::PER_WAVE];
+#pragma unroll
+  for (int j = 0; j < C::PER_WAVE; ++j) {
+    const int q = (wave * C::PER_WAVE + j) * 64 + lane;
+    const int piece = C::EL == 16 ? q : q / 4;
+    const int sub = C::EL == 16 ? 0 : q % 4;
+    const int r = piece / C::PPR;
+    const int p = (piece % C::PPR) ^ C::swz(r);
+    cbyte[j] = uint32_t(p * 16 + sub * 4);
+    crow[j] = uint32_t(grow(r) - bn) * uint32_t(rowb);
+  }
+
+  // Parameter copy j of this wave: dword slot q -> row r = q / WIN, slot
+  // d' = q % WIN holding group d = d' ^ f(r) of the window, f(r) = (r / 4) % 16.
+  const uint8_t* pbase = params + size_t(bn) * size_t(ng) * PB;
+  uint32_t prowoff[PPW];
+  int pgrp[PPW];
+#pragma unroll
+  for (int j = 0; j < PPW; ++j) {
+    const int q = (wave * PPW + j) * 64 + lane;
+    const int r = q / WIN;
+    pgrp[j] = (q % WIN) ^ ((r >> 2) & 15);
+    prowoff[j] = uint32_t(grow(r) - bn) * uint32_t(ng * PB);
+  }
+
+  // What this lane reads from LDS each step, for its two 32-row weight tiles.
   const int kh = lane >> 5, r32 = lane & 31;
-  const uint8_t* crow[2];
-  const uint8_t* prow[2];
+  int coff[2], prow[2], pswz[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    int row = tile_n * T::BN + wn * 64 + t * 32 + r32;
-    row = row < n ? row : n - 1;  // rows past N: computed, not stored
-    crow[t] = codes + size_t(row) * rowb;
-    prow[t] = params + size_t(row) * size_t(ng) * PB;
+    const int r = wn * 64 + t * 32 + r32;
+    const int bo = (kKW * wk + kKW / 2 * kh) * bits / 8;  // byte of the row's step segment
+    coff[t] = (r * C::PPR + ((bo / 16) ^ C::swz(r))) * 16 + bo % 16;
+    prow[t] = r * WIN;
+    pswz[t] = (r >> 2) & 15;
   }
-  // When a group spans the wave's whole K slice (G >= KW), both halves of the
-  // wave need the same group of both tiles' rows: one load fetches it (lanes
-  // of half h take tile h) and a swap of the halves gives every lane both.
-  constexpr bool kOneParamLoad = G >= KW;
-  const uint8_t* prow_h = kh ? prow[1] : prow[0];
 
   f32x16 acc[T::TM][2];
 #pragma unroll
@@ -262,137 +309,144 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint8_t* __restric
 #pragma unroll
       for (int j = 0; j < 16; ++j) acc[a][t][j] = 0.0f;
 
-  // Prefetch: step st's activation tile goes to buffer st % kNB and its codes
-  // to register set st % kNB, issued kNB - 1 steps ahead (the step loop is
-  // unrolled by kNB, so nothing is copied).  Each step issues the tile's
-  // copies and then the codes, always (clamped to valid addresses past the
-  // last step: loads under a branch make the compiler wait for every load
-  // where the paths join).  Waiting for step st then means waiting until at
-  // most the kNB - 2 later steps' loads are outstanding.
-  constexpr int NT = T::LOADS;                         // copies per step
-  constexpr int NC = 2 * code_loads<S, KW>() + (kOneParamLoad ? 1 : 2);  // code + parameter loads per step
-  constexpr int NWAIT = (kNB - 2) * (NT + NC);
-  static_assert(NWAIT < 64, "vmcnt field");
-  Codes<S, KW> cs[kNB][2];        // [set][tile]
-  uint32_t ps[kNB][2][NGRP];      // [set][tile][group]
-  bool live[kNB] = {};
-
-  // The loads of step st into set `set`, in SUB shares: share `part` holds the
-  // tile copies i with i % SUB == part and, for part < 2, the codes (and
-  // parameters) of weight tile `part`.  The shares are issued one per MFMA
-  // sub-step, so the loads of a step reach the memory pipeline spread over the
-  // previous step instead of in one burst after its barrier.
-  auto issue = [&](int st, int set, int part) __attribute__((always_inline)) {
-    int col = st * T::KS + 8 * cl;
-    col = col < k ? col : 0;  // past K: any valid chunk (the weights there are zeroed)
-    uint8_t* dst = buffer(set) + wave * 1024;
+  // Copies.  Per step, in this order: the parameter window that opens kDC
+  // steps later (when one does), the next step's activation tile (in kSUB
+  // shares, one per MFMA sub-step), and the codes of the step kDC ahead.
+  // Waiting at a step for all but the last PER_WAVE copies then covers
+  // everything the step reads.  Copies past K come from valid (clamped)
+  // addresses and are multiplied by w' = 0.
+  auto issue_params = [&](int win) __attribute__((always_inline)) {
+    uint8_t* pdst = pbuf(win & 1) + wave * PPW * 256;
 #pragma unroll
-    for (int i = 0; i < T::LOADS; ++i)
-      if (i % T::SUB == part)
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(arow[i] + col),
-                                         (__attribute__((address_space(3))) void*)(dst + i * kThreads * 16), 16, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    const int kb = st * T::KS + KW * wk;  // the wave's K slice
-    const int k0 = kb + KW / 2 * kh;      // the lane's half of it
-    if (part == 0) live[set] = k0 < k;
-    const int kc = k0 < k ? k0 : 0;       // past K: any valid slice (its weights are zeroed)
-    static_assert(NGRP <= 2 && (NGRP == 1 || PB == 4), "parameter load");
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      if (t != part) continue;
-      load_codes<S, KW>(cs[set][t], crow[t] + size_t(kc) * bits / 8);
-      if constexpr (kOneParamLoad) {
-        if (t == 0) {
-          const int kq = kb < k ? kb : 0;
-          const uint8_t* pp = prow_h + size_t(kq / G) * PB;
-          if constexpr (PB == 4) ps[set][0][0] = *reinterpret_cast<const uint32_t*>(pp);
-          else ps[set][0][0] = *reinterpret_cast<const uint16_t*>(pp);
-        }
-      } else {
-        const uint8_t* pp = prow[t] + size_t(kc / G) * PB;
-        if constexpr (NGRP == 2) {
-          const uint2 v = *reinterpret_cast<const uint2*>(pp);  // kc / G is even: 8-byte aligned
-          ps[set][t][0] = v.x;
-          ps[set][t][1] = v.y;
-        } else if constexpr (PB == 4) {
-          ps[set][t][0] = *reinterpret_cast<const uint32_t*>(pp);
-        } else {
-          ps[set][t][0] = *reinterpret_cast<const uint16_t*>(pp);
-        }
-      }
+    for (int j = 0; j < PPW; ++j) {
+      int g = win * WIN + pgrp[j];
+      g = g < ng ? g : ng - 1;  // past the row's groups: any valid one (not read)
+      const auto src = (const __attribute__((address_space(1))) void*)(pbase + (prowoff[j] + uint32_t(g * PB)));
+      const auto dst = (__attribute__((address_space(3))) void*)(pdst + j * 256);
+      if constexpr (PB == 4) __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0);
+      else __builtin_amdgcn_global_load_lds(src, dst, 2, 0, 0);  // lands zero-extended in a dword
     }
+  };
+  auto issue_act = [&](int st, int set, int part) __attribute__((always_inline)) {
+    int col = st * T::KS + 8 * cl;
+    col = col < k ? col : 0;
+    uint8_t* adst = abuf(set) + wave * 1024;
+#pragma unroll
+    for (int i = 0; i < T::ALOADS; ++i)
+      if (part < 0 || i % kSUB == part)
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(abase + (aoff[i] + uint32_t(col))),
+                                         (__attribute__((address_space(3))) void*)(adst + i * kThreads * 16), 16, 0, 0);
+  };
+  auto issue_codes = [&](int st, int cset) __attribute__((always_inline)) {
+    uint8_t* cdst = cbuf(cset) + wave * C::PER_WAVE * 64 * C::EL;
+#pragma unroll
+    for (int j = 0; j < C::PER_WAVE; ++j) {
+      uint32_t off = uint32_t(st) * C::RB + cbyte[j];
+      off = off < rowb ? off : 0u;  // past the row: any valid bytes (their weights are zeroed)
+      const auto src = (const __attribute__((address_space(1))) void*)(cbase + (crow[j] + off));
+      const auto dst = (__attribute__((address_space(3))) void*)(cdst + j * 64 * C::EL);
+      if constexpr (C::EL == 16) __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+      else __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0);
+    }
+  };
+  auto wait_step = [&]() __attribute__((always_inline)) {
+    // A plain s_barrier, not __syncthreads() (whose fences wait for every
+    // copy); the waits go through the builtin so that the compiler's
+    // wait-count tracking sees them.  The scheduling barriers keep the
+    // previous step's MFMAs from being moved after the wait.
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0x0F70 | C::PER_WAVE);  // vmcnt(PER_WAVE), gfx9 encoding
+    __builtin_amdgcn_s_waitcnt(0xC07F);                // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
   };
+  static_assert(C::PER_WAVE < 16, "vmcnt field");
 
-  // One K step from buffer and register set `set` = st % kNB.  Sub-steps are
-  // software-pipelined: while sub-step s's MFMAs run, the wave reads sub-step
-  // s+1's activation fragments and dequantizes its weights; the scheduling
-  // hints interleave each MFMA with a share of that VALU work.
-  auto step = [&](int st, int set) __attribute__((always_inline)) {
-    // A plain s_barrier, not __syncthreads(): the fences of the latter wait for
-    // every outstanding load (vmcnt(0)), the prefetched steps included.  The
-    // waits go through the builtin so that the compiler's wait-count tracking
-    // sees them (it then knows the tile's copies are done and adds no wait of
-    // its own before the fragment reads).  The ds_reads of the previous step
-    // have all been consumed by its MFMAs, so lgkmcnt(0) is immediate.
-    __builtin_amdgcn_s_waitcnt(0x0F70 | (NWAIT & 15) | ((NWAIT >> 4) << 14));  // vmcnt(NWAIT), gfx9 encoding
-    __builtin_amdgcn_s_waitcnt(0xC07F);                                         // lgkmcnt(0)
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();  // step st's tile is in LDS for every wave; buffer (st-1) % kNB is free
-    asm volatile("" ::: "memory");
-    uint32_t praw[2][NGRP];
-    if constexpr (kOneParamLoad) {
-      const auto sw = __builtin_amdgcn_permlane32_swap(ps[set][0][0], ps[set][0][0], false, false);
-      praw[0][0] = sw[0];  // tile 0's row (loaded by the lower half)
-      praw[1][0] = sw[1];  // tile 1's row (loaded by the upper half)
-    } else {
+  // The lane's codes and group parameters of step st, read from LDS (during
+  // the step before, once everything step st reads has landed).
+  auto read_step = [&](int st, int cset, Codes<S> (&cc)[2], uint32_t (&pr)[2]) __attribute__((always_inline)) {
+    const int k0 = st * T::KS + kKW * wk + kKW / 2 * kh;
+    const int win = st / SPW;
+    const int gi = (k0 / G) - win * WIN;  // the lane's group within the window
+    // Both window buffers are read and one value kept: a read through a
+    // pointer chosen at run time could be any LDS object to the compiler,
+    // which would then wait for every copy in flight first.
+    const uint32_t* pw0 = reinterpret_cast<const uint32_t*>(par0);
+    const uint32_t* pw1 = reinterpret_cast<const uint32_t*>(par1);
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int j = 0; j < NGRP; ++j) praw[t][j] = ps[set][t][j];
+    for (int t = 0; t < 2; ++t) {
+      const int i = prow[t] + (gi ^ pswz[t]);
+      const uint32_t v0 = pw0[i], v1 = pw1[i];
+      pr[t] = (win & 1) ? v1 : v0;
+      cc[t] = lds_codes<S>(cbuf(cset) + coff[t]);
     }
-    Params<S, G, KW> pc[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int j = 0; j < NGRP; ++j) {
-        const uint32_t v = live[set] ? praw[t][j] : 0u;  // K slice past K: w' = 0
-        if constexpr (S == UQ_NF4) {
-          pc[t].s[j] = h2f(uint16_t(v));
-          pc[t].z[j] = 0.0f;
-        } else {
-          pc[t].s[j] = h2f(uint16_t(v & 0xFFFFu));
-          pc[t].z[j] = h2f(uint16_t(v >> 16));
-        }
-      }
-    const Codes<S, KW> cc[2] = {cs[set][0], cs[set][1]};
+  };
 
-    const uint8_t* Ab = buffer(set) + r32 * T::CPR * 16;
+  Codes<S> ccur[2];
+  uint32_t pcur[2];
+
+  // One K step from activation buffer st % 2 and code buffer st % kNC.  Sub-
+  // steps are software-pipelined: while sub-step s's MFMAs run, the wave
+  // reads sub-step s+1's activation fragments and dequantizes its weights;
+  // the scheduling hints interleave each MFMA with a share of that VALU work.
+  auto step = [&](int st, int u) __attribute__((always_inline)) {
+    wait_step();  // everything step st reads is in LDS; the buffers of step st - 1 are free
+    // The next step's codes and parameters have landed too (copied kDC - 1 or
+    // more steps ago); read them now, before this step issues copies of its
+    // own, so that no copy in flight can be mistaken for a writer of them.
+    Codes<S> cnext[2];
+    uint32_t pnext[2];
+    read_step(st + 1, (u + 1) % kNC, cnext, pnext);
+    const bool live = st * T::KS + kKW * wk + kKW / 2 * kh < k;
+    float sc[2], zc[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const uint32_t v = live ? pcur[t] : 0u;  // past K: w' = 0
+      if constexpr (S == UQ_NF4) {
+        sc[t] = h2f(uint16_t(v));
+        zc[t] = 0.0f;
+      } else {
+        sc[t] = h2f(uint16_t(v & 0xFFFFu));
+        zc[t] = h2f(uint16_t(v >> 16));
+      }
+    }
+    const Codes<S> cc[2] = {ccur[0], ccur[1]};
+
+    const uint8_t* Ab = abuf(u & 1) + r32 * T::CPR * 16;
     auto afrag = [&](int a, int s) __attribute__((always_inline)) {
-      const int chunk = ((KW / 8) * wk + (KW / 16) * kh + s) ^ (r32 & 7);
+      const int chunk = ((kKW / 8) * wk + (kKW / 16) * kh + s) ^ (r32 & 15);
       return *reinterpret_cast<const bf16x8*>(Ab + (a * 32 * T::CPR + chunk) * 16);
     };
     bf16x8 acur[T::TM], bcur[2];
 #pragma unroll
     for (int a = 0; a < T::TM; ++a) acur[a] = afrag(a, 0);
 #pragma unroll
-    for (int t = 0; t < 2; ++t) bcur[t] = dequant8<S, G, KW>(cc[t], pc[t], 0, nf4);
+    for (int t = 0; t < 2; ++t) bcur[t] = dequant8<S>(cc[t], sc[t], zc[t], 0, nf4);
 #pragma unroll
-    for (int s = 0; s < T::SUB; ++s) {
-      issue(st + kNB - 1, (set + kNB - 1) % kNB, s);
+    for (int s = 0; s < kSUB; ++s) {
+      if (s == 0) {
+        if ((st + kDC) % SPW == 0) issue_params((st + kDC) / SPW);
+        issue_act(st + 1, (u + 1) & 1, 0);
+      } else {
+        issue_act(st + 1, (u + 1) & 1, s);
+        if (s == kSUB - 1) issue_codes(st + kDC, (u + kDC) % kNC);
+      }
+      __builtin_amdgcn_sched_barrier(0);
       bf16x8 anxt[T::TM], bnxt[2];
-      if (s + 1 < T::SUB) {
+      if (s + 1 < kSUB) {
 #pragma unroll
         for (int a = 0; a < T::TM; ++a) anxt[a] = afrag(a, s + 1);
 #pragma unroll
-        for (int t = 0; t < 2; ++t) bnxt[t] = dequant8<S, G, KW>(cc[t], pc[t], s + 1, nf4);
+        for (int t = 0; t < 2; ++t) bnxt[t] = dequant8<S>(cc[t], sc[t], zc[t], s + 1, nf4);
       }
 #pragma unroll
       for (int a = 0; a < T::TM; ++a)
 #pragma unroll
         for (int t = 0; t < 2; ++t)
           acc[a][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(acur[a], bcur[t], acc[a][t], 0, 0, 0);
-      if (s + 1 < T::SUB) {
+      if (s + 1 < kSUB) {
 #pragma unroll
         for (int q = 0; q < 2 * T::TM; ++q) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                    // one MFMA
@@ -405,58 +459,76 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint8_t* __restric
         for (int t = 0; t < 2; ++t) bcur[t] = bnxt[t];
       }
     }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      ccur[t] = cnext[t];
+      pcur[t] = pnext[t];
+    }
   };
 
+  // Prologue: the first window, the codes of steps 0 .. kDC - 1 and the
+  // activation tile of step 0, in the order the steps' waits expect (the
+  // codes of step kDC - 1 last).
+  issue_params(0);
 #pragma unroll
-  for (int j = 0; j < kNB - 1; ++j)
+  for (int j = 0; j + 1 < kDC; ++j) issue_codes(j, j);
+  issue_act(0, 0, -1);
+  issue_codes(kDC - 1, kDC - 1);
+  wait_step();
+  read_step(0, 0, ccur, pcur);
+  // Rounds of kNC steps; a step past K multiplies by w' = 0.
+  for (int st = 0; st < steps; st += kNC) {
 #pragma unroll
-    for (int p = 0; p < T::SUB; ++p) issue(j, j, p);
-  // Whole rounds of kNB steps; the steps past K multiply by w' = 0.
-  for (int st = 0; st < steps; st += kNB) {
-#pragma unroll
-    for (int u = 0; u < kNB; ++u) step(st + u, u);
+    for (int u = 0; u < kNC; ++u) step(st + u, u);
   }
 
-  // Sum the K slices: a halving tree through LDS (float4 per lane and
-  // element group, lane-major so the partner wave reads what it wrote).
-  constexpr int E4 = T::TM * 2 * 4;  // float4 per lane
-  constexpr int SB = E4 * 64 * 16;    // bytes of one wave's partial sums
-  static_assert(T::BYTES % SB == 0, "partial sums do not straddle the buffers");
+  // Sum the K slices: a halving tree through LDS (float4 per lane and element
+  // group, lane-major so the partner wave reads what it wrote), over AC of the
+  // TM M tiles at a time so that the partial sums fit the activation buffers.
+  constexpr int AC = T::ABYTES / 16384 < T::TM ? T::ABYTES / 16384 : T::TM;
+  static_assert(AC >= 1 && T::TM % AC == 0, "reduction passes");
+  constexpr int SB = AC * 2 * 4 * 64 * 16;  // bytes of one wave's partial sums per pass
+  static_assert(T::ABYTES % SB == 0 && (T::WGK / 2) * WGN * SB <= 2 * T::ABYTES, "partial sums fit");
   auto slot = [&](int sl) __attribute__((always_inline)) {
     const int off = sl * SB;
-    return reinterpret_cast<float4*>(buffer(off / T::BYTES) + off % T::BYTES) + lane;
+    return reinterpret_cast<float4*>(abuf(off / T::ABYTES) + off % T::ABYTES) + lane;
   };
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // the copies of the step past the end
   __syncthreads();
 #pragma unroll
-  for (int half = T::WGK / 2; half >= 1; half /= 2) {
-    if (wk >= half && wk < 2 * half) {
-      float4* dst = slot((wk - half) * WGN + wn);
+  for (int a0 = 0; a0 < T::TM; a0 += AC) {
 #pragma unroll
-      for (int a = 0; a < T::TM; ++a)
+    for (int half = T::WGK / 2; half >= 1; half /= 2) {
+      if (wk >= half && wk < 2 * half) {
+        float4* dst = slot((wk - half) * WGN + wn);
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int a = 0; a < AC; ++a)
 #pragma unroll
-          for (int j4 = 0; j4 < 4; ++j4)
-            dst[((a * 2 + t) * 4 + j4) * 64] = make_float4(acc[a][t][4 * j4], acc[a][t][4 * j4 + 1],
-                                                           acc[a][t][4 * j4 + 2], acc[a][t][4 * j4 + 3]);
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int j4 = 0; j4 < 4; ++j4)
+              dst[((a * 2 + t) * 4 + j4) * 64] =
+                  make_float4(acc[a0 + a][t][4 * j4], acc[a0 + a][t][4 * j4 + 1], acc[a0 + a][t][4 * j4 + 2],
+                              acc[a0 + a][t][4 * j4 + 3]);
+      }
+      __syncthreads();
+      if (wk < half) {
+        const float4* src = slot(wk * WGN + wn);
+#pragma unroll
+        for (int a = 0; a < AC; ++a)
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int j4 = 0; j4 < 4; ++j4) {
+              const float4 v = src[((a * 2 + t) * 4 + j4) * 64];
+              acc[a0 + a][t][4 * j4] += v.x;
+              acc[a0 + a][t][4 * j4 + 1] += v.y;
+              acc[a0 + a][t][4 * j4 + 2] += v.z;
+              acc[a0 + a][t][4 * j4 + 3] += v.w;
+            }
+      }
+      __syncthreads();
     }
-    __syncthreads();
-    if (wk < half) {
-      const float4* src = slot(wk * WGN + wn);
-#pragma unroll
-      for (int a = 0; a < T::TM; ++a)
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int j4 = 0; j4 < 4; ++j4) {
-            const float4 v = src[((a * 2 + t) * 4 + j4) * 64];
-            acc[a][t][4 * j4] += v.x;
-            acc[a][t][4 * j4 + 1] += v.y;
-            acc[a][t][4 * j4 + 2] += v.z;
-            acc[a][t][4 * j4 + 3] += v.w;
-          }
-    }
-    __syncthreads();
   }
   if (wk != 0) return;
 
@@ -466,7 +538,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint8_t* __restric
   for (int a = 0; a < T::TM; ++a)
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const int col = tile_n * T::BN + wn * 64 + t * 32 + r32;
+      const int col = bn + wn * 64 + t * 32 + r32;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int row = bm + a * 32 + 8 * (j / 4) + 4 * kh + (j % 4);
