@@ -47,8 +47,6 @@ namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kThreads = 512;
-constexpr int kWaves = 8;
 constexpr int kKW = 32;          // k per wave per step: 16 codes per lane, two MFMA sub-steps
 constexpr int kSUB = kKW / 16;
 constexpr int kDC = 3;           // codes are copied this many steps ahead (from HBM: long latency)
@@ -63,16 +61,17 @@ constexpr int param_window(int G, int KS) {
   return w;
 }
 
-template <int BM, int WGN>
+template <int BM, int WGN, int NW>
 struct Tile {
-  static constexpr int WGK = kWaves / WGN;              // K slices per step
+  static constexpr int NT = 64 * NW;                    // threads per workgroup
+  static constexpr int WGK = NW / WGN;                  // K slices per step
   static constexpr int KS = kKW * WGK;                  // k per step (256 or 128)
   static constexpr int BN = 64 * WGN;                   // weight rows per workgroup
   static constexpr int TM = BM / 32;                    // 32-row MFMA tiles of x
   static constexpr int CPR = KS / 8;                    // 16-byte chunks per activation row
   static constexpr int ABYTES = BM * KS * 2;            // one activation buffer
-  static constexpr int ALOADS = ABYTES / (kThreads * 16);  // 16-byte copies per thread per step
-  static constexpr int RPI = kThreads / CPR;            // activation rows per copy round
+  static constexpr int ALOADS = ABYTES / (NT * 16);    // 16-byte copies per thread per step
+  static constexpr int RPI = NT / CPR;                  // activation rows per copy round
   static_assert(ALOADS >= 1 && ALOADS % kSUB == 0 || ALOADS == 1, "copies split over the sub-steps");
   static_assert(RPI % 16 == 0 && CPR >= 16, "swizzle period");
 };
@@ -82,14 +81,14 @@ struct Tile {
 // together by a half-wave land on different banks.  Copied with 16-byte lanes
 // (INT4, INT8; rows are 16-byte aligned) or 4-byte lanes (INT2, whose rows are
 // only 8-byte aligned), eight or more lanes per 128-byte line.
-template <int S, int KS, int BN>
+template <int S, int KS, int BN, int NW>
 struct CodeTile {
   static constexpr int bits = Fmt<S>::bits;
   static constexpr int RB = KS * bits / 8;              // bytes of one weight row per step
   static constexpr int PPR = RB / 16;                   // 16-byte pieces per row
   static constexpr int BYTES = BN * RB;
   static constexpr int EL = bits == 2 ? 4 : 16;         // bytes per lane per copy
-  static constexpr int PER_WAVE = BYTES / (EL * 64 * kWaves);  // copies per wave per step
+  static constexpr int PER_WAVE = BYTES / (EL * 64 * NW);  // copies per wave per step
   static constexpr int SWZ_DIV = 16 / PPR;
   static constexpr int LANE_BYTES = kKW / 2 * bits / 8;  // codes of one lane: 4, 8 or 16 bytes
   static_assert(PPR >= 2 && PPR <= 16 && PER_WAVE >= 1, "code tile shape");
@@ -192,19 +191,19 @@ __device__ __forceinline__ int xcd_order(int b, int nb) {
   return x * q + (x < r ? x : r) + (b >> 3);
 }
 
-template <int S, int G, int BM, int WGN>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(const uint8_t* __restrict__ codes,
+template <int S, int G, int BM, int WGN, int NW>
+__global__ __launch_bounds__(64 * NW) void gemm_kernel(const uint8_t* __restrict__ codes,
                                                         const uint8_t* __restrict__ params,
                                                         const uint16_t* __restrict__ xb,
                                                         float* __restrict__ y, int n, int k, int m,
                                                         int tiles_m, int nblocks) {
-  using T = Tile<BM, WGN>;
-  using C = CodeTile<S, T::KS, T::BN>;
+  using T = Tile<BM, WGN, NW>;
+  using C = CodeTile<S, T::KS, T::BN, NW>;
   constexpr int bits = Fmt<S>::bits;
   constexpr int PB = param_bytes_per_group(S);
   constexpr int WIN = param_window(G, T::KS);     // groups per parameter window
   constexpr int SPW = WIN * G / T::KS;            // steps per parameter window
-  constexpr int PPW = T::BN * WIN / (64 * kWaves);  // parameter copies per wave per window
+  constexpr int PPW = T::BN * WIN / (64 * NW);    // parameter copies per wave per window
   constexpr int PBYTES = T::BN * WIN * 4;         // one window: a dword slot per group
   static_assert(SPW >= kDC && PPW >= 1, "parameter window shape");
   static_assert(G >= kKW / 2, "a lane's 16 codes lie in one group");
@@ -244,22 +243,17 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint8_t* __restric
     return row < n ? row : n - 1;  // rows past N: computed, not stored
   };
 
-  // Activation copy: thread tid moves 16-byte slot q = i * 512 + tid of the
+  // Activation copy: thread tid moves 16-byte slot q = i * NT + tid of the
   // step's tile (row q / CPR, physical chunk q % CPR, which holds logical
   // chunk (q % CPR) ^ (row & 15)).  RPI is a multiple of 16, so the logical
   // chunk is the same for every i.
   const int r0 = tid / T::CPR;
   const int cl = (tid % T::CPR) ^ (r0 & 15);
-  // Sources are a base common to the workgroup plus a 32-bit lane offset
-  // (the tile spans at most 128 rows of at most 2^16 elements).
+  // Sources are a base common to the workgroup (per copy i) plus a 32-bit lane
+  // offset.  The workspace holds whole 128-row tiles, so rows past M are read
+  // without clamping (their outputs are not stored).
   const uint16_t* abase = xb + size_t(bm) * size_t(k);
-  uint32_t aoff[T::ALOADS];
-#pragma unroll
-  for (int i = 0; i < T::ALOADS; ++i) {
-    int r = bm + i * T::RPI + r0;
-    r = r < m ? r : m - 1;  // rows past M: any valid row (their outputs are not stored)
-    aoff[i] = uint32_t(r - bm) * uint32_t(k);
-  }
+  const uint32_t alane = uint32_t(r0) * uint32_t(k);
 
   // Code copy j of this wave: lane slot q -> row r = piece / PPR, logical
   // piece p = (piece % PPR) ^ swz(r); 4-byte lanes take dword q % 4 of it.
@@ -334,8 +328,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint8_t* __restric
 #pragma unroll
     for (int i = 0; i < T::ALOADS; ++i)
       if (part < 0 || i % kSUB == part)
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(abase + (aoff[i] + uint32_t(col))),
-                                         (__attribute__((address_space(3))) void*)(adst + i * kThreads * 16), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(abase + size_t(i) * T::RPI * size_t(k) + (alane + uint32_t(col))),
+                                         (__attribute__((address_space(3))) void*)(adst + i * T::NT * 16), 16, 0, 0);
   };
   auto issue_codes = [&](int st, int cset) __attribute__((always_inline)) {
     uint8_t* cdst = cbuf(cset) + wave * C::PER_WAVE * 64 * C::EL;
@@ -610,10 +604,10 @@ hipError_t activation_workspace(hipStream_t stream, size_t bytes, void** out) {
   return hipSuccess;
 }
 
-template <int S, int G, int BM, int WGN>
+template <int S, int G, int BM, int WGN, int NW>
 hipError_t launch(const uq_layout* L, const void* codes, const void* params, const uint16_t* xb,
                   float* y, int m, hipStream_t stream) {
-  using T = Tile<BM, WGN>;
+  using T = Tile<BM, WGN, NW>;
   int n = int(L->n), k = int(L->k);
   int tiles_m = (m + BM - 1) / BM;
   const int64_t tiles_n = (int64_t(n) + T::BN - 1) / T::BN;
@@ -623,16 +617,20 @@ hipError_t launch(const uq_layout* L, const void* codes, const void* params, con
   const uint8_t* c8 = static_cast<const uint8_t*>(codes);
   const uint8_t* p8 = static_cast<const uint8_t*>(params);
   void* args[] = {&c8, &p8, (void*)&xb, &y, &n, &k, &m, &tiles_m, &nblocks};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&gemm_kernel<S, G, BM, WGN>), dim3(unsigned(nblocks)),
-                         dim3(kThreads), args, 0, stream);
+  return hipLaunchKernel(reinterpret_cast<const void*>(&gemm_kernel<S, G, BM, WGN, NW>), dim3(unsigned(nblocks)),
+                         dim3(T::NT), args, 0, stream);
 }
 
+// Tilings by M: 8 waves (two per SIMD), BM = 32, 64 or 128.  (A 256-row tile
+// on 4 waves, one per SIMD with the accumulators in AGPRs, halves the dequant
+// work per MFMA but measured slower: a lone wave per SIMD hides neither the
+// copies' waits nor the LDS latency.)
 template <int S, int G>
 hipError_t launch_tiles(const uq_layout* L, const void* codes, const void* params, const uint16_t* xb,
                         float* y, int m, hipStream_t stream) {
-  if (m <= 32) return launch<S, G, 32, 1>(L, codes, params, xb, y, m, stream);
-  if (m <= 64) return launch<S, G, 64, 1>(L, codes, params, xb, y, m, stream);
-  return launch<S, G, 128, 2>(L, codes, params, xb, y, m, stream);
+  if (m <= 32) return launch<S, G, 32, 1, 8>(L, codes, params, xb, y, m, stream);
+  if (m <= 64) return launch<S, G, 64, 1, 8>(L, codes, params, xb, y, m, stream);
+  return launch<S, G, 128, 2, 8>(L, codes, params, xb, y, m, stream);
 }
 
 }  // namespace
@@ -640,8 +638,11 @@ hipError_t launch_tiles(const uq_layout* L, const void* codes, const void* param
 hipError_t launch_gemm(const uq_layout* L, const void* codes, const void* params, const uint16_t* x,
                        float* y, int m, hipStream_t stream) {
   const int64_t count = int64_t(m) * L->k;  // k % 32 == 0: whole 8-value pieces
+  // Whole 128-row tiles: the GEMM reads rows past M without clamping (their
+  // products are never stored).
+  const int64_t rows = (int64_t(m) + 127) / 128 * 128;
   void* ws = nullptr;
-  hipError_t e = activation_workspace(stream, size_t(count) * 2, &ws);
+  hipError_t e = activation_workspace(stream, size_t(rows * L->k) * 2, &ws);
   if (e != hipSuccess) return e;
   uint16_t* xb = static_cast<uint16_t*>(ws);
   {

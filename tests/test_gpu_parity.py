@@ -177,6 +177,20 @@ def test_gemm_parity_small(lib, scheme, group):
             gate(y, o.gemm_ref(x[:m], wdq), xb, o.bf16_rne(wdq), f"gemm {scheme} G{group} m={m}")
 
 
+@pytest.mark.parametrize("scheme,group", [("int4", 128), ("int2", 16), ("int8", 64), ("nf4", 64)])
+def test_gemm_several_row_tiles(lib, scheme, group):
+    """M past one 256-row tile, with a partial last tile (rows past M are computed, not stored)."""
+    n, k = 100, 512
+    w, x = workloads.make_random(n, k, 513, seed=21, outliers=True)
+    lay, codes, params = packed_on_device(lib, scheme, group, w)
+    wdq = oracle_dequant(w, scheme, group)
+    for m in (129, 255, 256, 257, 300, 513):
+        note(f"gemm row tiles {scheme} G{group} m={m}")
+        y = run_gemm(lib, lay, codes, params, x, m)
+        xb = o.bf16_rne(x[:m].astype(np.float32))
+        gate(y, o.gemm_ref(x[:m], wdq), xb, o.bf16_rne(wdq), f"gemm {scheme} G{group} m={m}")
+
+
 @pytest.mark.parametrize("scheme,group", ALL_LAYOUTS)
 def test_gemm_identity_bit_exact(lib, scheme, group):
     """X = I (M = K) returns bf16(w')^T exactly."""
