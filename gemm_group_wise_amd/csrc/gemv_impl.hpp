@@ -16,7 +16,9 @@
 //     device_common.hpp), with two sums per group part: SX = sum x and
 //     C = 1024 * sum x'.  The lane forms t = sum (1024 + cls*q) * x/cls - C
 //     = sum q*x with packed fp16 dot products (fp32 accumulation) and adds
-//     s*t + z*SX, which is sum x*(q*s + z).  NF4: a * sum C16[q]*x.
+//     s*t + z*SX, which is sum x*(q*s + z).  NF4: a * sum (H[q] + L[q])*x,
+//     the codebook split into fp16 high and low parts (two dot products, no
+//     rounding of the codebook in the products).
 //   * Lane partials are summed across the wave with DPP and lane swizzles.
 #pragma once
 
@@ -112,13 +114,18 @@ __device__ __forceinline__ void load_pairs(const uint32_t* src, f16x2 (&xp)[PPD]
 }
 
 template <int S>
-__device__ __forceinline__ void unpack_dword(uint32_t w, uint32_t magic, const uint32_t* lut,
-                                             f16x2 (&hp)[Fmt<S>::PPD]) {
-  if constexpr (S == UQ_NF4) {
+__device__ __forceinline__ void unpack_dword(uint32_t w, uint32_t magic, f16x2 (&hp)[Fmt<S>::PPD]) {
+  unpack_pairs<S>(w, magic, hp);
+}
+
+// NF4: byte j of w -> the high and low fp16 parts of its two codes' values
+// (one 8-byte table entry: high pair, low pair).
+__device__ __forceinline__ void unpack_nf4(uint32_t w, const uint2* lut, f16x2 (&hp)[4], f16x2 (&lp)[4]) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) hp[j] = as_h2(lut[(w >> (8 * j)) & 0xFFu]);
-  } else {
-    unpack_pairs<S>(w, magic, hp);
+  for (int j = 0; j < 4; ++j) {
+    const uint2 e = lut[(w >> (8 * j)) & 0xFFu];
+    hp[j] = as_h2(e.x);
+    lp[j] = as_h2(e.y);
   }
 }
 
@@ -162,8 +169,8 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
 
   extern __shared__ uint4 lds4[];
   uint32_t* lds = reinterpret_cast<uint32_t*>(lds4);
-  uint32_t* lut = lds;                              // NF4: 256 fp16 pairs
-  uint32_t* xs = lds + (NF ? 256 : 0);              // [MT][kb_max/2] fp16 pairs
+  uint2* lut = reinterpret_cast<uint2*>(lds);       // NF4: 256 x (high pair, low pair)
+  uint32_t* xs = lds + (NF ? 512 : 0);              // [MT][kb_max/2] fp16 pairs
   float2* cs = reinterpret_cast<float2*>(xs + MT * (kb_max / 2));  // [MT][kb_max/GP]
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -185,9 +192,13 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
   const uint32_t magic = kMagic2;
 
   if constexpr (NF) {
-    // byte b -> (fp16(C[b & 15]), fp16(C[b >> 4]))
-    const _Float16 lo = _Float16(nf4_value(tid & 15)), hi = _Float16(nf4_value(tid >> 4));
-    lut[tid] = as_u32(f16x2{lo, hi});
+    // byte b -> the codes' values C[b & 15], C[b >> 4] as a pair of fp16 high
+    // parts h = fp16(C) and a pair of low parts l = fp16(C - h): h + l holds
+    // C to about 2^-22, and the dot products of x with h and with l are exact
+    // in fp32, so the NF4 products carry no rounding of the codebook.
+    const float c0 = nf4_value(tid & 15), c1 = nf4_value(tid >> 4);
+    const _Float16 h0 = _Float16(c0), h1 = _Float16(c1);
+    lut[tid] = make_uint2(as_u32(f16x2{h0, h1}), as_u32(f16x2{_Float16(c0 - float(h0)), _Float16(c1 - float(h1))}));
   }
 
   float acc_y[R][MT];
@@ -324,12 +335,17 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
 #pragma unroll
               for (int dl = 0; dl < DPG; ++dl) {
                 const int dd = pp * DPG + dl;
-                f16x2 hp[PPD];
-                unpack_dword<S>(dword_of(cur[u].code[r], dd), magic, lut, hp);
+                f16x2 hp[PPD], lp[NF ? PPD : 1];
+                if constexpr (NF) unpack_nf4(dword_of(cur[u].code[r], dd), lut, hp, lp);
+                else unpack_dword<S>(dword_of(cur[u].code[r], dd), magic, hp);
+                // (the same order of additions as the dword-outer path below)
 #pragma unroll
                 for (int mm = 0; mm < MT; ++mm)
 #pragma unroll
-                  for (int j = 0; j < PPD; ++j) acc[mm] = __builtin_amdgcn_fdot2(hp[j], xp[mm][dd][j], acc[mm], false);
+                  for (int j = 0; j < PPD; ++j) {
+                    acc[mm] = __builtin_amdgcn_fdot2(hp[j], xp[mm][dd][j], acc[mm], false);
+                    if constexpr (NF) acc[mm] = __builtin_amdgcn_fdot2(lp[j], xp[mm][dd][j], acc[mm], false);
+                  }
               }
               apply_group<NF>(valid ? cur[u].par[r][pp] : 0u, acc, cv, pp, acc_y[r]);
             }
@@ -352,8 +368,12 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
             for (int dl = 0; dl < DPG; ++dl) {
               const int dd = pp * DPG + dl;
               f16x2 hp[R][PPD];
+              f16x2 lp[R][NF ? 4 : 1];
 #pragma unroll
-              for (int r = 0; r < R; ++r) unpack_dword<S>(dword_of(cur[u].code[r], dd), magic, lut, hp[r]);
+              for (int r = 0; r < R; ++r) {
+                if constexpr (NF) unpack_nf4(dword_of(cur[u].code[r], dd), lut, hp[r], lp[r]);
+                else unpack_dword<S>(dword_of(cur[u].code[r], dd), magic, hp[r]);
+              }
 #pragma unroll
               for (int mm = 0; mm < MT; ++mm) {
                 f16x2 xq[PPD];
@@ -361,8 +381,10 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
 #pragma unroll
                 for (int r = 0; r < R; ++r)
 #pragma unroll
-                  for (int j = 0; j < PPD; ++j)
+                  for (int j = 0; j < PPD; ++j) {
                     acc[r][mm] = __builtin_amdgcn_fdot2(hp[r][j], xq[j], acc[r][mm], false);
+                    if constexpr (NF) acc[r][mm] = __builtin_amdgcn_fdot2(lp[r][j], xq[j], acc[r][mm], false);
+                  }
               }
             }
 #pragma unroll
@@ -425,7 +447,7 @@ hipError_t launch(const uq_layout* L, const void* codes, const void* params, con
   const int k = int(L->k), n = int(L->n);
   int kb_max = kXBlock / MT;
   if (kb_max > k) kb_max = k;
-  const size_t shmem = (Gm::NF ? 1024 : 0) + size_t(MT) * kb_max * 2 +
+  const size_t shmem = (Gm::NF ? 2048 : 0) + size_t(MT) * kb_max * 2 +
                        (Gm::NF ? 0 : size_t(MT) * (kb_max / Gm::GP) * 8);
   const int rows_per_block = kWaves * R;
   const dim3 grid(unsigned((n + rows_per_block - 1) / rows_per_block));

@@ -94,7 +94,8 @@ def test_gemv_one_hot_bit_exact(lib, scheme, group):
 
 
 def test_gemv_one_hot_nf4(lib):
-    """NF4 products use the codebook rounded to fp16: within 2^-11 relative of w'."""
+    """NF4 products use the codebook as fp16 high + low parts (about 22 bits): x = e_k
+    gives w' to within 2^-20 relative (plus 2^-23 of the largest weight for codes near 0)."""
     n, k = 45, 256
     w, _ = workloads.make_random(n, k, 1, seed=7)
     lay, codes, params = packed_on_device(lib, "nf4", 64, w)
@@ -106,7 +107,7 @@ def test_gemv_one_hot_nf4(lib):
     note("gemv one-hot nf4")
     y = run_gemv(lib, lay, codes, params, x, 4)
     want = np.stack([wdq[:, c] for c in cols]).astype(np.float64)
-    assert (np.abs(y - want) <= np.abs(want) * 2.0 ** -11 + 1e-30).all()
+    assert (np.abs(y - want) <= np.abs(want) * 2.0 ** -20 + 2.0 ** -23 * np.abs(wdq).max()).all()
 
 
 def test_gemv_batched_equivalence(lib):
