@@ -388,3 +388,93 @@ def check_rope_bruteforce(o, seed=3):
                 ya = u[i] * c - u[i + h] * s
                 yb = u[i + h] * c + u[i] * s
                 assert abs(y[t, hh, i] - ya) <= 1e-6 and abs(y[t, hh, i + h] - yb) <= 1e-6, (t, hh, i)
+
+
+# ---------------------------------------------------------------------------
+# Dynamic activation quantization and the integer-dot GEMV (R-AQ, R-AD)
+# ---------------------------------------------------------------------------
+def check_a8_grid(o, group=32, m=3, groups=4, seed=4):
+    """Groups built on the grid j * 2^e with a +-127 * 2^e element: the codes are
+    j exactly and s_x = 2^e; points halfway between grid values round to even."""
+    rng = np.random.default_rng(seed)
+    k = group * groups
+    x = np.zeros((m, k), dtype=np.float64)
+    want_q = np.zeros((m, k), dtype=np.int64)
+    want_s = np.zeros((m, groups), dtype=np.float64)
+    for i in range(m):
+        for g in range(groups):
+            e = int(rng.integers(-10, 4))
+            j = rng.integers(-126, 127, size=group)
+            j[0] = 127 if rng.random() < 0.5 else -127
+            half = np.zeros(group)
+            half[1:5] = 0.5                         # (j + 0.5) * 2^e: a tie for rint
+            j[1:5] = rng.integers(-100, 100, size=4)
+            x[i, g * group:(g + 1) * group] = (j + half) * 2.0 ** e
+            rounded = j + np.where(half > 0, np.where(j % 2 == 0, 0, 1), 0)  # ties to even
+            want_q[i, g * group:(g + 1) * group] = rounded
+            want_s[i, g] = 2.0 ** e
+    x16 = x.astype(np.float16)
+    assert np.array_equal(x16.astype(np.float64), x), "grid values must be exact in fp16"
+    q, s_x = o.quantize_activations(x16, group)
+    assert q.dtype == np.int8
+    assert np.array_equal(q.astype(np.int64), want_q)
+    assert np.array_equal(s_x.astype(np.float64), want_s)
+
+
+def check_a8_roundtrip(o, group=64, seed=5):
+    """|x - s_x q| <= s_x / 2 (plus fp32 slop); each group's largest |x| maps to +-127;
+    codes stay in [-127, 127]; an all-zero group gives codes 0 and scale 0."""
+    rng = np.random.default_rng(seed)
+    m, k = 4, group * 6
+    x = (rng.standard_normal((m, k)) * rng.choice([1e-3, 1.0, 300.0], size=(m, 1))).astype(np.float16)
+    x[1, group:2 * group] = 0
+    q, s_x = o.quantize_activations(x, group)
+    qg = q.astype(np.int64).reshape(m, k // group, group)
+    xg = x.astype(np.float64).reshape(m, k // group, group)
+    sx = s_x.astype(np.float64)[..., None]
+    assert (np.abs(qg) <= 127).all()
+    assert (np.abs(xg - sx * qg) <= sx * (0.5 + 2.0 ** -18)).all()
+    top = np.abs(xg).argmax(axis=-1)
+    hit = np.take_along_axis(np.abs(qg), top[..., None], axis=-1)[..., 0]
+    nz = np.abs(xg).max(axis=-1) > 0
+    assert (hit[nz] == 127).all()
+    assert (qg[1, 1] == 0).all() and s_x[1, 1] == 0
+
+
+def check_a8_products(o, seed=6):
+    """The grouped integer form equals the plain dot product of the dequantized
+    activations and weights (both fp64), on non-square shapes."""
+    rng = np.random.default_rng(seed)
+    for bits, group in ((2, 16), (4, 64), (8, 128)):
+        m, n, k = 3, 5, group * 5
+        x = (rng.standard_normal((m, k)) * 2.0).astype(np.float16)
+        w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+        q_w, s16, z16 = o.quantize_int(w, bits, group)
+        q_x, s_x = o.quantize_activations(x, group)
+        y = o.gemv_a8_ref(q_x, s_x, q_w, s16, z16, group)
+        xd = o.dequant_activations(q_x, s_x, group)
+        wd = (q_w.astype(np.float64).reshape(n, k // group, group) * s16.astype(np.float64)[..., None]
+              + z16.astype(np.float64)[..., None]).reshape(n, k)
+        want = xd @ wd.T
+        assert y.shape == (m, n)
+        assert np.allclose(y, want, rtol=1e-12, atol=1e-12 * np.abs(want).max())
+
+
+def check_a8_bruteforce(o, seed=7):
+    """Element-by-element loops on a tiny case (m=2, n=3, k=64, G=16)."""
+    rng = np.random.default_rng(seed)
+    m, n, k, group = 2, 3, 64, 16
+    x = (rng.standard_normal((m, k)) * 3.0).astype(np.float16)
+    w = (rng.standard_normal((n, k)) * 0.05).astype(np.float32)
+    q_w, s16, z16 = o.quantize_int(w, 4, group)
+    q_x, s_x = o.quantize_activations(x, group)
+    y = o.gemv_a8_ref(q_x, s_x, q_w, s16, z16, group)
+    for i in range(m):
+        for j in range(n):
+            acc = 0.0
+            for t in range(k):
+                g = t // group
+                xv = float(s_x[i, g]) * int(q_x[i, t])
+                wv = int(q_w[j, t]) * float(s16[j, g]) + float(z16[j, g])
+                acc += xv * wv
+            assert abs(acc - y[i, j]) <= 1e-12 * max(1.0, abs(acc))

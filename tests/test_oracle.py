@@ -144,3 +144,20 @@ def test_norm_rope_gate():
     i = np.unravel_index(np.argmax(np.abs(ref)), ref.shape)
     bad[i] += 3 * o.fp16_spacing(ref[i])
     assert not o.within_gate(bad, ref).all()
+
+
+# Dynamic activation quantization and the integer-dot GEMV (R-AQ, R-AD)
+def test_a8_grid():
+    pins.check_a8_grid(o)
+
+
+def test_a8_roundtrip():
+    pins.check_a8_roundtrip(o)
+
+
+def test_a8_products():
+    pins.check_a8_products(o)
+
+
+def test_a8_bruteforce():
+    pins.check_a8_bruteforce(o)

@@ -130,6 +130,46 @@ def rope_table_wrong_exponent(theta, d, max_pos):
     return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
 
 
+def a8_per_row_scale(x16, group):
+    # one scale for the whole activation row instead of one per group
+    x = np.asarray(x16, dtype=np.float16).astype(np.float32)
+    m, k = x.shape
+    a = np.abs(x).max(axis=1, keepdims=True)
+    r = np.where(a > 0, np.float32(127) / np.where(a > 0, a, 1), 0).astype(np.float32)
+    q = np.clip(np.rint((x * r).astype(np.float32)), -127, 127).astype(np.int8)
+    s = np.repeat((a / np.float32(127)).astype(np.float32), k // group, axis=1)
+    return q, s
+
+
+def a8_qmax_128(x16, group):
+    x = np.asarray(x16, dtype=np.float16).astype(np.float32)
+    m, k = x.shape
+    xg = x.reshape(m, k // group, group)
+    a = np.abs(xg).max(axis=-1)
+    r = np.where(a > 0, np.float32(128) / np.where(a > 0, a, 1), 0).astype(np.float32)
+    q = np.clip(np.rint((xg * r[..., None]).astype(np.float32)), -127, 127).astype(np.int8)
+    return q.reshape(m, k), (a / np.float32(128)).astype(np.float32)
+
+
+def a8_floor(x16, group):
+    x = np.asarray(x16, dtype=np.float16).astype(np.float32)
+    m, k = x.shape
+    xg = x.reshape(m, k // group, group)
+    a = np.abs(xg).max(axis=-1)
+    r = np.where(a > 0, np.float32(127) / np.where(a > 0, a, 1), 0).astype(np.float32)
+    q = np.clip(np.floor((xg * r[..., None]).astype(np.float32)), -127, 127).astype(np.int8)
+    return q.reshape(m, k), (a / np.float32(127)).astype(np.float32)
+
+
+def a8_drop_zero_term(q_x, s_x, q_w, s16, z16, group):
+    return o.gemv_a8_ref(q_x, s_x, q_w, s16, np.zeros_like(z16), group)
+
+
+def a8_scale_by_next_group(q_x, s_x, q_w, s16, z16, group):
+    # activation scales taken one group off
+    return o.gemv_a8_ref(q_x, np.roll(s_x, 1, axis=1), q_w, s16, z16, group)
+
+
 CASES = [
     ("dequant drops the zero term", dict(dequant_int=dequant_drop_zero),
      lambda ns: pins.check_grid_recovery(ns, 4, 64)),
@@ -166,6 +206,16 @@ CASES = [
      lambda ns: pins.check_rope_bruteforce(ns)),
     ("RoPE frequencies theta^(-i/D)", dict(rope_table=rope_table_wrong_exponent),
      lambda ns: pins.check_rope_table(ns)),
+    ("A8 one scale per row", dict(quantize_activations=a8_per_row_scale),
+     lambda ns: pins.check_a8_grid(ns)),
+    ("A8 scale 128", dict(quantize_activations=a8_qmax_128),
+     lambda ns: pins.check_a8_grid(ns)),
+    ("A8 floor codes", dict(quantize_activations=a8_floor),
+     lambda ns: pins.check_a8_roundtrip(ns)),
+    ("A8 drops the zero term", dict(gemv_a8_ref=a8_drop_zero_term),
+     lambda ns: pins.check_a8_products(ns)),
+    ("A8 scales one group off", dict(gemv_a8_ref=a8_scale_by_next_group),
+     lambda ns: pins.check_a8_bruteforce(ns)),
 ]
 
 
