@@ -42,7 +42,7 @@ class Layout(ctypes.Structure):
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
-                      "(or python -m gemm_group_wise_amd.build)")
+                      "(or python gemm_group_wise_amd/build.py)")
 
 # torch ships its own HIP runtime, which its libraries load by the unversioned
 # name libamdhip64.so.  libuq.so asks for libamdhip64.so.7; if it were opened
@@ -62,6 +62,8 @@ _lib.uq_pack_weights.argtypes = [_L, _P, _P, _P]
 _lib.uq_gemv.argtypes = [_L, _P, _P, _P, _P, ctypes.c_int64, _P]
 _lib.uq_gemm.argtypes = [_L, _P, _P, _P, _P, ctypes.c_int64, _P]
 _lib.uq_dequant.argtypes = [_L, _P, _P, _P, _P]
+_lib.uq_gemv_a8.argtypes = [_L, _P, _P, _P, _P, ctypes.c_int64, _P]
+_lib.uq_quantize_activations.argtypes = [ctypes.c_int32, _P, _P, _P, ctypes.c_int64, ctypes.c_int64, _P]
 _lib.uq_nf4_codebook.argtypes = [_P]
 _lib.uq_rope_table.argtypes = [ctypes.c_double, ctypes.c_int32, ctypes.c_int64, _P, _P]
 _lib.uq_rmsnorm_rope.argtypes = [_P, _P, _P, _P, _P, _P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
@@ -69,11 +71,12 @@ _lib.uq_rmsnorm_rope.argtypes = [_P, _P, _P, _P, _P, _P, ctypes.c_int64, ctypes.
 _lib.uq_status_str.argtypes = [ctypes.c_int]
 _lib.uq_status_str.restype = ctypes.c_char_p
 for _fn in ("uq_packed_size", "uq_pack_weights", "uq_gemv", "uq_gemm", "uq_dequant",
-            "uq_nf4_codebook", "uq_rope_table", "uq_rmsnorm_rope"):
+            "uq_nf4_codebook", "uq_rope_table", "uq_rmsnorm_rope", "uq_gemv_a8", "uq_quantize_activations"):
     getattr(_lib, _fn).restype = ctypes.c_int
 
 EXPORTS = ("uq_packed_size", "uq_pack_weights", "uq_gemv", "uq_gemm", "uq_dequant",
-           "uq_nf4_codebook", "uq_rope_table", "uq_rmsnorm_rope", "uq_status_str")
+           "uq_nf4_codebook", "uq_rope_table", "uq_rmsnorm_rope", "uq_gemv_a8", "uq_quantize_activations",
+           "uq_status_str")
 
 
 def _check(fn: str, status: int):
@@ -132,6 +135,16 @@ def uq_gemv(lay: Layout, codes, params, x, y, m: int, stream=None) -> None:
 def uq_gemm(lay: Layout, codes, params, x, y, m: int, stream=None) -> None:
     _check("uq_gemm", _lib.uq_gemm(ctypes.byref(lay), _ptr(codes), _ptr(params), _ptr(x), _ptr(y),
                                    int(m), _stream(stream)))
+
+
+def uq_gemv_a8(lay: Layout, codes, params, x, y, m: int, stream=None) -> None:
+    _check("uq_gemv_a8", _lib.uq_gemv_a8(ctypes.byref(lay), _ptr(codes), _ptr(params), _ptr(x), _ptr(y),
+                                         int(m), _stream(stream)))
+
+
+def uq_quantize_activations(group: int, x, q, sx, m: int, k: int, stream=None) -> None:
+    _check("uq_quantize_activations", _lib.uq_quantize_activations(int(group), _ptr(x), _ptr(q), _ptr(sx),
+                                                                   int(m), int(k), _stream(stream)))
 
 
 def uq_dequant(lay: Layout, codes, params, w, stream=None) -> None:

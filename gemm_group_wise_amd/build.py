@@ -1,6 +1,6 @@
 """Build libuq.so in-tree: HIP kernels for gfx950 plus the host packer.
 
-    python -m gemm_group_wise_amd.build        # or __graft_entry__.build()
+    python gemm_group_wise_amd/build.py        # or __graft_entry__.build()
 
 The host packer is plain C++ (g++, -ffp-contract=off) so its fp32/fp64
 arithmetic is one IEEE operation per step; the kernels and the C ABI are
@@ -23,7 +23,7 @@ LIB = os.path.join(PKG, "libuq.so")
 
 ARCH = "gfx950"
 HIP_SOURCES = ["uq_api.hip", "gemv.hip", "gemv_int2.hip", "gemv_int4.hip", "gemv_int8.hip",
-               "gemv_nf4.hip", "gemm.hip", "dequant.hip", "rmsnorm_rope.hip"]
+               "gemv_nf4.hip", "gemm.hip", "dequant.hip", "rmsnorm_rope.hip", "gemv_a8.hip"]
 CXX_SOURCES = ["uq_pack.cpp", "rope_table.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -15,6 +15,10 @@ hipError_t launch_gemm(const uq_layout* L, const void* codes, const void* params
                        float* y, int m, hipStream_t stream);
 hipError_t launch_dequant(const uq_layout* L, const void* codes, const void* params, float* w,
                           hipStream_t stream);
+hipError_t launch_gemv_a8(const uq_layout* L, const void* codes, const void* params, const uint16_t* x,
+                          float* y, int m, hipStream_t stream);
+hipError_t launch_quantize_a8(int32_t group, const uint16_t* x, int8_t* q, float* sx, int64_t m, int64_t k,
+                              hipStream_t stream);
 hipError_t launch_rmsnorm_rope(const uint16_t* x, uint16_t* y, const float* gamma, const int32_t* pos,
                                const float* cos_tab, const float* sin_tab, int64_t tokens, int32_t heads,
                                int32_t head_dim, int64_t max_pos, float eps, hipStream_t stream);
@@ -77,6 +81,26 @@ uq_status uq_dequant(const uq_layout* layout, const void* codes, const void* par
   if (!codes || !params || !w) return UQ_ERR_NULL;
   if (!uq::aligned16(codes) || !uq::aligned16(params) || !uq::aligned16(w)) return UQ_ERR_ALIGN;
   const hipError_t e = uq::launch_dequant(layout, codes, params, w, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? UQ_OK : UQ_ERR_HIP;
+}
+
+uq_status uq_gemv_a8(const uq_layout* layout, const void* codes, const void* params,
+                     const uint16_t* x, float* y, int64_t m, void* stream) {
+  const uq_status st = uq::check_product(layout, codes, params, x, y, m, UQ_GEMV_MAX_M);
+  if (st != UQ_OK) return st;
+  if (layout->scheme == UQ_NF4) return UQ_ERR_UNSUPPORTED;
+  const hipError_t e =
+      uq::launch_gemv_a8(layout, codes, params, x, y, int(m), static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? UQ_OK : UQ_ERR_HIP;
+}
+
+uq_status uq_quantize_activations(int32_t group, const uint16_t* x, int8_t* q, float* sx, int64_t m,
+                                  int64_t k, void* stream) {
+  if (!x || !q || !sx) return UQ_ERR_NULL;
+  if (group != 16 && group != 32 && group != 64 && group != 128) return UQ_ERR_UNSUPPORTED;
+  if (m < 1 || m > UQ_GEMM_MAX_M || k < 16 || k > uq::kMaxK || k % group || k % 16) return UQ_ERR_SHAPE;
+  if (!uq::aligned16(x) || !uq::aligned16(q) || (reinterpret_cast<uintptr_t>(sx) & 3u)) return UQ_ERR_ALIGN;
+  const hipError_t e = uq::launch_quantize_a8(group, x, q, sx, m, k, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? UQ_OK : UQ_ERR_HIP;
 }
 

@@ -107,7 +107,7 @@ uq_status uq_pack_weights(const uq_layout* layout, const float* w,
  *   y : device fp32 [m][n] row-major, 16-byte aligned, overwritten
  * The products are formed from fp16 activations with fp32 accumulation;
  * results match fp64 x . w'^T to within rounding (the NF4 codebook enters
- * the products rounded to fp16). */
+ * the products as fp16 high and low parts, about 22 bits). */
 uq_status uq_gemv(const uq_layout* layout, const void* codes,
                   const void* params, const uint16_t* x, float* y, int64_t m,
                   void* stream);
@@ -119,7 +119,8 @@ uq_status uq_gemv(const uq_layout* layout, const void* codes,
  * fixed by (layout, m), so repeated calls give identical bits.
  * Arguments as for uq_gemv.
  * Workspace: bf16(x) is staged in device memory the library owns, one buffer
- * per (device, stream), m * k * 2 bytes, allocated with hipMalloc by the first
+ * per (device, stream), m' * k * 2 bytes with m' = m rounded up to a multiple
+ * of 128, allocated with hipMalloc by the first
  * call that needs it to be larger (at least doubling) and kept until the
  * process ends.  Calls on one stream are ordered by the stream; calls on
  * different streams use different buffers.  A call that would have to grow
@@ -135,6 +136,31 @@ uq_status uq_gemm(const uq_layout* layout, const void* codes,
  *   w : device fp32 [n][k] row-major, 16-byte aligned, overwritten */
 uq_status uq_dequant(const uq_layout* layout, const void* codes,
                      const void* params, float* w, void* stream);
+
+/* ---- Dynamically quantized activations (Core Components > Quantized Model:
+ * the quantized layers quantize their activations on the fly; the page names
+ * no scheme, so this one is a reading). ----
+ *
+ * GEMV with int8 activations for the INT family (INT2/4/8 weights):
+ *   per activation row m and weight group g, a = max |x[m][k]| over the group,
+ *   q_x = clamp(rint(x * (127 / a)), -127, 127) with 127 / a and the product
+ *   rounded to fp32 (ties to even; a = 0 gives q_x = 0), s_x = a / 127 (fp32);
+ *   y[m][n] = sum_g s_x[m][g] * (s[n][g] * D + z[n][g] * Q),
+ *   D = sum_{k in g} q_w[n][k] * q_x[m][k],  Q = sum_{k in g} q_x[m][k]
+ * with D and Q exact integers and the scaling in fp32, for 1 <= m <= 8.
+ * Arguments as for uq_gemv.  NF4 layouts return UQ_ERR_UNSUPPORTED (its
+ * codebook values are not integers).  Allocates nothing. */
+uq_status uq_gemv_a8(const uq_layout* layout, const void* codes,
+                     const void* params, const uint16_t* x, float* y, int64_t m,
+                     void* stream);
+
+/* The activation quantization of uq_gemv_a8 on its own (test hook):
+ *   x  : device fp16 [m][k] (uint16 bits), 16-byte aligned, k % group == 0, k % 16 == 0
+ *   q  : device int8 [m][k], 16-byte aligned, overwritten with q_x
+ *   sx : device fp32 [m][k / group], 4-byte aligned, overwritten with s_x
+ * group in {16, 32, 64, 128}; 1 <= m <= 65536; 16 <= k <= 2^24. */
+uq_status uq_quantize_activations(int32_t group, const uint16_t* x, int8_t* q,
+                                  float* sx, int64_t m, int64_t k, void* stream);
 
 /* The 16 NF4 codebook entries (fp32) the library uses; host call. */
 uq_status uq_nf4_codebook(float out[16]);

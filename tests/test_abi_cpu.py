@@ -144,7 +144,7 @@ def test_pack_rejects_non_finite_and_huge(lib):
     assert lib.raw_call("uq_pack_weights", ctypes.byref(lay), w.ctypes.data, None, None) == 1
 
 
-@pytest.mark.parametrize("fn", ["uq_gemv", "uq_gemm"])
+@pytest.mark.parametrize("fn", ["uq_gemv", "uq_gemm", "uq_gemv_a8"])
 def test_product_validation(lib, fn):
     lay = lib.layout("int4", 64, 128, 256)
     A = 1 << 20  # fake, 16-byte aligned addresses: never dereferenced
@@ -153,7 +153,7 @@ def test_product_validation(lib, fn):
     assert lib.raw_call(fn, s(lay), None, A, A, A, 1, None) == 1                 # null codes
     assert lib.raw_call(fn, s(lay), A, A, A, None, 1, None) == 1                 # null y
     assert lib.raw_call(fn, s(lay), A, A, A, A, 0, None) == 2                    # m = 0
-    mmax = 8 if fn == "uq_gemv" else 65536
+    mmax = 8 if fn in ("uq_gemv", "uq_gemv_a8") else 65536
     assert lib.raw_call(fn, s(lay), A, A, A, A, mmax + 1, None) == 2             # m too big
     assert lib.raw_call(fn, s(lay), A + 4, A, A, A, 1, None) == 4                # misaligned
     assert lib.raw_call(fn, s(lay), A, A, A + 2, A, 1, None) == 4
@@ -162,6 +162,28 @@ def test_product_validation(lib, fn):
     assert lib.raw_call(fn, s(bad), A, A, A, A, 1, None) == 2
     badg = lib.layout("int4", 16, 128, 256)
     assert lib.raw_call(fn, s(badg), A, A, A, A, 1, None) == 3
+
+
+def test_gemv_a8_rejects_nf4(lib):
+    """The integer-dot path is defined for INT weights only; NF4 is refused before any HIP call."""
+    A = 1 << 20
+    lay = lib.layout("nf4", 64, 128, 256)
+    assert lib.raw_call("uq_gemv_a8", ctypes.byref(lay), A, A, A, A, 1, None) == 3
+
+
+def test_quantize_activations_validation(lib):
+    A = 1 << 20  # fake, 16-byte aligned addresses: never dereferenced
+    f = "uq_quantize_activations"
+    assert lib.raw_call(f, 64, None, A, A, 1, 256, None) == 1          # null x
+    assert lib.raw_call(f, 64, A, A, None, 1, 256, None) == 1          # null sx
+    assert lib.raw_call(f, 48, A, A, A, 1, 256, None) == 3             # group not served
+    assert lib.raw_call(f, 64, A, A, A, 0, 256, None) == 2             # m = 0
+    assert lib.raw_call(f, 64, A, A, A, 65537, 256, None) == 2         # m too big
+    assert lib.raw_call(f, 64, A, A, A, 1, 96, None) == 2              # k % group
+    assert lib.raw_call(f, 16, A, A, A, 1, 8, None) == 2               # k < 16
+    assert lib.raw_call(f, 64, A + 8, A, A, 1, 256, None) == 4         # x misaligned
+    assert lib.raw_call(f, 64, A, A + 8, A, 1, 256, None) == 4         # q misaligned
+    assert lib.raw_call(f, 64, A, A, A + 2, 1, 256, None) == 4         # sx misaligned
 
 
 def test_dequant_validation(lib):
