@@ -62,9 +62,9 @@ def kernel_source_hash(path: str) -> str:
 class Setup:
     """Packed weights (rotated device copies), activations and output for one workload."""
 
-    def __init__(self, uq, wl: workloads.Workload, m: int, rotate: int | None):
+    def __init__(self, uq, wl: workloads.Workload, m: int, rotate: int | None, a8: bool = False):
         import torch
-        self.uq, self.wl, self.m = uq, wl, m
+        self.uq, self.wl, self.m, self.a8 = uq, wl, m, a8
         w, x = workloads.make_workload(wl)
         self.w_host, self.x_host = w, x[:m]
         self.lay = uq.layout(wl.scheme, wl.group, wl.n, wl.k)
@@ -79,7 +79,7 @@ class Setup:
         self.params = [dp] + [dp.clone() for _ in range(rotate - 1)]
         self.x = torch.from_numpy(np.ascontiguousarray(self.x_host)).cuda()
         self.y = torch.empty(m * wl.n, dtype=torch.float32, device="cuda")
-        self.fn = uq.uq_gemv if wl.path == "gemv" else uq.uq_gemm
+        self.fn = uq.uq_gemv_a8 if a8 else (uq.uq_gemv if wl.path == "gemv" else uq.uq_gemm)
         torch.cuda.synchronize()
 
     def launch(self, i: int, stream: int) -> None:
@@ -138,7 +138,12 @@ class Setup:
         idx = np.sort(np.random.default_rng(seed).choice(self.wl.n, min(rows, self.wl.n), replace=False))
         codes, params = o.quantize_pack(self.w_host[idx], self.wl.scheme, self.wl.group)
         wdq = o.dequant_packed(codes, params, self.wl.scheme, self.wl.group, self.wl.k)
-        if self.wl.path == "gemv":
+        if self.a8:
+            q_w, s16, z16 = o.quantize_int(self.w_host[idx], o.BITS[self.wl.scheme], self.wl.group)
+            q_x, s_x = o.quantize_activations(self.x_host, self.wl.group)
+            ref = o.gemv_a8_ref(q_x, s_x, q_w, s16, z16, self.wl.group)
+            xs, ws = o.dequant_activations(q_x, s_x, self.wl.group), wdq
+        elif self.wl.path == "gemv":
             ref, xs, ws = o.gemv_ref(self.x_host, wdq), self.x_host, wdq
         else:
             ref = o.gemm_ref(self.x_host, wdq)
@@ -333,6 +338,16 @@ def report_all(uq, steps: int, warmup: int, path: str | None) -> None:
                         f"{gbs:.0f} | {100 * gbs / HBM_PEAK_GBS:.1f} | {tfl:.2f} | {mfma} |")
             log(rows[-1])
             del st
+            if wl.path == "gemv" and wl.scheme != "nf4":
+                st = Setup(uq, wl, m, None, a8=True)
+                ms, _ = st.time(steps, warmup)
+                st.check_sample()
+                gbs = st.bytes / (ms * 1e-3) / 1e9
+                tfl = 2.0 * m * wl.k * wl.n / (ms * 1e-3) / 1e12
+                rows.append(f"| {name} | gemv_a8 | {m} | {st.bytes / 1e6:.2f} | {ms * 1e3:.2f} | "
+                            f"{gbs:.0f} | {100 * gbs / HBM_PEAK_GBS:.1f} | {tfl:.2f} | - |")
+                log(rows[-1])
+                del st
     rows += ["", "| fused RMSNorm + RoPE | tokens | heads | head_dim | MB moved | us/launch | GB/s | % HBM |",
              "|---|---|---|---|---|---|---|---|"]
     for name, wl in workloads.NORM_ROPE.items():
@@ -382,6 +397,8 @@ def main() -> None:
     ap.add_argument("--workload", default=workloads.HEADLINE,
                     choices=list(workloads.WORKLOADS) + list(workloads.NORM_ROPE))
     ap.add_argument("--m", type=int, default=None)
+    ap.add_argument("--a8", action="store_true",
+                    help="time the activation-quantized GEMV (uq_gemv_a8) on an INT GEMV workload instead")
     ap.add_argument("--rotate", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--all", action="store_true", help="also time every workload (markdown)")
@@ -412,7 +429,9 @@ def main() -> None:
     if args.traffic_run:
         traffic_run(uq, wl, m, args.traffic_run)
         return
-    st = Setup(uq, wl, m, args.rotate)
+    if args.a8 and (wl.path != "gemv" or wl.scheme == "nf4"):
+        raise SystemExit("--a8 applies to the INT GEMV workloads")
+    st = Setup(uq, wl, m, args.rotate, a8=args.a8)
     torch.cuda.synchronize()
     ms, eager_ms = st.time(args.steps, args.warmup)
     rel = st.check_sample()
@@ -421,7 +440,8 @@ def main() -> None:
         f"{gbs:.1f} GB/s, rotate={st.rotate}, sampled rel-L2 {rel:.2e}")
 
     out = {
-        "metric": METRIC,
+        "metric": METRIC if not args.a8 else
+        "activation-quantized (int8 per group) GEMV weight GB/s & % HBM peak (not the headline metric)",
         "value": round(gbs, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -431,9 +451,10 @@ def main() -> None:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16" if wl.path == "gemv" else "bf16",
+        "dtype": "i8" if args.a8 else ("f16" if wl.path == "gemv" else "bf16"),
         "data": "synthetic",
-        "config": {"workload": f"{wl.name} {wl.path} m={m}", "scheme": wl.scheme, "group": wl.group,
+        "config": {"workload": f"{wl.name} {'gemv_a8' if args.a8 else wl.path} m={m}", "scheme": wl.scheme,
+                   "group": wl.group,
                    "m": m, "k": wl.k, "n": wl.n, "weight_bytes": st.bytes, "rotated_copies": st.rotate,
                    "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
                    "tflops": round(2.0 * m * wl.k * wl.n / (ms * 1e-3) / 1e12, 3),
@@ -441,13 +462,13 @@ def main() -> None:
     }
     if wl.path == "gemv":
         out["roofline"] = {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                           "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic_for(wl, m)}
+                           "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None if args.a8 else traffic_for(wl, m)}
     else:
         tfl = 2.0 * m * wl.k * wl.n / (ms * 1e-3) / 1e12
         out["roofline"] = {"bound": "mfma", "achieved": round(tfl, 3), "peak": BF16_PEAK_TFLOPS,
                            "unit": "TFLOP/s", "frac": round(tfl / BF16_PEAK_TFLOPS, 4),
                            "traffic": traffic_for(wl, m)}
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.a8:
         log("timing the oracle on the host (cpu_baseline) ...")
         out["cpu_baseline"] = cpu_baseline(wl, m, st.bytes)
     del st

@@ -58,10 +58,8 @@ __device__ __forceinline__ void quantize16(const float (&v)[16], float a, int (&
   }
 }
 
-// Load one unit's 16 fp16 values (16-byte aligned) as fp32 and their max |x|.
-__device__ __forceinline__ float load16(const uint16_t* p, float (&v)[16]) {
-  const uint4 a = reinterpret_cast<const uint4*>(p)[0];
-  const uint4 b = reinterpret_cast<const uint4*>(p)[1];
+// One unit's 16 fp16 values (two 16-byte loads) as fp32, and their max |x|.
+__device__ __forceinline__ float unpack16(const uint4& a, const uint4& b, float (&v)[16]) {
   const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
   float mx = 0.0f;
 #pragma unroll
@@ -71,6 +69,10 @@ __device__ __forceinline__ float load16(const uint16_t* p, float (&v)[16]) {
     mx = fmaxf(mx, fmaxf(fabsf(v[2 * i]), fabsf(v[2 * i + 1])));
   }
   return mx;
+}
+
+__device__ __forceinline__ float load16(const uint16_t* p, float (&v)[16]) {
+  return unpack16(reinterpret_cast<const uint4*>(p)[0], reinterpret_cast<const uint4*>(p)[1], v);
 }
 
 // Max over the G/16 consecutive lanes that hold one group's units.
@@ -120,22 +122,49 @@ __global__ __launch_bounds__(kA8Threads) void gemv_a8_kernel(const uint8_t* __re
 #pragma unroll
     for (int mm = 0; mm < MT; ++mm) acc_y[r][mm] = 0.0f;
 
+  // Loads of one batch of kA8Chunks chunks per lane and row (and their group
+  // parameters); chunks past the block re-read a valid one and are skipped.
+  uint4 cw[kA8Chunks][kA8Rows];
+  uint32_t pw[kA8Chunks][kA8Rows][NFU];
+  auto load_batch = [&](const uint8_t* cblk, int kb0, int cb, int nch) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < kA8Chunks; ++j) {
+      const int c0 = cb + j * 64 + lane;
+      const int c = c0 < nch ? c0 : nch - 1;
+#pragma unroll
+      for (int r = 0; r < kA8Rows; ++r) {
+        cw[j][r] = reinterpret_cast<const uint4*>(cblk + size_t(rr[r]) * rowb)[c];
+#pragma unroll
+        for (int f = 0; f < NFU; ++f) {
+          const int g = (kb0 + c * CPC + f * FU) / G;
+          pw[j][r][f] = reinterpret_cast<const uint32_t*>(params + size_t(rr[r]) * size_t(ng) * 4)[g];
+        }
+      }
+    }
+  };
+
   for (int kb0 = 0; kb0 < k; kb0 += kb_max) {
     const int kb = k - kb0 < kb_max ? k - kb0 : kb_max;
     const int upr = kb / 16;  // units per activation row in this block
+    const int nch = kb / CPC;  // chunks per row in the block (kb is a multiple of CPC)
+    const uint8_t* cblk = codes + size_t(kb0) * Fmt<S>::bits / 8;
     __syncthreads();          // the previous block's codes are no longer read
     // Stage: quantize each activation row of the block (rows past m: zeros).
+    // The first unit's activations are loaded before the first batch of
+    // weight loads, which then stay in flight while the units are quantized
+    // (loads complete in order: using the activations waits for them only).
     for (int u0 = 0; u0 < MT * upr; u0 += kA8Threads) {
       const int u = u0 + tid;
       const bool valid = u < MT * upr;
       const int mm = valid ? u / upr : 0, ul = valid ? u % upr : 0;
+      // Raw loads first (rows past m read row 0 and are zeroed below), then the
+      // first weight batch, then the conversion that waits for the raw loads.
+      const bool live = valid && mm < m;
+      const uint4* xp = reinterpret_cast<const uint4*>(x + (live ? size_t(mm) * k + kb0 + ul * 16 : 0));
+      const uint4 xa = xp[0], xb = xp[1];
+      if (u0 == 0) load_batch(cblk, kb0, 0, nch);
       float v[16];
-      float a = 0.0f;
-      if (valid && mm < m) a = load16(x + size_t(mm) * k + kb0 + ul * 16, v);
-      else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) v[i] = 0.0f;
-      }
+      float a = unpack16(live ? xa : make_uint4(0u, 0u, 0u, 0u), live ? xb : make_uint4(0u, 0u, 0u, 0u), v);
       a = group_max<G>(a);  // every lane takes part (G/16 divides 64 and upr)
       if (valid) {
         int q[16];
@@ -156,25 +185,8 @@ __global__ __launch_bounds__(kA8Threads) void gemv_a8_kernel(const uint8_t* __re
     __syncthreads();
 
     // Stream the rows' codes of this block in batches of kA8Chunks chunks per lane.
-    const int nch = kb / CPC;  // chunks per row in the block (kb is a multiple of CPC)
-    const uint8_t* cblk = codes + size_t(kb0) * Fmt<S>::bits / 8;
     for (int cb = 0; cb < nch; cb += 64 * kA8Chunks) {
-      uint4 cw[kA8Chunks][kA8Rows];
-      uint32_t pw[kA8Chunks][kA8Rows][NFU];
-#pragma unroll
-      for (int j = 0; j < kA8Chunks; ++j) {
-        const int c0 = cb + j * 64 + lane;
-        const int c = c0 < nch ? c0 : nch - 1;  // past the block: any valid chunk (not accumulated)
-#pragma unroll
-        for (int r = 0; r < kA8Rows; ++r) {
-          cw[j][r] = reinterpret_cast<const uint4*>(cblk + size_t(rr[r]) * rowb)[c];
-#pragma unroll
-          for (int f = 0; f < NFU; ++f) {
-            const int g = (kb0 + c * CPC + f * FU) / G;
-            pw[j][r][f] = reinterpret_cast<const uint32_t*>(params + size_t(rr[r]) * size_t(ng) * 4)[g];
-          }
-        }
-      }
+      if (cb > 0) load_batch(cblk, kb0, cb, nch);
 #pragma unroll
       for (int j = 0; j < kA8Chunks; ++j) {
         const int c = cb + j * 64 + lane;
