@@ -28,13 +28,14 @@ constexpr int kA8Threads = 256;
 constexpr int kA8Waves = kA8Threads / 64;
 constexpr int kA8Rows = 4;          // weight rows per wave
 constexpr int kA8Block = 32768;     // activation codes staged per LDS block (all rows of x together)
-constexpr int kA8Chunks = 2;        // 16-byte code chunks per lane per row in flight
 
 template <int S>
 struct A8 {
   static constexpr int bits = Fmt<S>::bits;
   static constexpr int CPC = 128 / bits;      // codes per 16-byte chunk: 16, 32, 64
   static constexpr int CPD = 32 / bits;       // codes per dword: 4, 8, 16
+  // 16-byte chunks per lane and row in flight: a whole row of K = 4096 per wave.
+  static constexpr int CHUNKS = bits / 2;
 };
 
 // Position of code i (0..15) of a 16-code unit in the LDS order of the
@@ -101,6 +102,7 @@ __global__ __launch_bounds__(kA8Threads) void gemv_a8_kernel(const uint8_t* __re
   constexpr int NFU = CPC / FU;                  // portions per chunk
   constexpr int DPF = FU / CPD;                  // dwords per portion
   constexpr int UPF = FU / 16;                   // 16-code units per portion
+  constexpr int kA8Chunks = F::CHUNKS;
 
   extern __shared__ uint4 a8_lds[];
   int8_t* qx = reinterpret_cast<int8_t*>(a8_lds);                      // [MT][kb_max]
