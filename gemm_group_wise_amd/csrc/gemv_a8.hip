@@ -9,9 +9,10 @@
 // where D and Q are exact integer sums (v_dot4 on int8 lanes, 4 products per
 // instruction) and only the per-group scaling is floating point (fp32).
 //
-//   * A workgroup is 4 waves; each wave owns 4 weight rows, so the staged
-//     activations serve 16 rows.  Per K block the workgroup quantizes every
-//     activation row into LDS once: int8 codes laid out in the order the
+//   * A workgroup is 4 waves; each wave owns 4 weight rows (2 when x has
+//     five to eight rows), so the staged activations serve 16 (8) weight
+//     rows.  Per K block the workgroup quantizes every activation row into
+//     LDS once: int8 codes laid out in the order the
 //     unpacked weight lanes take them (INT4: even codes then odd codes of each
 //     8; INT2: crumb j of each byte), the code sum of every 16, and s_x.
 //   * Lanes then stream 16-byte chunks of their rows' codes (coalesced along
@@ -26,7 +27,11 @@ namespace {
 
 constexpr int kA8Threads = 256;
 constexpr int kA8Waves = kA8Threads / 64;
-constexpr int kA8Rows = 4;          // weight rows per wave
+// Weight rows per wave: four, or two for eight activation rows (their
+// accumulators and activation codes would otherwise leave room for only one
+// wave per SIMD).
+template <int MT>
+constexpr int a8_rows() { return MT >= 8 ? 2 : 4; }
 constexpr int kA8Block = 32768;     // activation codes staged per LDS block (all rows of x together)
 
 template <int S>
@@ -103,6 +108,7 @@ __global__ __launch_bounds__(kA8Threads) void gemv_a8_kernel(const uint8_t* __re
   constexpr int DPF = FU / CPD;                  // dwords per portion
   constexpr int UPF = FU / 16;                   // 16-code units per portion
   constexpr int kA8Chunks = F::CHUNKS;
+  constexpr int kA8Rows = a8_rows<MT>();
 
   extern __shared__ uint4 a8_lds[];
   int8_t* qx = reinterpret_cast<int8_t*>(a8_lds);                      // [MT][kb_max]
@@ -297,7 +303,8 @@ hipError_t launch_a8(const uq_layout* L, const void* codes, const void* params, 
   int kb_max = kA8Block / MT;
   if (kb_max > k) kb_max = k;
   const size_t shmem = size_t(MT) * kb_max + size_t(MT) * (kb_max / 16) * 4 + size_t(MT) * (kb_max / G) * 4;
-  const int64_t blocks = (int64_t(n) + kA8Waves * kA8Rows - 1) / (kA8Waves * kA8Rows);
+  constexpr int R = a8_rows<MT>();
+  const int64_t blocks = (int64_t(n) + kA8Waves * R - 1) / (kA8Waves * R);
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   const uint8_t* c8 = static_cast<const uint8_t*>(codes);
   const uint8_t* p8 = static_cast<const uint8_t*>(params);
