@@ -61,7 +61,7 @@ BITS = {"int2": 2, "int4": 4, "int8": 8, "nf4": 4}
 QMAX = {2: 3, 4: 15, 8: 255}
 # Group sizes the path supports (reading: the page names no group size).
 GROUPS = {"int2": (16, 32, 64, 128), "int4": (32, 64, 128),
-          "int8": (64, 128), "nf4": (64,)}
+          "int8": (32, 64, 128), "nf4": (64,)}
 
 NF4_PSTAR = 0.9677083
 

@@ -478,3 +478,138 @@ def check_a8_bruteforce(o, seed=7):
                 wv = int(q_w[j, t]) * float(s16[j, g]) + float(z16[j, g])
                 acc += xv * wv
             assert abs(acc - y[i, j]) <= 1e-12 * max(1.0, abs(acc))
+
+
+# ---------------------------------------------------------------------------
+# GGUF Q4_0 / Q8_0 blocks (readings R-GG, R-GI)
+# ---------------------------------------------------------------------------
+_GGUF_TYPES = {"q4_0": 2, "q8_0": 8}
+
+
+def load_gguf_cases():
+    """Parse tests/golden/gguf_blocks_handbuilt.txt into a list of case dicts."""
+    cases, cur = [], None
+    with open(os.path.join(GOLDEN, "gguf_blocks_handbuilt.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            if line.startswith("case "):
+                _, name, fmt, n, k = line.split()
+                cur = dict(name=name, gtype=_GGUF_TYPES[fmt], n=int(n[2:]), k=int(k[2:]),
+                           blocks={}, values={})
+                cases.append(cur)
+                continue
+            key, val = line.split(":", 1)
+            m = re.fullmatch(r"(blocks|values)(\d+)", key)
+            kind, row = m.group(1), int(m.group(2))
+            if kind == "blocks":
+                cur["blocks"][row] = bytes(int(b, 16) for b in val.split())
+            else:
+                vals = []
+                for tok in val.split():
+                    rep = re.fullmatch(r"(.+)\{(\d+)\}", tok)
+                    v, c = (rep.group(1), int(rep.group(2))) if rep else (tok, 1)
+                    vals += [Fraction(v)] * c
+                cur["values"][row] = vals
+    return cases
+
+
+def _gguf_blob(case):
+    return np.frombuffer(b"".join(case["blocks"][r] for r in range(case["n"])), dtype=np.uint8)
+
+
+def check_gguf_golden(o):
+    """Decode each hand-built block row; every value must equal the fixture.
+
+    Source: the Q4_0 / Q8_0 formats the Ultra LLM Engine page names (Roadmap
+    Ideas), laid out as the public GGUF definition (R-GG); the expected values
+    are derived by hand in the fixture file."""
+    for case in load_gguf_cases():
+        w = o.decode_gguf(_gguf_blob(case), case["gtype"], case["n"], case["k"])
+        assert w.shape == (case["n"], case["k"]), case["name"]
+        for r in range(case["n"]):
+            want = [float(v) for v in case["values"][r]]
+            assert len(want) == case["k"], case["name"]
+            assert w[r].tolist() == want, (case["name"], r)
+
+
+def check_gguf_placement(o):
+    """Brute force over positions: one marked value per block lands where the
+    format puts it, and blocks and rows land in order (distinct d per block)."""
+    one = np.float16(1.0).view(np.uint16)
+    for p in range(32):
+        b = np.zeros(18, dtype=np.uint8)
+        b[0], b[1] = one & 0xFF, one >> 8
+        b[2:] = 0x88                                            # every nibble 8 -> 0
+        j = p % 16
+        b[2 + j] = 0x89 if p < 16 else 0x98                     # this value -> 1
+        w = o.decode_gguf(b, 2, 1, 32)[0]
+        assert w[p] == 1.0 and np.count_nonzero(w) == 1, ("q4_0", p)
+        b8 = np.zeros(34, dtype=np.uint8)
+        b8[0], b8[1] = one & 0xFF, one >> 8
+        b8[2 + p] = 1
+        w8 = o.decode_gguf(b8, 8, 1, 32)[0]
+        assert w8[p] == 1.0 and np.count_nonzero(w8) == 1, ("q8_0", p)
+    n, nb = 3, 4
+    for gtype, size, fill in ((2, 18, 0x99), (8, 34, 0x01)):   # every value 1 * d
+        blob = np.full((n, nb, size), fill, dtype=np.uint8)
+        ds = np.arange(1, n * nb + 1, dtype=np.float16).reshape(n, nb)
+        bits = ds.view(np.uint16)
+        blob[..., 0], blob[..., 1] = bits & 0xFF, bits >> 8
+        w = o.decode_gguf(blob.reshape(-1), gtype, n, nb * 32)
+        want = np.repeat(ds.astype(np.float64), 32, axis=1)
+        assert np.array_equal(w, want), gtype
+
+
+def check_gguf_q8_identity(o, seed=8):
+    """Q8_0 with d = 1 gives the signed bytes; d = 2^e scales them exactly."""
+    rng = np.random.default_rng(seed)
+    n, k = 4, 256
+    q = rng.integers(-128, 128, size=(n, k // 32, 32)).astype(np.int8)
+    for e in (0, -7, 5):
+        d = np.float16(2.0 ** e).view(np.uint16)
+        blob = np.zeros((n, k // 32, 34), dtype=np.uint8)
+        blob[..., 0], blob[..., 1] = d & 0xFF, d >> 8
+        blob[..., 2:] = q.view(np.uint8)
+        w = o.decode_gguf(blob.reshape(-1), 8, n, k)
+        assert np.array_equal(w, q.reshape(n, k).astype(np.float64) * 2.0 ** e), e
+
+
+def random_gguf(gtype, n, k, seed, dmax=0.05):
+    """Random blocks: uniform bytes, fp16 d of random sign and magnitude."""
+    rng = np.random.default_rng(seed)
+    size = 18 if gtype == 2 else 34
+    blob = rng.integers(0, 256, size=(n, k // 32, size)).astype(np.uint8)
+    d = (rng.standard_normal((n, k // 32)) * dmax).astype(np.float16).view(np.uint16)
+    blob[..., 0], blob[..., 1] = d & 0xFF, d >> 8
+    return blob.reshape(-1)
+
+
+def check_gguf_int_form(o, seed=9):
+    """The INT form (R-GI) dequantizes to the decoded blocks, value for value,
+    and refuses scales whose zero point leaves fp16 or that are not finite."""
+    for gtype in (2, 8):
+        n, k = 5, 320
+        blob = random_gguf(gtype, n, k, seed + gtype)
+        q, s16, z16 = o.gguf_as_int(blob, gtype, n, k)
+        assert q.dtype == np.uint8 and s16.shape == (n, k // 32) and z16.shape == (n, k // 32)
+        wd = o.dequant_int(q, s16, z16, 32)
+        assert np.array_equal(wd.astype(np.float64), o.decode_gguf(blob, gtype, n, k)), gtype
+    # largest scales that still fit, and the first that do not
+    for gtype, ok, bad in ((2, 8188.0, 8192.0), (8, 511.75, 512.0)):
+        size = 18 if gtype == 2 else 34
+        for d, fits in ((ok, True), (bad, False), (np.inf, False), (np.nan, False)):
+            b = np.full(size, 0x5A, dtype=np.uint8)
+            bits = np.float16(d).view(np.uint16)
+            b[0], b[1] = bits & 0xFF, bits >> 8
+            if fits:
+                q, s16, z16 = o.gguf_as_int(b, gtype, 1, 32)
+                assert np.array_equal(o.dequant_int(q, s16, z16, 32).astype(np.float64),
+                                      o.decode_gguf(b, gtype, 1, 32)), (gtype, d)
+            else:
+                try:
+                    o.gguf_as_int(b, gtype, 1, 32)
+                except ValueError:
+                    continue
+                raise AssertionError(f"scale {d} accepted for type {gtype}")

@@ -7,7 +7,7 @@ import workloads
 from tests import pins
 
 INT_CASES = [(2, g) for g in (16, 32, 64, 128)] + [(4, g) for g in (32, 64, 128)] + \
-            [(8, g) for g in (64, 128)]
+            [(8, g) for g in (32, 64, 128)]
 
 
 def test_fp16_primitive_rounds_to_nearest_even():
@@ -161,3 +161,28 @@ def test_a8_products():
 
 def test_a8_bruteforce():
     pins.check_a8_bruteforce(o)
+
+
+def test_gguf_golden():
+    pins.check_gguf_golden(o)
+
+
+def test_gguf_placement():
+    pins.check_gguf_placement(o)
+
+
+def test_gguf_q8_identity():
+    pins.check_gguf_q8_identity(o)
+
+
+def test_gguf_int_form():
+    pins.check_gguf_int_form(o)
+
+
+def test_gguf_rejects_bad_shapes():
+    with pytest.raises(ValueError):
+        o.decode_gguf(np.zeros(18, np.uint8), 3, 1, 32)      # not a Q4_0 / Q8_0 type
+    with pytest.raises(ValueError):
+        o.decode_gguf(np.zeros(18, np.uint8), 2, 1, 48)      # k not whole blocks
+    with pytest.raises(ValueError):
+        o.decode_gguf(np.zeros(17, np.uint8), 2, 1, 32)      # short blob

@@ -170,6 +170,54 @@ def a8_scale_by_next_group(q_x, s_x, q_w, s16, z16, group):
     return o.gemv_a8_ref(q_x, np.roll(s_x, 1, axis=1), q_w, s16, z16, group)
 
 
+
+def gguf_q4_consecutive_nibbles(blob, gtype, n, k):
+    # value 2j in the low nibble of byte j, 2j+1 in the high (the INT4 order)
+    if gtype != 2:
+        return o.decode_gguf(blob, gtype, n, k)
+    b = np.asarray(blob, np.uint8).reshape(n, k // 32, 18)
+    d = (b[..., 0].astype(np.uint16) | (b[..., 1].astype(np.uint16) << 8)).view(np.float16)
+    qs = b[..., 2:].astype(np.int64)
+    v = np.stack([qs & 15, qs >> 4], axis=-1).reshape(n, k // 32, 32) - 8
+    return (v * d.astype(np.float64)[..., None]).reshape(n, k)
+
+
+def gguf_q4_no_offset(blob, gtype, n, k):
+    w = o.decode_gguf(blob, gtype, n, k)
+    if gtype != 2:
+        return w
+    b = np.asarray(blob, np.uint8).reshape(n, k // 32, 18)
+    d = (b[..., 0].astype(np.uint16) | (b[..., 1].astype(np.uint16) << 8)).view(np.float16)
+    return w + np.repeat(8.0 * d.astype(np.float64), 32, axis=1)
+
+
+def gguf_q8_unsigned(blob, gtype, n, k):
+    if gtype != 8:
+        return o.decode_gguf(blob, gtype, n, k)
+    b = np.asarray(blob, np.uint8).reshape(n, k // 32, 34)
+    d = (b[..., 0].astype(np.uint16) | (b[..., 1].astype(np.uint16) << 8)).view(np.float16)
+    return (b[..., 2:].astype(np.float64) * d.astype(np.float64)[..., None]).reshape(n, k)
+
+
+def gguf_scale_big_endian(blob, gtype, n, k):
+    size = 18 if gtype == 2 else 34
+    b = np.asarray(blob, np.uint8).reshape(-1, size).copy()
+    b[:, [0, 1]] = b[:, [1, 0]]
+    return o.decode_gguf(b.reshape(-1), gtype, n, k)
+
+
+def gguf_as_int_zero_off_by_one(blob, gtype, n, k):
+    q, s16, z16 = o.gguf_as_int(blob, gtype, n, k)
+    return q, s16, (z16.astype(np.float64) + s16.astype(np.float64)).astype(np.float16)
+
+
+def gguf_as_int_no_bias(blob, gtype, n, k):
+    # Q8_0 bytes taken as unsigned codes with the -128 d zero point kept
+    q, s16, z16 = o.gguf_as_int(blob, gtype, n, k)
+    if gtype == 8:
+        q = (q.astype(np.int64) - 128).astype(np.uint8)
+    return q, s16, z16
+
 CASES = [
     ("dequant drops the zero term", dict(dequant_int=dequant_drop_zero),
      lambda ns: pins.check_grid_recovery(ns, 4, 64)),
@@ -216,6 +264,18 @@ CASES = [
      lambda ns: pins.check_a8_products(ns)),
     ("A8 scales one group off", dict(gemv_a8_ref=a8_scale_by_next_group),
      lambda ns: pins.check_a8_bruteforce(ns)),
+    ("GGUF Q4_0 nibbles in INT4 order", dict(decode_gguf=gguf_q4_consecutive_nibbles),
+     lambda ns: pins.check_gguf_placement(ns)),
+    ("GGUF Q4_0 without the -8", dict(decode_gguf=gguf_q4_no_offset),
+     lambda ns: pins.check_gguf_golden(ns)),
+    ("GGUF Q8_0 bytes unsigned", dict(decode_gguf=gguf_q8_unsigned),
+     lambda ns: pins.check_gguf_golden(ns)),
+    ("GGUF scale big-endian", dict(decode_gguf=gguf_scale_big_endian),
+     lambda ns: pins.check_gguf_golden(ns)),
+    ("GGUF INT form zero point one step off", dict(gguf_as_int=gguf_as_int_zero_off_by_one),
+     lambda ns: pins.check_gguf_int_form(ns)),
+    ("GGUF INT form Q8_0 codes not biased", dict(gguf_as_int=gguf_as_int_no_bias),
+     lambda ns: pins.check_gguf_int_form(ns)),
 ]
 
 
