@@ -65,10 +65,15 @@ class Setup:
     def __init__(self, uq, wl: workloads.Workload, m: int, rotate: int | None, a8: bool = False):
         import torch
         self.uq, self.wl, self.m, self.a8 = uq, wl, m, a8
-        w, x = workloads.make_workload(wl)
-        self.w_host, self.x_host = w, x[:m]
-        self.lay = uq.layout(wl.scheme, wl.group, wl.n, wl.k)
-        codes, params = uq.uq_pack_weights(self.lay, w)
+        if wl.gguf:   # GGUF blocks, re-laid on the host into the INT layout
+            blob, x = workloads.make_gguf_workload(wl)
+            self.w_host, self.x_host = blob.reshape(wl.n, -1), x[:m]
+            self.lay, codes, params = uq.uq_import_gguf(wl.gguf, blob, wl.n, wl.k)
+        else:
+            w, x = workloads.make_workload(wl)
+            self.w_host, self.x_host = w, x[:m]
+            self.lay = uq.layout(wl.scheme, wl.group, wl.n, wl.k)
+            codes, params = uq.uq_pack_weights(self.lay, w)
         self.codes_host, self.params_host = codes, params
         self.bytes = codes.nbytes + params.nbytes
         if rotate is None:  # > 256 MB Infinity Cache + 32 MB L2
@@ -136,10 +141,17 @@ class Setup:
         import oracle as o
         torch_y = self.y.cpu().numpy().reshape(self.m, self.wl.n)
         idx = np.sort(np.random.default_rng(seed).choice(self.wl.n, min(rows, self.wl.n), replace=False))
-        codes, params = o.quantize_pack(self.w_host[idx], self.wl.scheme, self.wl.group)
-        wdq = o.dequant_packed(codes, params, self.wl.scheme, self.wl.group, self.wl.k)
+        if self.wl.gguf:
+            blob = self.w_host[idx].reshape(-1)
+            wdq = o.decode_gguf(blob, self.wl.gguf, idx.size, self.wl.k).astype(np.float32)
+        else:
+            codes, params = o.quantize_pack(self.w_host[idx], self.wl.scheme, self.wl.group)
+            wdq = o.dequant_packed(codes, params, self.wl.scheme, self.wl.group, self.wl.k)
         if self.a8:
-            q_w, s16, z16 = o.quantize_int(self.w_host[idx], o.BITS[self.wl.scheme], self.wl.group)
+            if self.wl.gguf:
+                q_w, s16, z16 = o.gguf_as_int(blob, self.wl.gguf, idx.size, self.wl.k)
+            else:
+                q_w, s16, z16 = o.quantize_int(self.w_host[idx], o.BITS[self.wl.scheme], self.wl.group)
             q_x, s_x = o.quantize_activations(self.x_host, self.wl.group)
             ref = o.gemv_a8_ref(q_x, s_x, q_w, s16, z16, self.wl.group)
             xs, ws = o.dequant_activations(q_x, s_x, self.wl.group), wdq
@@ -160,14 +172,20 @@ class Setup:
 def cpu_baseline(wl: workloads.Workload, m: int, nbytes: int) -> dict:
     """The oracle (unpack + dequant + fp64 product) on the same matrix, on host cores."""
     import oracle as o
-    w, x = workloads.make_workload(wl)
-    codes, params = o.quantize_pack(w, wl.scheme, wl.group)   # offline for both sides
-    xs = x[:m]
     ref = o.gemv_ref if wl.path == "gemv" else o.gemm_ref
+    if wl.gguf:
+        blob, x = workloads.make_gguf_workload(wl)
+        xs = x[:m]
 
-    def run():
-        wdq = o.dequant_packed(codes, params, wl.scheme, wl.group, wl.k)
-        return ref(xs, wdq)
+        def run():
+            return ref(xs, o.decode_gguf(blob, wl.gguf, wl.n, wl.k))
+    else:
+        w, x = workloads.make_workload(wl)
+        codes, params = o.quantize_pack(w, wl.scheme, wl.group)   # offline for both sides
+        xs = x[:m]
+
+        def run():
+            return ref(xs, o.dequant_packed(codes, params, wl.scheme, wl.group, wl.k))
 
     run()
     times = []

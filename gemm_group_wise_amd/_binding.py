@@ -18,6 +18,8 @@ LIB_PATH = os.path.join(_HERE, "libuq.so")
 
 SCHEMES = {"int2": 1, "int4": 2, "int8": 3, "nf4": 4}
 BITS = {"int2": 2, "int4": 4, "int8": 8, "nf4": 4}
+GGUF_TYPES = {"q4_0": 2, "q8_0": 8}
+GGUF_BLOCK_BYTES = {2: 18, 8: 34}
 GEMV_MAX_M = 8
 GEMM_MAX_M = 65536
 
@@ -59,6 +61,7 @@ _P = ctypes.c_void_p
 _L = ctypes.POINTER(Layout)
 _lib.uq_packed_size.argtypes = [_L, ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]
 _lib.uq_pack_weights.argtypes = [_L, _P, _P, _P]
+_lib.uq_import_gguf.argtypes = [ctypes.c_int32, _P, ctypes.c_int64, ctypes.c_int64, _L, _P, _P]
 _lib.uq_gemv.argtypes = [_L, _P, _P, _P, _P, ctypes.c_int64, _P]
 _lib.uq_gemm.argtypes = [_L, _P, _P, _P, _P, ctypes.c_int64, _P]
 _lib.uq_dequant.argtypes = [_L, _P, _P, _P, _P]
@@ -70,11 +73,11 @@ _lib.uq_rmsnorm_rope.argtypes = [_P, _P, _P, _P, _P, _P, ctypes.c_int64, ctypes.
                                  ctypes.c_int64, ctypes.c_float, _P]
 _lib.uq_status_str.argtypes = [ctypes.c_int]
 _lib.uq_status_str.restype = ctypes.c_char_p
-for _fn in ("uq_packed_size", "uq_pack_weights", "uq_gemv", "uq_gemm", "uq_dequant",
+for _fn in ("uq_packed_size", "uq_pack_weights", "uq_import_gguf", "uq_gemv", "uq_gemm", "uq_dequant",
             "uq_nf4_codebook", "uq_rope_table", "uq_rmsnorm_rope", "uq_gemv_a8", "uq_quantize_activations"):
     getattr(_lib, _fn).restype = ctypes.c_int
 
-EXPORTS = ("uq_packed_size", "uq_pack_weights", "uq_gemv", "uq_gemm", "uq_dequant",
+EXPORTS = ("uq_packed_size", "uq_pack_weights", "uq_import_gguf", "uq_gemv", "uq_gemm", "uq_dequant",
            "uq_nf4_codebook", "uq_rope_table", "uq_rmsnorm_rope", "uq_gemv_a8", "uq_quantize_activations",
            "uq_status_str")
 
@@ -125,6 +128,24 @@ def uq_pack_weights(lay: Layout, w: np.ndarray) -> tuple[np.ndarray, np.ndarray]
     _check("uq_pack_weights", _lib.uq_pack_weights(ctypes.byref(lay), w.ctypes.data,
                                                   codes.ctypes.data, params.ctypes.data))
     return codes, params.reshape(lay.n, -1)
+
+
+def uq_import_gguf(gguf_type: str | int, blocks: np.ndarray, n: int, k: int):
+    """Re-lay host GGUF Q4_0 / Q8_0 blocks of an [n, k] matrix; returns
+    (layout, codes uint8 [n, -1], params uint16 [n, k / 32, 2])."""
+    t = GGUF_TYPES[gguf_type] if isinstance(gguf_type, str) else int(gguf_type)
+    blocks = np.ascontiguousarray(blocks, dtype=np.uint8).reshape(-1)
+    shaped = t in GGUF_BLOCK_BYTES and n >= 1 and k >= 32 and k % 32 == 0
+    if shaped and blocks.size != n * (k // 32) * GGUF_BLOCK_BYTES[t]:
+        # the library cannot see the buffer's length: never let it read past it
+        raise ValueError(f"blocks hold {blocks.size} bytes, not {n * (k // 32) * GGUF_BLOCK_BYTES[t]}")
+    # buffers for a valid call; on a rejected shape the library writes nothing
+    codes = np.empty(n * k // (2 if t == 2 else 1) if shaped else 1, dtype=np.uint8)
+    params = np.empty(n * (k // 32) * 2 if shaped else 1, dtype=np.uint16)
+    lay = Layout()
+    _check("uq_import_gguf", _lib.uq_import_gguf(t, blocks.ctypes.data, int(n), int(k), ctypes.byref(lay),
+                                                codes.ctypes.data, params.ctypes.data))
+    return lay, codes.reshape(lay.n, -1), params.reshape(lay.n, -1, 2)
 
 
 def uq_gemv(lay: Layout, codes, params, x, y, m: int, stream=None) -> None:

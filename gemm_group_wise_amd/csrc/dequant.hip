@@ -68,6 +68,7 @@ hipError_t launch_dequant(const uq_layout* L, const void* codes, const void* par
     case UQ_INT4 * 1000 + 32: return launch<UQ_INT4, 32>(L, codes, params, w, stream);
     case UQ_INT4 * 1000 + 64: return launch<UQ_INT4, 64>(L, codes, params, w, stream);
     case UQ_INT4 * 1000 + 128: return launch<UQ_INT4, 128>(L, codes, params, w, stream);
+    case UQ_INT8 * 1000 + 32: return launch<UQ_INT8, 32>(L, codes, params, w, stream);
     case UQ_INT8 * 1000 + 64: return launch<UQ_INT8, 64>(L, codes, params, w, stream);
     case UQ_INT8 * 1000 + 128: return launch<UQ_INT8, 128>(L, codes, params, w, stream);
     case UQ_NF4 * 1000 + 64: return launch<UQ_NF4, 64>(L, codes, params, w, stream);

@@ -661,6 +661,7 @@ hipError_t launch_gemm(const uq_layout* L, const void* codes, const void* params
     case UQ_INT4 * 1000 + 32: return launch_tiles<UQ_INT4, 32>(L, codes, params, xb, y, m, stream);
     case UQ_INT4 * 1000 + 64: return launch_tiles<UQ_INT4, 64>(L, codes, params, xb, y, m, stream);
     case UQ_INT4 * 1000 + 128: return launch_tiles<UQ_INT4, 128>(L, codes, params, xb, y, m, stream);
+    case UQ_INT8 * 1000 + 32: return launch_tiles<UQ_INT8, 32>(L, codes, params, xb, y, m, stream);
     case UQ_INT8 * 1000 + 64: return launch_tiles<UQ_INT8, 64>(L, codes, params, xb, y, m, stream);
     case UQ_INT8 * 1000 + 128: return launch_tiles<UQ_INT8, 128>(L, codes, params, xb, y, m, stream);
     case UQ_NF4 * 1000 + 64: return launch_tiles<UQ_NF4, 64>(L, codes, params, xb, y, m, stream);

@@ -345,6 +345,7 @@ hipError_t launch_gemv_a8(const uq_layout* L, const void* codes, const void* par
     case UQ_INT4 * 1000 + 32: return launch_a8_m<UQ_INT4, 32>(L, codes, params, x, y, m, stream);
     case UQ_INT4 * 1000 + 64: return launch_a8_m<UQ_INT4, 64>(L, codes, params, x, y, m, stream);
     case UQ_INT4 * 1000 + 128: return launch_a8_m<UQ_INT4, 128>(L, codes, params, x, y, m, stream);
+    case UQ_INT8 * 1000 + 32: return launch_a8_m<UQ_INT8, 32>(L, codes, params, x, y, m, stream);
     case UQ_INT8 * 1000 + 64: return launch_a8_m<UQ_INT8, 64>(L, codes, params, x, y, m, stream);
     case UQ_INT8 * 1000 + 128: return launch_a8_m<UQ_INT8, 128>(L, codes, params, x, y, m, stream);
     default: return hipErrorInvalidValue;

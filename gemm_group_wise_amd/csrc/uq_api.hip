@@ -56,6 +56,11 @@ uq_status uq_pack_weights(const uq_layout* layout, const float* w, uint8_t* code
   return uq::pack_weights(layout, w, codes, params);
 }
 
+uq_status uq_import_gguf(int32_t gguf_type, const void* blocks, int64_t n, int64_t k, uq_layout* layout,
+                         uint8_t* codes, uint16_t* params) {
+  return uq::import_gguf(gguf_type, blocks, n, k, layout, codes, params);
+}
+
 uq_status uq_gemv(const uq_layout* layout, const void* codes, const void* params,
                   const uint16_t* x, float* y, int64_t m, void* stream) {
   const uq_status st = uq::check_product(layout, codes, params, x, y, m, UQ_GEMV_MAX_M);

@@ -31,7 +31,7 @@ constexpr int scheme_bits(int scheme) {
 constexpr bool group_supported(int scheme, int g) {
   return scheme == UQ_INT2 ? (g == 16 || g == 32 || g == 64 || g == 128)
        : scheme == UQ_INT4 ? (g == 32 || g == 64 || g == 128)
-       : scheme == UQ_INT8 ? (g == 64 || g == 128)
+       : scheme == UQ_INT8 ? (g == 32 || g == 64 || g == 128)
        : scheme == UQ_NF4  ? (g == 64)
                            : false;
 }
@@ -65,6 +65,10 @@ inline size_t param_row_bytes(const uq_layout* L) {
 // Host packer (uq_pack.cpp).
 uq_status pack_weights(const uq_layout* L, const float* w, uint8_t* codes,
                        uint16_t* params);
+
+// Host re-layout of GGUF Q4_0 / Q8_0 blocks into the INT4 / INT8 G = 32 layout (uq_gguf.cpp).
+uq_status import_gguf(int32_t type, const void* blocks, int64_t n, int64_t k, uq_layout* L,
+                      uint8_t* codes, uint16_t* params);
 
 // Host rotary table (rope_table.cpp).
 uq_status rope_table(double theta, int32_t head_dim, int64_t max_pos, float* cos_out, float* sin_out);

@@ -68,7 +68,7 @@ typedef enum uq_status {
 typedef enum uq_scheme {
   UQ_INT2 = 1, /* groups 16, 32, 64, 128 */
   UQ_INT4 = 2, /* groups 32, 64, 128     */
-  UQ_INT8 = 3, /* groups 64, 128         */
+  UQ_INT8 = 3, /* groups 32, 64, 128     */
   UQ_NF4 = 4   /* group 64               */
 } uq_scheme;
 
@@ -161,6 +161,35 @@ uq_status uq_gemv_a8(const uq_layout* layout, const void* codes,
  * group in {16, 32, 64, 128}; 1 <= m <= 65536; 16 <= k <= 2^24. */
 uq_status uq_quantize_activations(int32_t group, const uint16_t* x, int8_t* q,
                                   float* sx, int64_t m, int64_t k, void* stream);
+
+/* ---- GGUF weight blocks (the "Ultra LLM Engine" page's Roadmap Ideas: Q4_0
+ * and Q8_0 dequantizers; its Checkpoint Loading section: formats the loader
+ * cannot decode are refused, not guessed).  The block layout is the public
+ * GGUF one; the pages do not print it. ---- */
+typedef enum uq_gguf_type {
+  UQ_GGUF_Q4_0 = 2, /* GGUF tensor type ids */
+  UQ_GGUF_Q8_0 = 8
+} uq_gguf_type;
+
+/* Re-lay GGUF Q4_0 / Q8_0 blocks of a weight matrix W[n][k] into this
+ * library's INT layout, host call, exact:
+ *   blocks : host, the tensor's data: n rows of k / 32 blocks, row-major;
+ *            Q4_0 block = fp16 d (little-endian) + 16 bytes (byte j: weight j
+ *            in the low nibble, weight j + 16 in the high), w = (nibble - 8) d;
+ *            Q8_0 block = fp16 d + 32 int8 q, w = q d
+ *   layout : written: Q4_0 -> {UQ_INT4, 32, n, k}, Q8_0 -> {UQ_INT8, 32, n, k}
+ *   codes, params : host, uq_packed_size(layout) bytes, written
+ * The result holds s = d and z = -8 d (Q4_0) or -128 d (Q8_0) per block and
+ * codes nibble (Q4_0) or q + 128 (Q8_0), so uq_dequant returns every weight
+ * exactly (as a number: a zero may change sign) and uq_gemv / uq_gemm /
+ * uq_gemv_a8 serve the weights as any INT layout.  Errors: UQ_ERR_UNSUPPORTED
+ * for another type; UQ_ERR_SHAPE unless n >= 1, k is a multiple of 32 and
+ * k <= 2^24; UQ_ERR_RANGE if a scale is NaN or infinite or its zero point
+ * exceeds fp16 (|d| >= 8192 for Q4_0, >= 512 for Q8_0).  All scales are
+ * checked before anything is written. */
+uq_status uq_import_gguf(int32_t gguf_type, const void* blocks, int64_t n,
+                         int64_t k, uq_layout* layout, uint8_t* codes,
+                         uint16_t* params);
 
 /* The 16 NF4 codebook entries (fp32) the library uses; host call. */
 uq_status uq_nf4_codebook(float out[16]);

@@ -6,6 +6,7 @@ import sys
 import numpy as np
 
 import oracle as o
+import workloads
 
 REL_L2_MAX = 1e-3
 ABS_COEF = 2e-3
@@ -56,6 +57,19 @@ def packed_on_device(lib, scheme, group, w):
     lay = lib.layout(scheme, group, w.shape[0], w.shape[1])
     codes, params = lib.uq_pack_weights(lay, w)
     return lay, dev(codes), dev(params)
+
+
+def workload_on_device(lib, wl):
+    """(layout, codes and params on the GPU, the oracle's w' fp32 [n, k], x) of a
+    workload: fp32 weights through the packer, or GGUF blocks through the import."""
+    if wl.gguf:
+        blob, x = workloads.make_gguf_workload(wl)
+        lay, codes, params = lib.uq_import_gguf(wl.gguf, blob, wl.n, wl.k)
+        wdq = o.decode_gguf(blob, wl.gguf, wl.n, wl.k).astype(np.float32)
+        return lay, dev(codes), dev(params), wdq, x
+    w, x = workloads.make_workload(wl)
+    lay, codes, params = packed_on_device(lib, wl.scheme, wl.group, w)
+    return lay, codes, params, oracle_dequant(w, wl.scheme, wl.group), x
 
 
 def oracle_dequant(w, scheme, group):

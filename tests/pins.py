@@ -13,6 +13,8 @@ from fractions import Fraction
 
 import numpy as np
 
+import workloads
+
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
 
@@ -577,13 +579,8 @@ def check_gguf_q8_identity(o, seed=8):
 
 
 def random_gguf(gtype, n, k, seed, dmax=0.05):
-    """Random blocks: uniform bytes, fp16 d of random sign and magnitude."""
-    rng = np.random.default_rng(seed)
-    size = 18 if gtype == 2 else 34
-    blob = rng.integers(0, 256, size=(n, k // 32, size)).astype(np.uint8)
-    d = (rng.standard_normal((n, k // 32)) * dmax).astype(np.float16).view(np.uint16)
-    blob[..., 0], blob[..., 1] = d & 0xFF, d >> 8
-    return blob.reshape(-1)
+    """Random blocks from the shared seeded generator (uniform bytes, fp16 d)."""
+    return workloads.make_gguf_blocks(gtype, n, k, seed=seed, dmax=dmax)
 
 
 def check_gguf_int_form(o, seed=9):

@@ -16,7 +16,7 @@ from tests import pins
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 ALL_LAYOUTS = [("int2", g) for g in (16, 32, 64, 128)] + [("int4", g) for g in (32, 64, 128)] + \
-              [("int8", g) for g in (64, 128)] + [("nf4", 64)]
+              [("int8", g) for g in (32, 64, 128)] + [("nf4", 64)]
 
 
 def header_functions():
@@ -102,6 +102,14 @@ def test_packer_matches_oracle_edge_values(lib, scheme, group):
 @pytest.mark.parametrize("name", list(workloads.WORKLOADS))
 def test_packer_matches_oracle_full_configs(lib, name):
     wl = workloads.WORKLOADS[name]
+    if wl.gguf:
+        blob, _ = workloads.make_gguf_workload(wl)
+        _, codes, params = lib.uq_import_gguf(wl.gguf, blob, wl.n, wl.k)
+        q, s16, z16 = o.gguf_as_int(blob, wl.gguf, wl.n, wl.k)
+        rc, rp = o.pack_codes(q, o.BITS[wl.scheme]), o.pack_params_int(s16, z16)
+        assert np.array_equal(codes, rc)
+        assert np.array_equal(params.reshape(-1), rp.reshape(-1))
+        return
     w, _ = workloads.make_workload(wl)
     codes, params = lib.uq_pack_weights(lib.layout(wl.scheme, wl.group, wl.n, wl.k), w)
     rc, rp = o.quantize_pack(w, wl.scheme, wl.group)
@@ -116,7 +124,7 @@ def test_layout_errors(lib):
     bad = [
         (lib.layout(9, 64, 4, 256), "UQ_ERR_UNSUPPORTED"),
         (lib.layout("int4", 16, 4, 256), "UQ_ERR_UNSUPPORTED"),
-        (lib.layout("int8", 32, 4, 256), "UQ_ERR_UNSUPPORTED"),
+        (lib.layout("int8", 16, 4, 256), "UQ_ERR_UNSUPPORTED"),
         (lib.layout("nf4", 32, 4, 256), "UQ_ERR_UNSUPPORTED"),
         (lib.layout("int4", 64, 0, 256), "UQ_ERR_SHAPE"),
         (lib.layout("int4", 64, 4, 96), "UQ_ERR_SHAPE"),       # k % G
@@ -245,3 +253,88 @@ def test_rmsnorm_rope_validation(lib):
     assert v(10, ctypes.c_float(float("nan"))) == 5 and v(10, ctypes.c_float(-1.0)) == 5
     assert v(0, A + 8) == 4 and v(1, A + 2) == 4 and v(3, A + 2) == 4   # alignment
     assert v(6, 0) == 0                                                  # no tokens: nothing launched
+
+
+# ---------------------------------------------------------------------------
+# GGUF Q4_0 / Q8_0 import (host re-layout into INT4 / INT8 with G = 32)
+# ---------------------------------------------------------------------------
+GGUF = [("q4_0", 2, 4, 18), ("q8_0", 8, 8, 34)]
+
+
+def _set_scales(blob, size, d16):
+    b = blob.reshape(-1, size)
+    bits = np.asarray(d16, dtype=np.float16).view(np.uint16).reshape(-1)
+    b[:, 0], b[:, 1] = bits & 0xFF, bits >> 8
+    return b.reshape(-1)
+
+
+@pytest.mark.parametrize("fmt,t,bits,size", GGUF)
+@pytest.mark.parametrize("n,k,seed", [(1, 32, 1), (7, 96, 2), (33, 2048, 3), (300, 4096, 4)])
+def test_import_gguf_matches_oracle(lib, fmt, t, bits, size, n, k, seed):
+    """Library bytes equal the oracle's INT form packed by the oracle, and
+    decode (through the oracle's INT dequant) to the oracle's block values."""
+    blob = pins.random_gguf(t, n, k, seed)
+    lay, codes, params = lib.uq_import_gguf(fmt, blob, n, k)
+    assert (lay.scheme, lay.group, lay.n, lay.k) == (lib.SCHEMES["int4" if t == 2 else "int8"], 32, n, k)
+    q, s16, z16 = o.gguf_as_int(blob, t, n, k)
+    assert np.array_equal(codes, o.pack_codes(q, bits))
+    assert np.array_equal(params.reshape(-1), o.pack_params_int(s16, z16).reshape(-1))
+    name = "int4" if t == 2 else "int8"
+    wd = o.dequant_packed(codes, params, name, 32, k)
+    assert np.array_equal(wd.astype(np.float64), o.decode_gguf(blob, t, n, k))
+
+
+@pytest.mark.parametrize("fmt,t,bits,size", GGUF)
+def test_import_gguf_edge_scales(lib, fmt, t, bits, size):
+    """Subnormal, signed-zero, negative and the largest accepted scales."""
+    n, k = 4, 32 * 8
+    blob = pins.random_gguf(t, n, k, 5)
+    top = 8188.0 if t == 2 else 511.75
+    d = np.array([2.0 ** -24, 1023 * 2.0 ** -24, -2.0 ** -24, 0.0, -0.0, top, -top, 6.1e-5] * n,
+                 dtype=np.float16)
+    blob = _set_scales(blob, size, d)
+    lay, codes, params = lib.uq_import_gguf(fmt, blob, n, k)
+    q, s16, z16 = o.gguf_as_int(blob, t, n, k)
+    assert np.array_equal(codes, o.pack_codes(q, bits))
+    assert np.array_equal(params.reshape(-1), o.pack_params_int(s16, z16).reshape(-1))
+    wd = o.dequant_packed(codes, params, "int4" if t == 2 else "int8", 32, k)
+    assert np.array_equal(wd.astype(np.float64), o.decode_gguf(blob, t, n, k))
+
+
+def test_import_gguf_hand_built(lib):
+    """The hand-built fixture blocks import to their hand-derived values."""
+    for case in pins.load_gguf_cases():
+        blob = np.frombuffer(b"".join(case["blocks"][r] for r in range(case["n"])), dtype=np.uint8)
+        fmt = "q4_0" if case["gtype"] == 2 else "q8_0"
+        lay, codes, params = lib.uq_import_gguf(fmt, blob, case["n"], case["k"])
+        wd = o.dequant_packed(codes, params, "int4" if case["gtype"] == 2 else "int8", 32, case["k"])
+        for r in range(case["n"]):
+            assert wd[r].astype(np.float64).tolist() == [float(v) for v in case["values"][r]], case["name"]
+
+
+def test_import_gguf_errors(lib):
+    def status(t, blob, n, k):
+        lay = lib.Layout()
+        codes = np.full(max(n * k, 1), 0xAB, dtype=np.uint8)
+        params = np.full(max(n * (k // 32) * 2, 1), 0xABAB, dtype=np.uint16)
+        st = lib.raw_call("uq_import_gguf", t, blob.ctypes.data, n, k, ctypes.byref(lay),
+                          codes.ctypes.data, params.ctypes.data)
+        return lib.STATUS[st], codes, params
+
+    good = pins.random_gguf(2, 2, 64, 6)
+    assert status(2, good, 2, 64)[0] == "UQ_OK"
+    assert status(3, good, 2, 64)[0] == "UQ_ERR_UNSUPPORTED"     # not Q4_0 / Q8_0
+    assert status(2, good, 2, 48)[0] == "UQ_ERR_SHAPE"           # k not whole blocks
+    assert status(2, good, 0, 64)[0] == "UQ_ERR_SHAPE"
+    assert status(8, good, 1, (1 << 24) + 32)[0] == "UQ_ERR_SHAPE"
+    assert lib.raw_call("uq_import_gguf", 2, None, 2, 64, None, None, None) == 1
+    for t, size, bad in ((2, 18, 8192.0), (8, 34, 512.0), (2, 18, np.inf), (8, 34, np.nan)):
+        blob = pins.random_gguf(t, 3, 128, 7)
+        d = np.full(3 * 4, 0.01, dtype=np.float16)
+        d[-1] = bad                                              # only the last block is bad
+        blob = _set_scales(blob, size, d)
+        st, codes, params = status(t, blob, 3, 128)
+        assert st == "UQ_ERR_RANGE", (t, bad)
+        assert (codes == 0xAB).all() and (params == 0xABAB).all(), "written before the check"
+    with pytest.raises(ValueError):
+        lib.uq_import_gguf("q4_0", good[:-1], 2, 64)               # short buffer refused in Python

@@ -15,7 +15,7 @@ from tests.gpu_util import Guarded, dev, gate, note, packed_on_device
 pytestmark = pytest.mark.gpu
 
 INT_LAYOUTS = [("int2", g) for g in (16, 32, 64, 128)] + [("int4", g) for g in (32, 64, 128)] + \
-              [("int8", g) for g in (64, 128)]
+              [("int8", g) for g in (32, 64, 128)]
 BITS = {"int2": 2, "int4": 4, "int8": 8}
 
 

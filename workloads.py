@@ -30,6 +30,7 @@ class Workload:
     outliers: bool = False
     seed: int = 0
     path: str = "gemv"   # "gemv" (M <= 8) or "gemm" (bf16 matrix cores)
+    gguf: int = 0        # GGUF block type the weights arrive in (2 Q4_0, 8 Q8_0); 0: fp32 weights
     note: str = field(default="", compare=False)
 
     @property
@@ -67,6 +68,16 @@ WORKLOADS = {
     "nf4_g64_k4096_n14336_gemm": Workload(
         "nf4_g64_k4096_n14336_gemm", "nf4", 64, 4096, 14336, (64, 256), seed=3,
         path="gemm", note="wide MLP projection, batched"),
+    # GGUF blocks (random quant bytes and scales) re-laid into INT4 / INT8 with G = 32.
+    "q4_0_k4096_n11008": Workload(
+        "q4_0_k4096_n11008", "int4", 32, 4096, 11008, (1, 4), seed=4, gguf=2,
+        note="7B-style MLP up-projection from GGUF Q4_0, decode"),
+    "q8_0_k4096_n4096": Workload(
+        "q8_0_k4096_n4096", "int8", 32, 4096, 4096, (1, 8), seed=5, gguf=8,
+        note="attention q/o projection from GGUF Q8_0, decode"),
+    "q4_0_k4096_n11008_gemm": Workload(
+        "q4_0_k4096_n11008_gemm", "int4", 32, 4096, 11008, (256,), seed=6, gguf=2,
+        path="gemm", note="GGUF Q4_0 MLP up-projection, batched"),
 }
 
 @dataclass(frozen=True)
@@ -139,6 +150,31 @@ def make_workload(wl: Workload):
     w = make_weights(wl.n, wl.k, outliers=wl.outliers, rng=rng)
     x = make_x(wl.mmax, wl.k, rng)
     return w, x
+
+
+# Bytes per 32-weight block of the GGUF block formats (a size, not arithmetic).
+GGUF_BLOCK_BYTES = {2: 18, 8: 34}
+
+
+def make_gguf_blocks(gtype: int, n: int, k: int, seed: int = 0, dmax: float = 0.01,
+                     rng: np.random.Generator | None = None) -> np.ndarray:
+    """GGUF Q4_0 (2) or Q8_0 (8) blocks of an [n, k] matrix, uint8 [n * k/32 * size]:
+    uniform random quant bytes after an fp16 scale d ~ N(0, dmax) (either sign)
+    stored little-endian in the first two bytes of each block."""
+    rng = np.random.default_rng(seed) if rng is None else rng
+    size = GGUF_BLOCK_BYTES[gtype]
+    blob = rng.integers(0, 256, size=(n, k // 32, size)).astype(np.uint8)
+    d = (rng.standard_normal((n, k // 32)) * dmax).astype(np.float16).view(np.uint16)
+    blob[..., 0], blob[..., 1] = d & 0xFF, d >> 8
+    return blob.reshape(-1)
+
+
+def make_gguf_workload(wl: Workload):
+    """(GGUF blocks of W [n, k], x fp16 [mmax, k]) from one generator seeded with wl.seed."""
+    rng = np.random.default_rng(wl.seed)
+    blob = make_gguf_blocks(wl.gguf, wl.n, wl.k, rng=rng)
+    x = make_x(wl.mmax, wl.k, rng)
+    return blob, x
 
 
 def make_random(n: int, k: int, m: int, seed: int, outliers: bool = False):
