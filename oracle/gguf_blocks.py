@@ -25,8 +25,8 @@ is exact in fp32; the oracle forms it in fp64.
 R-GI (the same weights in the INT form w' = q * s + z with G = 32): Q4_0 is
 q = nibble, s = d, z = -8 d; Q8_0 is q = byte + 128 (as unsigned), s = d,
 z = -128 d.  z is exact in fp16 unless it overflows; a non-finite d or an
-overflowing z is refused, never guessed (the lollm page's "hard-fail" design
-principle; the Ultra LLM Engine loader's loud refusal).
+overflowing z is refused, never guessed (the lollm page, Vision, item 3; the
+Ultra LLM Engine loader's loud refusal).
 The INT form reproduces every value exactly as a number (a zero may change
 sign: (nibble - 8) * d is -0 where nibble * d - 8 d is +0).
 """
