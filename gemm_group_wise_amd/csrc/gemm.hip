@@ -621,16 +621,25 @@ hipError_t launch(const uq_layout* L, const void* codes, const void* params, con
                          dim3(T::NT), args, 0, stream);
 }
 
-// Tilings by M: 8 waves (two per SIMD), BM = 32, 64 or 128.  (A 256-row tile
-// on 4 waves, one per SIMD with the accumulators in AGPRs, halves the dequant
-// work per MFMA but measured slower: a lone wave per SIMD hides neither the
-// copies' waits nor the LDS latency.)
+// Tilings: 8 waves (two per SIMD), BM = 128, 64 or 32.  The largest tile that
+// fits M is the cheapest per output (each dequantized fragment feeds BM / 32
+// M tiles) as long as the grid still gives at least half of the 256 CUs a
+// workgroup; a narrower weight matrix takes the next smaller tile instead
+// (N = 4096, M = 256: 64 workgroups of 128 rows took 49.6 us, 256 of 64 rows
+// 28.3 us; at N = 11008 the 172 large tiles beat 688 small ones, 47.8 against
+// 64.8 us).  (A 256-row tile on 4 waves, one per SIMD with the accumulators in
+// AGPRs, halves the dequant work per MFMA but measured slower: a lone wave per
+// SIMD hides neither the copies' waits nor the LDS latency.)
+constexpr int64_t kMinTiles = 128;
+
 template <int S, int G>
 hipError_t launch_tiles(const uq_layout* L, const void* codes, const void* params, const uint16_t* xb,
                         float* y, int m, hipStream_t stream) {
-  if (m <= 32) return launch<S, G, 32, 1, 8>(L, codes, params, xb, y, m, stream);
-  if (m <= 64) return launch<S, G, 64, 1, 8>(L, codes, params, xb, y, m, stream);
-  return launch<S, G, 128, 2, 8>(L, codes, params, xb, y, m, stream);
+  const int64_t n = L->n;
+  auto tiles = [&](int bm, int bn) { return ((int64_t(m) + bm - 1) / bm) * ((n + bn - 1) / bn); };
+  if (m > 64 && tiles(128, 128) >= kMinTiles) return launch<S, G, 128, 2, 8>(L, codes, params, xb, y, m, stream);
+  if (m > 32 && tiles(64, 64) >= kMinTiles) return launch<S, G, 64, 1, 8>(L, codes, params, xb, y, m, stream);
+  return launch<S, G, 32, 1, 8>(L, codes, params, xb, y, m, stream);
 }
 
 }  // namespace

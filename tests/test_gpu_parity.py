@@ -180,16 +180,19 @@ def test_gemm_parity_small(lib, scheme, group):
 
 @pytest.mark.parametrize("scheme,group", [("int4", 128), ("int2", 16), ("int8", 64), ("nf4", 64)])
 def test_gemm_several_row_tiles(lib, scheme, group):
-    """M past one 256-row tile, with a partial last tile (rows past M are computed, not stored)."""
-    n, k = 100, 512
-    w, x = workloads.make_random(n, k, 513, seed=21, outliers=True)
-    lay, codes, params = packed_on_device(lib, scheme, group, w)
-    wdq = oracle_dequant(w, scheme, group)
-    for m in (129, 255, 256, 257, 300, 513):
-        note(f"gemm row tiles {scheme} G{group} m={m}")
-        y = run_gemm(lib, lay, codes, params, x, m)
-        xb = o.bf16_rne(x[:m].astype(np.float32))
-        gate(y, o.gemm_ref(x[:m], wdq), xb, o.bf16_rne(wdq), f"gemm {scheme} G{group} m={m}")
+    """M over several row tiles with a partial last one (rows past M are computed, not
+    stored), at widths that select each tile height: N = 100 runs 32-row tiles, N = 4100
+    64-row tiles and N = 8100 128-row tiles once M > 64 (the grid must reach 128 tiles)."""
+    k = 256
+    for n, seed in ((100, 21), (4100, 22), (8100, 23)):
+        w, x = workloads.make_random(n, k, 513, seed=seed, outliers=True)
+        lay, codes, params = packed_on_device(lib, scheme, group, w)
+        wdq = oracle_dequant(w, scheme, group)
+        for m in (129, 255, 256, 257, 300, 513):
+            note(f"gemm row tiles {scheme} G{group} n={n} m={m}")
+            y = run_gemm(lib, lay, codes, params, x, m)
+            xb = o.bf16_rne(x[:m].astype(np.float32))
+            gate(y, o.gemm_ref(x[:m], wdq), xb, o.bf16_rne(wdq), f"gemm {scheme} G{group} n={n} m={m}")
 
 
 @pytest.mark.parametrize("scheme,group", ALL_LAYOUTS)
