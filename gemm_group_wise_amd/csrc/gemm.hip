@@ -37,6 +37,7 @@
 // MFMA sub-step s (0, 1) takes codes 8s..8s+7 of that half on both the A and
 // the B side (any consistent assignment of k within an MFMA gives the same
 // dot product).
+#include <atomic>
 #include <mutex>
 #include <vector>
 
@@ -51,6 +52,7 @@ constexpr int kKW = 32;          // k per wave per step: 16 codes per lane, two 
 constexpr int kSUB = kKW / 16;
 constexpr int kDC = 3;           // codes are copied this many steps ahead (from HBM: long latency)
 constexpr int kNC = kDC + 1;     // code buffers
+constexpr int kMaxSplit = 4;     // workgroups one tile's K steps may be split over
 
 // Groups per parameter window: at least 16, and enough that a window spans
 // kDC or more steps (the next window is copied kDC steps before it is used,
@@ -72,7 +74,7 @@ struct Tile {
   static constexpr int ABYTES = BM * KS * 2;            // one activation buffer
   static constexpr int ALOADS = ABYTES / (NT * 16);    // 16-byte copies per thread per step
   static constexpr int RPI = NT / CPR;                  // activation rows per copy round
-  static_assert(ALOADS >= 1 && ALOADS % kSUB == 0 || ALOADS == 1, "copies split over the sub-steps");
+  static_assert((ALOADS >= 1 && ALOADS % kSUB == 0) || ALOADS == 1, "copies split over the sub-steps");
   static_assert(RPI % 16 == 0 && CPR >= 16, "swizzle period");
 };
 
@@ -196,7 +198,9 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const uint8_t* __restrict
                                                         const uint8_t* __restrict__ params,
                                                         const uint16_t* __restrict__ xb,
                                                         float* __restrict__ y, int n, int k, int m,
-                                                        int tiles_m, int nblocks) {
+                                                        int tiles_m, int nblocks, int ksplit,
+                                                        float* __restrict__ part,
+                                                        unsigned* __restrict__ arrivals) {
   using T = Tile<BM, WGN, NW>;
   using C = CodeTile<S, T::KS, T::BN, NW>;
   constexpr int bits = Fmt<S>::bits;
@@ -230,9 +234,12 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const uint8_t* __restrict
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wn = wave % WGN, wk = wave / WGN;
   const int b = xcd_order(blockIdx.x, nblocks);
-  const int tile_m = b % tiles_m, tile_n = b / tiles_m;
+  const int split = b % ksplit, tile = b / ksplit;
+  const int tile_m = tile % tiles_m, tile_n = tile / tiles_m;
   const int bm = tile_m * BM, bn = tile_n * T::BN;
+  // This workgroup's share of the K steps: [st0, st1), balanced over ksplit.
   const int steps = (k + T::KS - 1) / T::KS;
+  const int st0 = split * steps / ksplit, st1 = (split + 1) * steps / ksplit;
   const size_t rowb = size_t(k) * bits / 8;
   const int ng = k / G;
   if constexpr (S == UQ_NF4) {
@@ -393,7 +400,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const uint8_t* __restrict
     Codes<S> cnext[2];
     uint32_t pnext[2];
     read_step(st + 1, (u + 1) % kNC, cnext, pnext);
-    const bool live = st * T::KS + kKW * wk + kKW / 2 * kh < k;
+    const bool live = st < st1 && st * T::KS + kKW * wk + kKW / 2 * kh < k;
     float sc[2], zc[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -460,28 +467,35 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const uint8_t* __restrict
     }
   };
 
-  // Prologue: the first window, the codes of steps 0 .. kDC - 1 and the
-  // activation tile of step 0, in the order the steps' waits expect (the
-  // codes of step kDC - 1 last).
-  issue_params(0);
+  // Prologue: the window of step st0 (and the next one when the steps would
+  // issue it less than kDC steps after st0, i.e. before this range starts),
+  // the codes of steps st0 .. st0 + kDC - 1 and the activation tile of step
+  // st0, in the order the steps' waits expect (the codes of step
+  // st0 + kDC - 1 last).  Buffers are indexed by the step's place in the
+  // range: codes st0 + j in buffer j % kNC, activations in set j % 2.
+  issue_params(st0 / SPW);
+  if ((st0 / SPW + 1) * SPW < st0 + kDC) issue_params(st0 / SPW + 1);
 #pragma unroll
-  for (int j = 0; j + 1 < kDC; ++j) issue_codes(j, j);
-  issue_act(0, 0, -1);
-  issue_codes(kDC - 1, kDC - 1);
+  for (int j = 0; j + 1 < kDC; ++j) issue_codes(st0 + j, j);
+  issue_act(st0, 0, -1);
+  issue_codes(st0 + kDC - 1, kDC - 1);
   wait_step();
-  read_step(0, 0, ccur, pcur);
-  // Rounds of kNC steps; a step past K multiplies by w' = 0.
-  for (int st = 0; st < steps; st += kNC) {
+  read_step(st0, 0, ccur, pcur);
+  // Rounds of kNC steps; a step past the range multiplies by w' = 0.
+  for (int st = st0; st < st1; st += kNC) {
 #pragma unroll
     for (int u = 0; u < kNC; ++u) step(st + u, u);
   }
 
   // Sum the K slices: a halving tree through LDS (float4 per lane and element
-  // group, lane-major so the partner wave reads what it wrote), over AC of the
-  // TM M tiles at a time so that the partial sums fit the activation buffers.
-  constexpr int AC = T::ABYTES / 16384 < T::TM ? T::ABYTES / 16384 : T::TM;
-  static_assert(AC >= 1 && T::TM % AC == 0, "reduction passes");
-  constexpr int SB = AC * 2 * 4 * 64 * 16;  // bytes of one wave's partial sums per pass
+  // group, lane-major so the partner wave reads what it wrote), over FP of the
+  // wave's 2 * TM accumulator tiles (tile f = 2 a + t) at a time so that the
+  // partial sums fit the activation buffers.
+  constexpr int FB = 4 * 64 * 16;  // bytes of one accumulator tile of one wave
+  constexpr int FP_FIT = 2 * T::ABYTES / ((T::WGK / 2) * WGN * FB);
+  constexpr int FP = FP_FIT >= 2 * T::TM ? 2 * T::TM : FP_FIT >= 4 ? 4 : FP_FIT >= 2 ? 2 : 1;
+  static_assert(FP_FIT >= 1 && (2 * T::TM) % FP == 0, "reduction passes");
+  constexpr int SB = FP * FB;  // bytes of one wave's partial sums per pass
   static_assert(T::ABYTES % SB == 0 && (T::WGK / 2) * WGN * SB <= 2 * T::ABYTES, "partial sums fit");
   auto slot = [&](int sl) __attribute__((always_inline)) {
     const int off = sl * SB;
@@ -490,52 +504,120 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const uint8_t* __restrict
   __builtin_amdgcn_s_waitcnt(0x0F70);  // the copies of the step past the end
   __syncthreads();
 #pragma unroll
-  for (int a0 = 0; a0 < T::TM; a0 += AC) {
+  for (int f0 = 0; f0 < 2 * T::TM; f0 += FP) {
 #pragma unroll
     for (int half = T::WGK / 2; half >= 1; half /= 2) {
       if (wk >= half && wk < 2 * half) {
         float4* dst = slot((wk - half) * WGN + wn);
 #pragma unroll
-        for (int a = 0; a < AC; ++a)
+        for (int f = 0; f < FP; ++f)
 #pragma unroll
-          for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int j4 = 0; j4 < 4; ++j4)
-              dst[((a * 2 + t) * 4 + j4) * 64] =
-                  make_float4(acc[a0 + a][t][4 * j4], acc[a0 + a][t][4 * j4 + 1], acc[a0 + a][t][4 * j4 + 2],
-                              acc[a0 + a][t][4 * j4 + 3]);
+          for (int j4 = 0; j4 < 4; ++j4) {
+            const f32x16& v = acc[(f0 + f) / 2][(f0 + f) % 2];
+            dst[(f * 4 + j4) * 64] = make_float4(v[4 * j4], v[4 * j4 + 1], v[4 * j4 + 2], v[4 * j4 + 3]);
+          }
       }
       __syncthreads();
       if (wk < half) {
         const float4* src = slot(wk * WGN + wn);
 #pragma unroll
-        for (int a = 0; a < AC; ++a)
+        for (int f = 0; f < FP; ++f)
 #pragma unroll
-          for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int j4 = 0; j4 < 4; ++j4) {
-              const float4 v = src[((a * 2 + t) * 4 + j4) * 64];
-              acc[a0 + a][t][4 * j4] += v.x;
-              acc[a0 + a][t][4 * j4 + 1] += v.y;
-              acc[a0 + a][t][4 * j4 + 2] += v.z;
-              acc[a0 + a][t][4 * j4 + 3] += v.w;
-            }
+          for (int j4 = 0; j4 < 4; ++j4) {
+            const float4 v = src[(f * 4 + j4) * 64];
+            f32x16& d = acc[(f0 + f) / 2][(f0 + f) % 2];
+            d[4 * j4] += v.x;
+            d[4 * j4 + 1] += v.y;
+            d[4 * j4 + 2] += v.z;
+            d[4 * j4 + 3] += v.w;
+          }
       }
       __syncthreads();
     }
   }
-  if (wk != 0) return;
 
   // D layout of a 32x32 tile: lane l, element j -> row 8*(j/4) + 4*(l/32) + j%4
   // (an x row), column l % 32 (a weight row).
+  auto out_row = [&](int a, int j) __attribute__((always_inline)) { return bm + a * 32 + 8 * (j / 4) + 4 * kh + (j % 4); };
+  auto out_col = [&](int t) __attribute__((always_inline)) { return bn + wn * 64 + t * 32 + r32; };
+
+  // (Split only for row tiles up to 64: the summing pass keeps kMaxSplit
+  // values of BM * BN / NT elements per thread in registers.)
+  if constexpr (BM <= 64) if (ksplit > 1) {
+    // K split over ksplit (<= kMaxSplit) workgroups: each writes its partial
+    // tile to part[split], and the last of the tile's workgroups to arrive
+    // (counted with one device-scope atomic per tile) adds the ksplit partial
+    // tiles in split order and stores y, so the sum does not depend on which
+    // one arrives last.  Nothing waits on another workgroup.  Each XCD has
+    // its own L2, so the partial tiles are written and read with device-scope
+    // (coherent) accesses instead of fences: a device-scope fence here writes
+    // back and invalidates the whole L2, evicting the activations every other
+    // workgroup on that XCD is streaming.  The last workgroup also returns
+    // the tile's counter to zero for the next call.
+    const size_t rows = size_t(tiles_m) * BM;
+    if (wk == 0) {
+      float* dst = part + size_t(split) * rows * size_t(n);
+#pragma unroll
+      for (int a = 0; a < T::TM; ++a)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int col = out_col(t);
+#pragma unroll
+          for (int j = 0; j < 16; ++j)
+            if (col < n)
+              __hip_atomic_store(dst + size_t(out_row(a, j)) * size_t(n) + col, acc[a][t][j], __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the partial tile has been written
+    __syncthreads();
+    __shared__ unsigned last;
+    if (tid == 0) {
+      const unsigned before = atomicAdd(arrivals + tile, 1u);
+      last = before == unsigned(ksplit - 1);
+      if (last) atomicExch(arrivals + tile, 0u);
+    }
+    __syncthreads();
+    if (!last) return;
+    // All threads of the last workgroup: thread tid takes elements
+    // e = i * NT + tid of the BM x BN tile (consecutive threads, consecutive
+    // columns), issues the loads of every partial tile at once and then adds
+    // them in split order.
+    constexpr int E = BM * T::BN / T::NT;
+    float v[kMaxSplit][E];
+#pragma unroll
+    for (int sp = 0; sp < kMaxSplit; ++sp) {
+      const int spc = sp < ksplit ? sp : ksplit - 1;  // past ksplit: a valid address, value unused
+      const float* src = part + (size_t(spc) * rows + size_t(bm)) * size_t(n);
+#pragma unroll
+      for (int i = 0; i < E; ++i) {
+        const int e = i * T::NT + tid;
+        const int col = min(bn + e % T::BN, n - 1);
+        v[sp][i] = __hip_atomic_load(src + size_t(e / T::BN) * size_t(n) + col, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      float sum = v[0][i];
+#pragma unroll
+      for (int sp = 1; sp < kMaxSplit; ++sp) sum = sp < ksplit ? sum + v[sp][i] : sum;
+      const int e = i * T::NT + tid;
+      const int row = bm + e / T::BN, col = bn + e % T::BN;
+      if (row < m && col < n) y[size_t(row) * size_t(n) + col] = sum;
+    }
+    return;
+  }
+
+  if (wk != 0) return;
 #pragma unroll
   for (int a = 0; a < T::TM; ++a)
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const int col = bn + wn * 64 + t * 32 + r32;
+      const int col = out_col(t);
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const int row = bm + a * 32 + 8 * (j / 4) + 4 * kh + (j % 4);
+        const int row = out_row(a, j);
         if (row < m && col < n) y[size_t(row) * size_t(n) + col] = acc[a][t][j];
       }
     }
@@ -556,11 +638,13 @@ __global__ __launch_bounds__(256) void to_bf16_kernel(const uint16_t* __restrict
   }
 }
 
-// Activation workspace, one per (device, stream) so calls on different
-// streams never share it; calls on one stream are ordered by the stream.  A
-// buffer that is outgrown stays allocated (a captured graph may still name
-// it) until the process ends; growth is at least 2x, so the retired buffers
-// add up to less than the live one.
+// GEMM workspace, one per (device, stream) so calls on different streams
+// never share it; calls on one stream are ordered by the stream.  It holds
+// the arrival counters of K-split tiles (zeroed once, when the buffer is
+// allocated; every call leaves them at zero again), the bf16 activations and
+// the partial tiles of a K split.  A buffer that is outgrown stays allocated
+// (a captured graph may still name it) until the process ends; growth is at
+// least 2x, so the retired buffers add up to less than the live one.
 struct Workspace {
   int device;
   hipStream_t stream;
@@ -571,7 +655,7 @@ std::mutex g_ws_mutex;
 std::vector<Workspace> g_ws;
 std::vector<void*> g_ws_retired;
 
-hipError_t activation_workspace(hipStream_t stream, size_t bytes, void** out) {
+hipError_t gemm_workspace(hipStream_t stream, size_t zeroed_bytes, size_t bytes, void** out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
@@ -593,6 +677,11 @@ hipError_t activation_workspace(hipStream_t stream, size_t bytes, void** out) {
   void* p = nullptr;
   e = hipMalloc(&p, want);
   if (e != hipSuccess) return e;
+  e = hipMemsetAsync(p, 0, zeroed_bytes, stream);  // ordered before the first kernel that uses it
+  if (e != hipSuccess) {
+    (void)hipFree(p);
+    return e;
+  }
   if (w) {
     g_ws_retired.push_back(w->ptr);
     w->ptr = p;
@@ -604,56 +693,150 @@ hipError_t activation_workspace(hipStream_t stream, size_t bytes, void** out) {
   return hipSuccess;
 }
 
+// Tilings: 8 waves (two per SIMD); BM rows of x by BN = 64 * WGN weight
+// rows, with the K steps of each tile split over ksplit workgroups when the
+// tiles alone would leave CUs idle.
+struct Plan {
+  int bm, wgn, ksplit;
+};
+
+// Tiles whose K split is summed by the last workgroup need one arrival
+// counter each; the workspace holds this many.
+constexpr int64_t kMaxSplitTiles = 16384;
+
+// The largest tile that fits M is the cheapest per output (each dequantized
+// fragment feeds BM / 32 M tiles) as long as the grid still gives at least
+// half of the 256 CUs a workgroup; a narrower weight matrix takes the next
+// smaller tile instead (N = 4096, M = 256: 64 workgroups of 128 rows took
+// 49.6 us, 256 of 64 rows 28.3 us; at N = 11008 the 172 large tiles beat 688
+// small ones, 47.8 against 64.8 us).  (A 256-row tile on 4 waves, one per
+// SIMD with the accumulators in AGPRs, halves the dequant work per MFMA but
+// measured slower: a lone wave per SIMD hides neither the copies' waits nor
+// the LDS latency.)
+//
+// Up to 64 rows a workgroup's time is mostly the latency of its K steps
+// (each waits for codes copied two steps earlier), so fewer steps per
+// workgroup help as long as the extra workgroups are resident at once:
+// ksplit = the workgroups the chip holds at once (CUs x workgroups per CU,
+// from the kernel's LDS and registers) over the tiles, at most kMaxSplit.  Measured
+// (uq_gemm call, M = 64): INT8 / INT2 at N = 4096 (64 tiles, one workgroup
+// per CU) 27.1 / 25.4 us unsplit, 18.1 / 17.5 us in four; INT4 at
+// N = 11008, M = 16 (172 tiles, two per CU) 22.5 us unsplit, 19.8 us in
+// two; at M = 64 (172 tiles, one per CU) a split only adds a second round
+// of workgroups and was slower (26.9 against 34.9 us in two).
+constexpr int64_t kMinTiles = 128;
+
+Plan plan_gemm(int64_t m, int64_t n) {
+  auto tiles = [&](int bm, int bn) { return ((m + bm - 1) / bm) * ((n + bn - 1) / bn); };
+  if (m > 64 && tiles(128, 128) >= kMinTiles) return {128, 2, 1};
+  if (m > 32) return {64, 1, 1};
+  return {32, 1, 1};
+}
+
+// Workgroups of this kernel one CU holds at once (cached per kernel).
+template <int S, int G, int BM, int WGN, int NW>
+int resident_per_cu() {
+  static std::atomic<int> cached{0};
+  int v = cached.load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int occ = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(&gemm_kernel<S, G, BM, WGN, NW>),
+                                                   64 * NW, 0) != hipSuccess || occ < 1)
+    occ = 1;
+  cached.store(occ, std::memory_order_relaxed);
+  return occ;
+}
+
+int device_cus() {
+  static std::atomic<int> cached{0};
+  int v = cached.load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus < 1)
+    cus = 256;
+  cached.store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+// K split for a plan: see above.  Row tiles of up to 64 only, at least two
+// K steps per workgroup.
+template <int S, int G>
+int plan_ksplit(const Plan& p, int64_t m, int64_t n, int64_t k) {
+  if (m > 64 || p.bm > 64) return 1;
+  const int64_t tiles = ((m + p.bm - 1) / p.bm) * ((n + 64 * p.wgn - 1) / (64 * p.wgn));
+  if (tiles > kMaxSplitTiles) return 1;
+  const int64_t ks_step = 32 * 8 / p.wgn;
+  const int64_t steps = (k + ks_step - 1) / ks_step;
+  const int per_cu = p.bm == 64 ? resident_per_cu<S, G, 64, 1, 8>() : resident_per_cu<S, G, 32, 1, 8>();
+  int64_t ks = int64_t(device_cus()) * per_cu / tiles;
+  if (ks > kMaxSplit) ks = kMaxSplit;
+  if (ks > steps / 2) ks = steps / 2;
+  return ks > 1 ? int(ks) : 1;
+}
+
 template <int S, int G, int BM, int WGN, int NW>
 hipError_t launch(const uq_layout* L, const void* codes, const void* params, const uint16_t* xb,
-                  float* y, int m, hipStream_t stream) {
+                  float* y, int m, int ksplit, float* part, unsigned* arrivals, hipStream_t stream) {
   using T = Tile<BM, WGN, NW>;
   int n = int(L->n), k = int(L->k);
   int tiles_m = (m + BM - 1) / BM;
   const int64_t tiles_n = (int64_t(n) + T::BN - 1) / T::BN;
-  const int64_t nb = int64_t(tiles_m) * tiles_n;
+  const int64_t nb = int64_t(tiles_m) * tiles_n * ksplit;
   if (nb > 0x7fffffff) return hipErrorInvalidValue;
   int nblocks = int(nb);
   const uint8_t* c8 = static_cast<const uint8_t*>(codes);
   const uint8_t* p8 = static_cast<const uint8_t*>(params);
-  void* args[] = {&c8, &p8, (void*)&xb, &y, &n, &k, &m, &tiles_m, &nblocks};
+  void* args[] = {&c8, &p8, (void*)&xb, &y, &n, &k, &m, &tiles_m, &nblocks, &ksplit, &part, &arrivals};
   return hipLaunchKernel(reinterpret_cast<const void*>(&gemm_kernel<S, G, BM, WGN, NW>), dim3(unsigned(nblocks)),
                          dim3(T::NT), args, 0, stream);
 }
 
-// Tilings: 8 waves (two per SIMD), BM = 128, 64 or 32.  The largest tile that
-// fits M is the cheapest per output (each dequantized fragment feeds BM / 32
-// M tiles) as long as the grid still gives at least half of the 256 CUs a
-// workgroup; a narrower weight matrix takes the next smaller tile instead
-// (N = 4096, M = 256: 64 workgroups of 128 rows took 49.6 us, 256 of 64 rows
-// 28.3 us; at N = 11008 the 172 large tiles beat 688 small ones, 47.8 against
-// 64.8 us).  (A 256-row tile on 4 waves, one per SIMD with the accumulators in
-// AGPRs, halves the dequant work per MFMA but measured slower: a lone wave per
-// SIMD hides neither the copies' waits nor the LDS latency.)
-constexpr int64_t kMinTiles = 128;
-
 template <int S, int G>
-hipError_t launch_tiles(const uq_layout* L, const void* codes, const void* params, const uint16_t* xb,
-                        float* y, int m, hipStream_t stream) {
-  const int64_t n = L->n;
-  auto tiles = [&](int bm, int bn) { return ((int64_t(m) + bm - 1) / bm) * ((n + bn - 1) / bn); };
-  if (m > 64 && tiles(128, 128) >= kMinTiles) return launch<S, G, 128, 2, 8>(L, codes, params, xb, y, m, stream);
-  if (m > 32 && tiles(64, 64) >= kMinTiles) return launch<S, G, 64, 1, 8>(L, codes, params, xb, y, m, stream);
-  return launch<S, G, 32, 1, 8>(L, codes, params, xb, y, m, stream);
+hipError_t launch_plan(const Plan& p, const uq_layout* L, const void* codes, const void* params,
+                       const uint16_t* xb, float* y, int m, float* part, unsigned* arrivals, hipStream_t stream) {
+  if (p.bm == 128) return launch<S, G, 128, 2, 8>(L, codes, params, xb, y, m, p.ksplit, part, arrivals, stream);
+  if (p.bm == 64) return launch<S, G, 64, 1, 8>(L, codes, params, xb, y, m, p.ksplit, part, arrivals, stream);
+  return launch<S, G, 32, 1, 8>(L, codes, params, xb, y, m, p.ksplit, part, arrivals, stream);
 }
 
 }  // namespace
 
 hipError_t launch_gemm(const uq_layout* L, const void* codes, const void* params, const uint16_t* x,
                        float* y, int m, hipStream_t stream) {
+  Plan plan = plan_gemm(m, L->n);
+#define UQ_GEMM_CASE(SC, GR) \
+  case SC * 1000 + GR: plan.ksplit = plan_ksplit<SC, GR>(plan, m, L->n, L->k); break;
+  switch (L->scheme * 1000 + L->group) {
+    UQ_GEMM_CASE(UQ_INT2, 16)
+    UQ_GEMM_CASE(UQ_INT2, 32)
+    UQ_GEMM_CASE(UQ_INT2, 64)
+    UQ_GEMM_CASE(UQ_INT2, 128)
+    UQ_GEMM_CASE(UQ_INT4, 32)
+    UQ_GEMM_CASE(UQ_INT4, 64)
+    UQ_GEMM_CASE(UQ_INT4, 128)
+    UQ_GEMM_CASE(UQ_INT8, 32)
+    UQ_GEMM_CASE(UQ_INT8, 64)
+    UQ_GEMM_CASE(UQ_INT8, 128)
+    UQ_GEMM_CASE(UQ_NF4, 64)
+    default: return hipErrorInvalidValue;
+  }
+#undef UQ_GEMM_CASE
   const int64_t count = int64_t(m) * L->k;  // k % 32 == 0: whole 8-value pieces
-  // Whole 128-row tiles: the GEMM reads rows past M without clamping (their
+  // Workspace: [arrival counters][bf16 x, whole 128-row tiles][partial
+  // tiles of a K split].  The GEMM reads rows past M without clamping (their
   // products are never stored).
   const int64_t rows = (int64_t(m) + 127) / 128 * 128;
+  const size_t counter_bytes = size_t(kMaxSplitTiles) * 4;
+  const size_t act_bytes = size_t(rows * L->k) * 2;
+  const size_t part_bytes =
+      plan.ksplit > 1 ? size_t(plan.ksplit) * size_t((m + plan.bm - 1) / plan.bm * plan.bm) * size_t(L->n) * 4 : 0;
   void* ws = nullptr;
-  hipError_t e = activation_workspace(stream, size_t(rows * L->k) * 2, &ws);
+  hipError_t e = gemm_workspace(stream, counter_bytes, counter_bytes + act_bytes + part_bytes, &ws);
   if (e != hipSuccess) return e;
-  uint16_t* xb = static_cast<uint16_t*>(ws);
+  unsigned* arrivals = static_cast<unsigned*>(ws);
+  uint16_t* xb = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(ws) + counter_bytes);
+  float* part = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + counter_bytes + act_bytes);
   {
     int64_t count8 = count / 8;
     const int64_t want = (count8 + 255) / 256;
@@ -662,20 +845,23 @@ hipError_t launch_gemm(const uq_layout* L, const void* codes, const void* params
     e = hipLaunchKernel(reinterpret_cast<const void*>(&to_bf16_kernel), dim3(grid), dim3(256), args, 0, stream);
     if (e != hipSuccess) return e;
   }
+#define UQ_GEMM_CASE(SC, GR) \
+  case SC * 1000 + GR: return launch_plan<SC, GR>(plan, L, codes, params, xb, y, m, part, arrivals, stream);
   switch (L->scheme * 1000 + L->group) {
-    case UQ_INT2 * 1000 + 16: return launch_tiles<UQ_INT2, 16>(L, codes, params, xb, y, m, stream);
-    case UQ_INT2 * 1000 + 32: return launch_tiles<UQ_INT2, 32>(L, codes, params, xb, y, m, stream);
-    case UQ_INT2 * 1000 + 64: return launch_tiles<UQ_INT2, 64>(L, codes, params, xb, y, m, stream);
-    case UQ_INT2 * 1000 + 128: return launch_tiles<UQ_INT2, 128>(L, codes, params, xb, y, m, stream);
-    case UQ_INT4 * 1000 + 32: return launch_tiles<UQ_INT4, 32>(L, codes, params, xb, y, m, stream);
-    case UQ_INT4 * 1000 + 64: return launch_tiles<UQ_INT4, 64>(L, codes, params, xb, y, m, stream);
-    case UQ_INT4 * 1000 + 128: return launch_tiles<UQ_INT4, 128>(L, codes, params, xb, y, m, stream);
-    case UQ_INT8 * 1000 + 32: return launch_tiles<UQ_INT8, 32>(L, codes, params, xb, y, m, stream);
-    case UQ_INT8 * 1000 + 64: return launch_tiles<UQ_INT8, 64>(L, codes, params, xb, y, m, stream);
-    case UQ_INT8 * 1000 + 128: return launch_tiles<UQ_INT8, 128>(L, codes, params, xb, y, m, stream);
-    case UQ_NF4 * 1000 + 64: return launch_tiles<UQ_NF4, 64>(L, codes, params, xb, y, m, stream);
+    UQ_GEMM_CASE(UQ_INT2, 16)
+    UQ_GEMM_CASE(UQ_INT2, 32)
+    UQ_GEMM_CASE(UQ_INT2, 64)
+    UQ_GEMM_CASE(UQ_INT2, 128)
+    UQ_GEMM_CASE(UQ_INT4, 32)
+    UQ_GEMM_CASE(UQ_INT4, 64)
+    UQ_GEMM_CASE(UQ_INT4, 128)
+    UQ_GEMM_CASE(UQ_INT8, 32)
+    UQ_GEMM_CASE(UQ_INT8, 64)
+    UQ_GEMM_CASE(UQ_INT8, 128)
+    UQ_GEMM_CASE(UQ_NF4, 64)
     default: return hipErrorInvalidValue;
   }
+#undef UQ_GEMM_CASE
 }
 
 }  // namespace uq

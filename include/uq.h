@@ -118,15 +118,21 @@ uq_status uq_gemv(const uq_layout* layout, const void* codes,
  * Both casts round to nearest even; products accumulate in fp32, in an order
  * fixed by (layout, m), so repeated calls give identical bits.
  * Arguments as for uq_gemv.
- * Workspace: bf16(x) is staged in device memory the library owns, one buffer
- * per (device, stream), m' * k * 2 bytes with m' = m rounded up to a multiple
- * of 128, allocated with hipMalloc by the first
- * call that needs it to be larger (at least doubling) and kept until the
- * process ends.  Calls on one stream are ordered by the stream; calls on
- * different streams use different buffers.  A call that would have to grow
- * the buffer while `stream` is being captured into a graph returns
- * UQ_ERR_HIP without launching: make one call of the largest m * k on that
- * stream before capturing. */
+ * For m <= 64 the K dimension is split over several workgroups per output
+ * tile; the last of them to finish adds the partial tiles in a fixed order,
+ * so results stay bitwise repeatable.
+ * Workspace: device memory the library owns, one buffer per (device,
+ * stream), holding 64 KiB of arrival counters (zeroed when the buffer is
+ * allocated; every call leaves them zero), bf16(x) as m' * k * 2 bytes with
+ * m' = m rounded up to a multiple of 128, and for a K split its partial
+ * tiles (at most 8 * m'' * n * 4 bytes, m'' = m rounded up to the row tile).
+ * It is allocated with hipMalloc by the first call that needs it to be
+ * larger (at least doubling) and kept until the process ends.  Calls on one
+ * stream are ordered by the stream; calls on different streams use
+ * different buffers.  A call that would have to grow the buffer while
+ * `stream` is being captured into a graph returns UQ_ERR_HIP without
+ * launching: make one call of the largest m * k (and m * n) on that stream
+ * before capturing. */
 uq_status uq_gemm(const uq_layout* layout, const void* codes,
                   const void* params, const uint16_t* x, float* y, int64_t m,
                   void* stream);

@@ -223,10 +223,10 @@ def test_gemm_k_tail(lib, k):
 def test_gemm_batched_equivalence(lib):
     """Row i of an M-row GEMM equals the single-row GEMM of x[i].
 
-    Up to M = 64 the GEMM uses one tiling (K cut into slices of 64 per step
-    of 512) whatever M is, so rows agree bit for bit; from M = 65 the K step
-    is 256 and the slices are summed in another order, so rows agree to fp32
-    reassociation.  (GEMM and GEMV rows are not compared under the gate: the
+    Up to M = 64 the GEMM uses one K order whatever M is (steps of 128 cut
+    into four slices of 32, the same K split over workgroups), so rows agree
+    bit for bit; from M = 65 the steps are split and summed in another order,
+    so rows agree to fp32 reassociation.  (GEMM and GEMV rows are not compared under the gate: the
     bf16 rounding of w' alone moves the GEMM by ~2e-3 relative to the fp16
     GEMV, which is why the GEMM's oracle applies the same casts.)
     """
@@ -242,11 +242,44 @@ def test_gemm_batched_equivalence(lib):
     assert np.abs(y - ys).max() <= 1e-5 * np.abs(ys).max()
 
 
+@pytest.mark.parametrize("scheme,group", [("int4", 128), ("int2", 16), ("int8", 32), ("nf4", 64), ("int4", 32)])
+def test_gemm_k_split(lib, scheme, group):
+    """Up to M = 64 the K steps are split over several workgroups and the last
+    one to finish a tile adds the partial tiles.  K values give ranges that
+    start inside a parameter window, odd step counts and a ragged last tile
+    of weight rows; N small enough that every tile is split four ways."""
+    for n, k, seed in ((100, 2560, 31), (300, 1536, 32), (129, 4096, 33)):
+        w, x = workloads.make_random(n, k, 64, seed=seed, outliers=True)
+        lay, codes, params = packed_on_device(lib, scheme, group, w)
+        wdq = oracle_dequant(w, scheme, group)
+        for m in (1, 16, 33, 64):
+            note(f"gemm k split {scheme} G{group} n={n} k={k} m={m}")
+            y = run_gemm(lib, lay, codes, params, x, m)
+            xb = o.bf16_rne(x[:m].astype(np.float32))
+            gate(y, o.gemm_ref(x[:m], wdq), xb, o.bf16_rne(wdq), f"gemm split {scheme} G{group} n={n} k={k} m={m}")
+
+
+@pytest.mark.parametrize("scheme,group", [("int4", 128), ("int2", 16), ("int8", 64), ("nf4", 64)])
+def test_gemm_k_split_identity_bit_exact(lib, scheme, group):
+    """X = the first 64 rows of I with K = 2560 (K split over four workgroups):
+    each output is one product, so the partial tiles and their sum are exact
+    and y = bf16(w')^T[:64] bit for bit."""
+    n, k = 70, 2560
+    w, _ = workloads.make_random(n, k, 1, seed=34, outliers=True)
+    lay, codes, params = packed_on_device(lib, scheme, group, w)
+    wdq = oracle_dequant(w, scheme, group)
+    x = np.eye(k, dtype=np.float16)[:64]
+    note(f"gemm k split identity {scheme} G{group}")
+    y = run_gemm(lib, lay, codes, params, x, 64)
+    want = o.bf16_rne(wdq).T[:64]
+    assert np.array_equal(y.view(np.uint32), np.ascontiguousarray(want).view(np.uint32))
+
+
 def test_gemm_deterministic(lib):
     """Repeated calls give identical bits (no atomics, fixed summation order)."""
     w, x = workloads.make_random(1000, 4096, 256, seed=16)
     lay, codes, params = packed_on_device(lib, "int4", 128, w)
-    for m in (16, 256):
+    for m in (1, 16, 64, 256):
         note(f"gemm deterministic m={m}")
         a = run_gemm(lib, lay, codes, params, x, m)
         b = run_gemm(lib, lay, codes, params, x, m)
