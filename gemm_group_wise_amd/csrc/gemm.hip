@@ -6,9 +6,13 @@
 // w' = fma(q, s, z) (INT-N) or C[q] * a (NF4) is the exact fp32 dequant and
 // both casts round to nearest even.
 //
-// Two launches on the caller's stream:
-//   1. x (fp16) -> bf16 into an activation workspace, once per call, so the
-//      conversion is not repeated by every column tile.
+// One or two launches on the caller's stream:
+//   1. From 65 activation rows: x (fp16) -> bf16 into an activation
+//      workspace, once per call, so the conversion is not repeated by every
+//      column tile (there the GEMM is bound by VALU issue).  Up to 64 rows
+//      the GEMM is bound by memory latency instead; it stages the caller's
+//      fp16 x and rounds each fragment to bf16 as it reads it from LDS (the
+//      same bits), which saves the extra launch (~4.7 us at M = 16).
 //   2. The GEMM.  A workgroup is 8 waves (two per SIMD, so one wave's
 //      dequant VALU work and LDS reads run under the other's MFMAs; on gfx950
 //      a single wave does not overlap them well).  The workgroup owns BM rows
@@ -193,7 +197,7 @@ __device__ __forceinline__ int xcd_order(int b, int nb) {
   return x * q + (x < r ? x : r) + (b >> 3);
 }
 
-template <int S, int G, int BM, int WGN, int NW>
+template <int S, int G, int BM, int WGN, int NW, bool XF>
 __global__ __launch_bounds__(64 * NW) void gemm_kernel(const uint8_t* __restrict__ codes,
                                                         const uint8_t* __restrict__ params,
                                                         const uint16_t* __restrict__ xb,
@@ -256,11 +260,18 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const uint8_t* __restrict
   // chunk is the same for every i.
   const int r0 = tid / T::CPR;
   const int cl = (tid % T::CPR) ^ (r0 & 15);
-  // Sources are a base common to the workgroup (per copy i) plus a 32-bit lane
-  // offset.  The workspace holds whole 128-row tiles, so rows past M are read
-  // without clamping (their outputs are not stored).
+  // Sources are a base common to the workgroup plus a 32-bit lane offset per
+  // copy.  From the bf16 workspace (whole 128-row tiles) rows past M are read
+  // without clamping; from the caller's fp16 x (XF) they are clamped to row
+  // M - 1.  Either way their outputs are not stored.
   const uint16_t* abase = xb + size_t(bm) * size_t(k);
-  const uint32_t alane = uint32_t(r0) * uint32_t(k);
+  uint32_t alane[T::ALOADS];
+#pragma unroll
+  for (int i = 0; i < T::ALOADS; ++i) {
+    int r = i * T::RPI + r0;
+    if constexpr (XF) r = bm + r < m ? r : m - 1 - bm;
+    alane[i] = uint32_t(r) * uint32_t(k);
+  }
 
   // Code copy j of this wave: lane slot q -> row r = piece / PPR, logical
   // piece p = (piece % PPR) ^ swz(r); 4-byte lanes take dword q % 4 of it.
@@ -335,7 +346,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const uint8_t* __restrict
 #pragma unroll
     for (int i = 0; i < T::ALOADS; ++i)
       if (part < 0 || i % kSUB == part)
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(abase + size_t(i) * T::RPI * size_t(k) + (alane + uint32_t(col))),
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(abase + (alane[i] + uint32_t(col))),
                                          (__attribute__((address_space(3))) void*)(adst + i * T::NT * 16), 16, 0, 0);
   };
   auto issue_codes = [&](int st, int cset) __attribute__((always_inline)) {
@@ -418,7 +429,16 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const uint8_t* __restrict
     const uint8_t* Ab = abuf(u & 1) + r32 * T::CPR * 16;
     auto afrag = [&](int a, int s) __attribute__((always_inline)) {
       const int chunk = ((kKW / 8) * wk + (kKW / 16) * kh + s) ^ (r32 & 15);
-      return *reinterpret_cast<const bf16x8*>(Ab + (a * 32 * T::CPR + chunk) * 16);
+      if constexpr (XF) {  // fp16 in LDS: round to bf16 here (exact fp32 widening, then RNE)
+        const uint4 h = *reinterpret_cast<const uint4*>(Ab + (a * 32 * T::CPR + chunk) * 16);
+        const uint4 v = make_uint4(pack_bf16(h2f(uint16_t(h.x)), h2f(uint16_t(h.x >> 16))),
+                                   pack_bf16(h2f(uint16_t(h.y)), h2f(uint16_t(h.y >> 16))),
+                                   pack_bf16(h2f(uint16_t(h.z)), h2f(uint16_t(h.z >> 16))),
+                                   pack_bf16(h2f(uint16_t(h.w)), h2f(uint16_t(h.w >> 16))));
+        return __builtin_bit_cast(bf16x8, v);
+      } else {
+        return *reinterpret_cast<const bf16x8*>(Ab + (a * 32 * T::CPR + chunk) * 16);
+      }
     };
     bf16x8 acur[T::TM], bcur[2];
 #pragma unroll
@@ -698,6 +718,7 @@ hipError_t gemm_workspace(hipStream_t stream, size_t zeroed_bytes, size_t bytes,
 // tiles alone would leave CUs idle.
 struct Plan {
   int bm, wgn, ksplit;
+  bool xf;  // the GEMM stages the caller's fp16 x and rounds it to bf16 itself
 };
 
 // Tiles whose K split is summed by the last workgroup need one arrival
@@ -728,19 +749,20 @@ constexpr int64_t kMinTiles = 128;
 
 Plan plan_gemm(int64_t m, int64_t n) {
   auto tiles = [&](int bm, int bn) { return ((m + bm - 1) / bm) * ((n + bn - 1) / bn); };
-  if (m > 64 && tiles(128, 128) >= kMinTiles) return {128, 2, 1};
-  if (m > 32) return {64, 1, 1};
-  return {32, 1, 1};
+  if (m > 64 && tiles(128, 128) >= kMinTiles) return {128, 2, 1, false};
+  if (m > 64) return {64, 1, 1, false};
+  if (m > 32) return {64, 1, 1, true};
+  return {32, 1, 1, true};
 }
 
 // Workgroups of this kernel one CU holds at once (cached per kernel).
-template <int S, int G, int BM, int WGN, int NW>
+template <int S, int G, int BM, int WGN, int NW, bool XF>
 int resident_per_cu() {
   static std::atomic<int> cached{0};
   int v = cached.load(std::memory_order_relaxed);
   if (v > 0) return v;
   int occ = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(&gemm_kernel<S, G, BM, WGN, NW>),
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(&gemm_kernel<S, G, BM, WGN, NW, XF>),
                                                    64 * NW, 0) != hipSuccess || occ < 1)
     occ = 1;
   cached.store(occ, std::memory_order_relaxed);
@@ -768,14 +790,14 @@ int plan_ksplit(const Plan& p, int64_t m, int64_t n, int64_t k) {
   if (tiles > kMaxSplitTiles) return 1;
   const int64_t ks_step = 32 * 8 / p.wgn;
   const int64_t steps = (k + ks_step - 1) / ks_step;
-  const int per_cu = p.bm == 64 ? resident_per_cu<S, G, 64, 1, 8>() : resident_per_cu<S, G, 32, 1, 8>();
+  const int per_cu = p.bm == 64 ? resident_per_cu<S, G, 64, 1, 8, true>() : resident_per_cu<S, G, 32, 1, 8, true>();
   int64_t ks = int64_t(device_cus()) * per_cu / tiles;
   if (ks > kMaxSplit) ks = kMaxSplit;
   if (ks > steps / 2) ks = steps / 2;
   return ks > 1 ? int(ks) : 1;
 }
 
-template <int S, int G, int BM, int WGN, int NW>
+template <int S, int G, int BM, int WGN, int NW, bool XF>
 hipError_t launch(const uq_layout* L, const void* codes, const void* params, const uint16_t* xb,
                   float* y, int m, int ksplit, float* part, unsigned* arrivals, hipStream_t stream) {
   using T = Tile<BM, WGN, NW>;
@@ -788,16 +810,17 @@ hipError_t launch(const uq_layout* L, const void* codes, const void* params, con
   const uint8_t* c8 = static_cast<const uint8_t*>(codes);
   const uint8_t* p8 = static_cast<const uint8_t*>(params);
   void* args[] = {&c8, &p8, (void*)&xb, &y, &n, &k, &m, &tiles_m, &nblocks, &ksplit, &part, &arrivals};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&gemm_kernel<S, G, BM, WGN, NW>), dim3(unsigned(nblocks)),
+  return hipLaunchKernel(reinterpret_cast<const void*>(&gemm_kernel<S, G, BM, WGN, NW, XF>), dim3(unsigned(nblocks)),
                          dim3(T::NT), args, 0, stream);
 }
 
 template <int S, int G>
 hipError_t launch_plan(const Plan& p, const uq_layout* L, const void* codes, const void* params,
                        const uint16_t* xb, float* y, int m, float* part, unsigned* arrivals, hipStream_t stream) {
-  if (p.bm == 128) return launch<S, G, 128, 2, 8>(L, codes, params, xb, y, m, p.ksplit, part, arrivals, stream);
-  if (p.bm == 64) return launch<S, G, 64, 1, 8>(L, codes, params, xb, y, m, p.ksplit, part, arrivals, stream);
-  return launch<S, G, 32, 1, 8>(L, codes, params, xb, y, m, p.ksplit, part, arrivals, stream);
+  if (p.bm == 128) return launch<S, G, 128, 2, 8, false>(L, codes, params, xb, y, m, p.ksplit, part, arrivals, stream);
+  if (p.bm == 64 && !p.xf) return launch<S, G, 64, 1, 8, false>(L, codes, params, xb, y, m, p.ksplit, part, arrivals, stream);
+  if (p.bm == 64) return launch<S, G, 64, 1, 8, true>(L, codes, params, xb, y, m, p.ksplit, part, arrivals, stream);
+  return launch<S, G, 32, 1, 8, true>(L, codes, params, xb, y, m, p.ksplit, part, arrivals, stream);
 }
 
 }  // namespace
@@ -823,21 +846,22 @@ hipError_t launch_gemm(const uq_layout* L, const void* codes, const void* params
   }
 #undef UQ_GEMM_CASE
   const int64_t count = int64_t(m) * L->k;  // k % 32 == 0: whole 8-value pieces
-  // Workspace: [arrival counters][bf16 x, whole 128-row tiles][partial
-  // tiles of a K split].  The GEMM reads rows past M without clamping (their
-  // products are never stored).
+  // Workspace: [arrival counters][bf16 x, whole 128-row tiles, unless the
+  // GEMM reads the caller's fp16 x][partial tiles of a K split].  The GEMM
+  // reads workspace rows past M without clamping (their products are never
+  // stored).
   const int64_t rows = (int64_t(m) + 127) / 128 * 128;
   const size_t counter_bytes = size_t(kMaxSplitTiles) * 4;
-  const size_t act_bytes = size_t(rows * L->k) * 2;
+  const size_t act_bytes = plan.xf ? 0 : size_t(rows * L->k) * 2;
   const size_t part_bytes =
       plan.ksplit > 1 ? size_t(plan.ksplit) * size_t((m + plan.bm - 1) / plan.bm * plan.bm) * size_t(L->n) * 4 : 0;
   void* ws = nullptr;
   hipError_t e = gemm_workspace(stream, counter_bytes, counter_bytes + act_bytes + part_bytes, &ws);
   if (e != hipSuccess) return e;
   unsigned* arrivals = static_cast<unsigned*>(ws);
-  uint16_t* xb = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(ws) + counter_bytes);
+  uint16_t* xb = plan.xf ? const_cast<uint16_t*>(x) : reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(ws) + counter_bytes);
   float* part = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + counter_bytes + act_bytes);
-  {
+  if (!plan.xf) {
     int64_t count8 = count / 8;
     const int64_t want = (count8 + 255) / 256;
     const unsigned grid = unsigned(want < 1024 ? want : 1024);
