@@ -215,24 +215,34 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const uint8_t* __restrict
   constexpr int PBYTES = T::BN * WIN * 4;         // one window: a dword slot per group
   static_assert(SPW >= kDC && PPW >= 1, "parameter window shape");
   static_assert(G >= kKW / 2, "a lane's 16 codes lie in one group");
-  // Every buffer is its own LDS object and the step loop is unrolled by kNC,
-  // so the compiler can tell the copies into one buffer from the reads of
-  // another and adds no waits of its own.
+  // Activation buffers: three when they fit next to the code ring (the tile
+  // of step st + 2 is copied during step st), else two (st + 1).  Copies
+  // complete in issue order, so the activation look-ahead also bounds how
+  // long the codes copied before it may stay in flight.
+  constexpr int LDS_FIXED = 2 * T::ABYTES + kNC * C::BYTES + 2 * PBYTES + 256;
+  constexpr int AB = LDS_FIXED + T::ABYTES <= 160 * 1024 ? 3 : 2;
+  constexpr int UNROLL = AB == 3 ? 12 : kNC;  // steps per round: buffer indices are constants
+  // Every buffer the steps read while copies into another one are in flight
+  // is its own LDS object (the activation and code buffers), and the step
+  // loop is unrolled so each index is a constant: the compiler can then tell
+  // the copies into one buffer from the reads of another and adds no waits
+  // of its own.  The two parameter windows share one object: they are read
+  // only at the start of a step, before the step issues any copy.
   __shared__ __attribute__((aligned(16))) uint8_t act0[T::ABYTES];
   __shared__ __attribute__((aligned(16))) uint8_t act1[T::ABYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t act2[AB == 3 ? T::ABYTES : 16];
   __shared__ __attribute__((aligned(16))) uint8_t cod0[C::BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t cod1[C::BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t cod2[C::BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t cod3[C::BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t par0[PBYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t par1[PBYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t par[2 * PBYTES];
   __shared__ float nf4[16];
-  static_assert(kNC == 4, "four code buffers");
-  auto abuf = [&](int i) __attribute__((always_inline)) { return i ? act1 : act0; };
+  static_assert(kNC == 4 && UNROLL % kNC == 0 && UNROLL % AB == 0, "buffer indices repeat every round");
+  auto abuf = [&](int i) __attribute__((always_inline)) { return i == 0 ? act0 : i == 1 ? act1 : act2; };
   auto cbuf = [&](int i) __attribute__((always_inline)) {
     return i == 0 ? cod0 : i == 1 ? cod1 : i == 2 ? cod2 : cod3;
   };
-  auto pbuf = [&](int i) __attribute__((always_inline)) { return i ? par1 : par0; };
+  auto pbuf = [&](int i) __attribute__((always_inline)) { return par + i * PBYTES; };
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -361,20 +371,25 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const uint8_t* __restrict
       else __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0);
     }
   };
+  // Copies a wave may still have in flight when a step starts: those the
+  // step before issued for later steps (its codes, and with three activation
+  // buffers its activation tile too).  Everything older -- including what
+  // this step reads -- has landed.
+  constexpr int INFLIGHT = C::PER_WAVE + (AB == 3 ? T::ALOADS : 0);
   auto wait_step = [&]() __attribute__((always_inline)) {
     // A plain s_barrier, not __syncthreads() (whose fences wait for every
     // copy); the waits go through the builtin so that the compiler's
     // wait-count tracking sees them.  The scheduling barriers keep the
     // previous step's MFMAs from being moved after the wait.
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(0x0F70 | C::PER_WAVE);  // vmcnt(PER_WAVE), gfx9 encoding
+    __builtin_amdgcn_s_waitcnt(0x0F70 | INFLIGHT);     // vmcnt(INFLIGHT), gfx9 encoding
     __builtin_amdgcn_s_waitcnt(0xC07F);                // lgkmcnt(0)
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
   };
-  static_assert(C::PER_WAVE < 16, "vmcnt field");
+  static_assert(INFLIGHT < 16, "vmcnt field");
 
   // The lane's codes and group parameters of step st, read from LDS (during
   // the step before, once everything step st reads has landed).
@@ -382,16 +397,10 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const uint8_t* __restrict
     const int k0 = st * T::KS + kKW * wk + kKW / 2 * kh;
     const int win = st / SPW;
     const int gi = (k0 / G) - win * WIN;  // the lane's group within the window
-    // Both window buffers are read and one value kept: a read through a
-    // pointer chosen at run time could be any LDS object to the compiler,
-    // which would then wait for every copy in flight first.
-    const uint32_t* pw0 = reinterpret_cast<const uint32_t*>(par0);
-    const uint32_t* pw1 = reinterpret_cast<const uint32_t*>(par1);
+    const uint32_t* pw = reinterpret_cast<const uint32_t*>(par) + (win & 1) * (PBYTES / 4);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const int i = prow[t] + (gi ^ pswz[t]);
-      const uint32_t v0 = pw0[i], v1 = pw1[i];
-      pr[t] = (win & 1) ? v1 : v0;
+      pr[t] = pw[prow[t] + (gi ^ pswz[t])];
       cc[t] = lds_codes<S>(cbuf(cset) + coff[t]);
     }
   };
@@ -399,7 +408,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const uint8_t* __restrict
   Codes<S> ccur[2];
   uint32_t pcur[2];
 
-  // One K step from activation buffer st % 2 and code buffer st % kNC.  Sub-
+  // One K step from activation buffer u % AB and code buffer u % kNC.  Sub-
   // steps are software-pipelined: while sub-step s's MFMAs run, the wave
   // reads sub-step s+1's activation fragments and dequantizes its weights;
   // the scheduling hints interleave each MFMA with a share of that VALU work.
@@ -426,7 +435,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const uint8_t* __restrict
     }
     const Codes<S> cc[2] = {ccur[0], ccur[1]};
 
-    const uint8_t* Ab = abuf(u & 1) + r32 * T::CPR * 16;
+    const uint8_t* Ab = abuf(u % AB) + r32 * T::CPR * 16;
     auto afrag = [&](int a, int s) __attribute__((always_inline)) {
       const int chunk = ((kKW / 8) * wk + (kKW / 16) * kh + s) ^ (r32 & 15);
       if constexpr (XF) {  // fp16 in LDS: round to bf16 here (exact fp32 widening, then RNE)
@@ -449,9 +458,9 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const uint8_t* __restrict
     for (int s = 0; s < kSUB; ++s) {
       if (s == 0) {
         if ((st + kDC) % SPW == 0) issue_params((st + kDC) / SPW);
-        issue_act(st + 1, (u + 1) & 1, 0);
+        issue_act(st + AB - 1, (u + AB - 1) % AB, 0);
       } else {
-        issue_act(st + 1, (u + 1) & 1, s);
+        issue_act(st + AB - 1, (u + AB - 1) % AB, s);
         if (s == kSUB - 1) issue_codes(st + kDC, (u + kDC) % kNC);
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -489,23 +498,30 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const uint8_t* __restrict
 
   // Prologue: the window of step st0 (and the next one when the steps would
   // issue it less than kDC steps after st0, i.e. before this range starts),
-  // the codes of steps st0 .. st0 + kDC - 1 and the activation tile of step
-  // st0, in the order the steps' waits expect (the codes of step
-  // st0 + kDC - 1 last).  Buffers are indexed by the step's place in the
-  // range: codes st0 + j in buffer j % kNC, activations in set j % 2.
+  // the codes of steps st0 .. st0 + kDC - 1 and the activation tiles of
+  // steps st0 .. st0 + AB - 2, in the order the steps' waits expect (what
+  // "the step before st0" would have issued last).  Buffers are indexed by
+  // the step's place in the range: codes st0 + j in buffer j % kNC,
+  // activations in buffer j % AB.
   issue_params(st0 / SPW);
   if ((st0 / SPW + 1) * SPW < st0 + kDC) issue_params(st0 / SPW + 1);
 #pragma unroll
   for (int j = 0; j + 1 < kDC; ++j) issue_codes(st0 + j, j);
-  issue_act(st0, 0, -1);
+#pragma unroll
+  for (int j = 0; j + 1 < AB; ++j) issue_act(st0 + j, j, -1);
   issue_codes(st0 + kDC - 1, kDC - 1);
   wait_step();
   read_step(st0, 0, ccur, pcur);
-  // Rounds of kNC steps; a step past the range multiplies by w' = 0.
-  for (int st = st0; st < st1; st += kNC) {
+  // Rounds of UNROLL steps, left after the range's last step (copies it
+  // issued for later steps are drained below).
+  for (int st = st0;;) {
 #pragma unroll
-    for (int u = 0; u < kNC; ++u) step(st + u, u);
+    for (int u = 0; u < UNROLL; ++u) {
+      step(st, u);
+      if (++st >= st1) goto steps_done;
+    }
   }
+steps_done:
 
   // Sum the K slices: a halving tree through LDS (float4 per lane and element
   // group, lane-major so the partner wave reads what it wrote), over FP of the
@@ -714,8 +730,8 @@ hipError_t gemm_workspace(hipStream_t stream, size_t zeroed_bytes, size_t bytes,
 }
 
 // Tilings: 8 waves (two per SIMD); BM rows of x by BN = 64 * WGN weight
-// rows, with the K steps of each tile split over ksplit workgroups when the
-// tiles alone would leave CUs idle.
+// rows; up to 64 rows, the K steps of each tile split over ksplit
+// workgroups when the tiles alone would leave CUs idle.
 struct Plan {
   int bm, wgn, ksplit;
   bool xf;  // the GEMM stages the caller's fp16 x and rounds it to bf16 itself
@@ -736,15 +752,15 @@ constexpr int64_t kMaxSplitTiles = 16384;
 // the LDS latency.)
 //
 // Up to 64 rows a workgroup's time is mostly the latency of its K steps
-// (each waits for codes copied two steps earlier), so fewer steps per
-// workgroup help as long as the extra workgroups are resident at once:
+// (each waits for copies issued one or two steps earlier), so fewer steps
+// per workgroup help as long as the extra workgroups are resident at once:
 // ksplit = the workgroups the chip holds at once (CUs x workgroups per CU,
-// from the kernel's LDS and registers) over the tiles, at most kMaxSplit.  Measured
-// (uq_gemm call, M = 64): INT8 / INT2 at N = 4096 (64 tiles, one workgroup
-// per CU) 27.1 / 25.4 us unsplit, 18.1 / 17.5 us in four; INT4 at
-// N = 11008, M = 16 (172 tiles, two per CU) 22.5 us unsplit, 19.8 us in
-// two; at M = 64 (172 tiles, one per CU) a split only adds a second round
-// of workgroups and was slower (26.9 against 34.9 us in two).
+// from the kernel's LDS and registers) over the tiles, at most kMaxSplit.
+// Measured per uq_gemm call: INT8 / INT2 at N = 4096, M = 64 (64 tiles, one
+// workgroup per CU) 27.1 / 25.4 us unsplit, 14.5 / 14.3 us in four; INT4 at
+// N = 11008 (172 tiles, one workgroup per CU with three activation buffers
+// in LDS) M = 16 16.4 us unsplit against 22.1 / 24.1 us in two / four, and
+// M = 64 22.6 us on 64-row tiles against 30.4 us on 344 tiles of 32 rows.
 constexpr int64_t kMinTiles = 128;
 
 Plan plan_gemm(int64_t m, int64_t n) {

@@ -223,10 +223,10 @@ def test_gemm_k_tail(lib, k):
 def test_gemm_batched_equivalence(lib):
     """Row i of an M-row GEMM equals the single-row GEMM of x[i].
 
-    Up to M = 64 the GEMM uses one K order whatever M is (steps of 128 cut
-    into four slices of 32, the same K split over workgroups), so rows agree
-    bit for bit; from M = 65 the steps are split and summed in another order,
-    so rows agree to fp32 reassociation.  (GEMM and GEMV rows are not compared under the gate: the
+    Up to M = 64 the GEMM uses one K order whatever M is (32- and 64-row
+    tiles both cut K steps of 256 into eight slices of 32, with the same K
+    split over workgroups), so rows agree bit for bit; from M = 65 the steps
+    and slices differ and rows agree to fp32 reassociation.  (GEMM and GEMV rows are not compared under the gate: the
     bf16 rounding of w' alone moves the GEMM by ~2e-3 relative to the fp16
     GEMV, which is why the GEMM's oracle applies the same casts.)
     """
