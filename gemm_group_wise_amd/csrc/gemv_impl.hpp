@@ -29,7 +29,13 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kXBlock = 16384;  // activations staged per LDS block (all rows of x together)
+// Activations staged per LDS block (all rows of x together).  INT2 takes
+// twice as many: with 5-8 activation rows its K = 4096 then fits one block
+// and the loop-free path (INT2 G16 N4096 M=8 15.0 -> 10.6 us); INT8 is
+// slower that way (11.3 -> 12.3 us at M=8: 388 VGPRs, one wave per SIMD).
+template <int S>
+constexpr int x_block() { return S == UQ_INT2 ? 32768 : 16384; }
+constexpr int kMaxIPT = 8;  // activation group parts staged per thread and K block, at most
 
 template <int S, int G, int MT = 1>
 struct Geo {
@@ -41,7 +47,7 @@ struct Geo {
   static constexpr int XV = GP / 8;           // 128-bit activation loads per part
   // chunks per lane per group: up to 4096 codes of K, but no more than one
   // LDS block of activations holds
-  static constexpr int U0 = (kXBlock / MT) / (64 * CW);
+  static constexpr int U0 = (x_block<S>() / MT) / (64 * CW);
   static constexpr int U = U0 < 1 ? 1 : (U0 < 64 / CW ? U0 : 64 / CW);
   static constexpr bool NF = (S == UQ_NF4);
 };
@@ -436,7 +442,8 @@ template <int S, int G, int MT, int R, bool ONE>
 hipError_t launch_ipt(int ipt, dim3 grid, void** args, size_t shmem, hipStream_t stream) {
   const void* fn = ipt == 1   ? reinterpret_cast<const void*>(&gemv_kernel<S, G, MT, R, ONE, 1>)
                    : ipt == 2 ? reinterpret_cast<const void*>(&gemv_kernel<S, G, MT, R, ONE, 2>)
-                              : reinterpret_cast<const void*>(&gemv_kernel<S, G, MT, R, ONE, 4>);
+                   : ipt == 4 ? reinterpret_cast<const void*>(&gemv_kernel<S, G, MT, R, ONE, 4>)
+                              : reinterpret_cast<const void*>(&gemv_kernel<S, G, MT, R, ONE, 8>);
   return hipLaunchKernel(fn, grid, dim3(kThreads), args, shmem, stream);
 }
 
@@ -445,8 +452,11 @@ hipError_t launch(const uq_layout* L, const void* codes, const void* params, con
                   float* y, int m, hipStream_t stream) {
   using Gm = Geo<S, G, MT>;
   const int k = int(L->k), n = int(L->n);
-  int kb_max = kXBlock / MT;
+  int kb_max = x_block<S>() / MT;
   if (kb_max > k) kb_max = k;
+  // At most 8 staged activation parts per thread (kMaxIPT): a block holds at
+  // most kMaxIPT * kThreads parts of GP activations across the MT rows.
+  if (int64_t(MT) * (kb_max / Gm::GP) > int64_t(kMaxIPT) * kThreads) kb_max = kMaxIPT * kThreads * Gm::GP / MT;
   const size_t shmem = (Gm::NF ? 2048 : 0) + size_t(MT) * kb_max * 2 +
                        (Gm::NF ? 0 : size_t(MT) * (kb_max / Gm::GP) * 8);
   const int rows_per_block = kWaves * R;
@@ -455,7 +465,7 @@ hipError_t launch(const uq_layout* L, const void* codes, const void* params, con
   const uint8_t* p8 = static_cast<const uint8_t*>(params);
   void* args[] = {&c8, &p8, (void*)&x, &y, (void*)&n, (void*)&k, &m, &kb_max};
   const int items = MT * (kb_max / Gm::GP);  // staged activation parts per K block
-  const int ipt = items <= kThreads ? 1 : items <= 2 * kThreads ? 2 : 4;
+  const int ipt = items <= kThreads ? 1 : items <= 2 * kThreads ? 2 : items <= 4 * kThreads ? 4 : 8;
   const bool one = kb_max == k && k <= 64 * Gm::U * Gm::CW;
   return one ? launch_ipt<S, G, MT, R, true>(ipt, grid, args, shmem, stream)
              : launch_ipt<S, G, MT, R, false>(ipt, grid, args, shmem, stream);

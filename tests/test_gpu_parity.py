@@ -133,9 +133,10 @@ def test_gemv_batched_equivalence(lib):
                     gate(y, np.stack(ys[:m]).astype(np.float64), x[:m], wdq, f"equiv {scheme} m={m}")
 
 
-@pytest.mark.parametrize("m,k", [(1, 20480), (8, 8192), (4, 4224)])
+@pytest.mark.parametrize("m,k", [(1, 36864), (8, 8192), (4, 8320)])
 def test_gemv_k_blocks(lib, m, k):
-    """K larger than one LDS block of activations, with a ragged last block."""
+    """K larger than one LDS block of activations (16384 values over all rows, 32768 for
+    INT2), with a ragged last block."""
     w, x = workloads.make_random(70, k, m, seed=9)
     for scheme, group in (("int4", 128), ("int2", 64), ("nf4", 64), ("int8", 64)):
         if k % max(group, CW[scheme]):
