@@ -22,12 +22,14 @@
 //      (v_mfma_f32_32x32x16_bf16 tiles) and the K slices are summed through
 //      LDS at the end, so no partial sums go to memory.
 //   * Everything a step needs is copied into LDS by global_load_lds (no VGPR
-//     staging): the bf16 activation tile (BM x KS, from L2) one step ahead
-//     into the other of two buffers; the packed codes of the BN weight rows
-//     for the step (from HBM, so with a longer wait) three steps ahead into a
-//     ring of four; and a window of 16 or more groups of parameters per
-//     weight row, at least three steps ahead into the other of two.  The vector memory pipeline charges about a
-//     cycle per four adjacent lanes and cache line touched, so every copy is
+//     staging): the activation tile (BM x KS, from L2) two steps ahead into
+//     a ring of three buffers (one step ahead into two where three do not
+//     fit); the packed codes of the BN weight rows for the step (from HBM, so
+//     with a longer wait) three steps ahead into a ring of four; and a window
+//     of 16 or more groups of parameters per weight row, at least three steps
+//     ahead into the other half of a two-window buffer.  The vector memory
+//     pipeline charges about a cycle per four adjacent lanes and cache line
+//     touched, so every copy is
 //     laid out for four or more adjacent lanes to read one line: a per-lane
 //     load of each lane's own codes (32 rows per instruction) costs 3-4x as
 //     much for the same bytes.  Each lane then reads its 16 codes and its

@@ -290,7 +290,9 @@ def test_gemm_deterministic(lib):
 def test_gemm_graph_replay(lib):
     """A call captured in a HIP graph (after a warm-up call on the capture
     stream, which sizes the activation workspace) replays the eager result,
-    replay after replay, with eager work on the same buffers in between."""
+    replay after replay, with eager work on the same buffers in between.
+    N = 384 makes six tiles, so K is split over two workgroups per tile: the
+    replays also check that each call leaves the arrival counters at zero."""
     import torch
     w, x = workloads.make_random(384, 1024, 64, seed=17)
     lay, codes, params = packed_on_device(lib, "int4", 64, w)
