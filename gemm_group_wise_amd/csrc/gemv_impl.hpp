@@ -198,6 +198,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
   const uint32_t magic = kMagic2;
 
   if constexpr (NF) {
+    static_assert(kThreads == 256, "the NF4 byte table takes one entry per thread");
     // byte b -> the codes' values C[b & 15], C[b >> 4] as a pair of fp16 high
     // parts h = fp16(C) and a pair of low parts l = fp16(C - h): h + l holds
     // C to about 2^-22, and the dot products of x with h and with l are exact
