@@ -430,13 +430,16 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
   }
 }
 
-// Weight rows per wave.  Four for a single activation row; with two or more
+// Weight rows per wave.  Four for a single activation row (two for INT8,
+// whose rows hold twice the bytes: N4096 M=1 5.43 -> 5.03 us; INT4 is slower
+// with two, 6.79 -> 7.24 us, and every scheme with eight); with two or more
 // activation rows the per-row state grows and two rows per wave keep more
 // waves resident (measured on MI355X: 5-14 % faster for INT4 M=4 and INT8
 // M=8).  INT2 keeps four (its LDS traffic per code byte is the highest).
 template <int S, int MT>
 constexpr int rows_per_wave() {
-  return (MT == 1 || S == UQ_INT2) ? 4 : 2;
+  if (MT == 1) return S == UQ_INT8 ? 2 : 4;
+  return S == UQ_INT2 ? 4 : 2;
 }
 
 template <int S, int G, int MT, int R, bool ONE>
