@@ -82,6 +82,8 @@ class Setup:
         dc, dp = torch.from_numpy(codes).cuda(), torch.from_numpy(params.view(np.int16)).cuda()
         self.codes = [dc] + [dc.clone() for _ in range(rotate - 1)]
         self.params = [dp] + [dp.clone() for _ in range(rotate - 1)]
+        if self.x_host.shape[0] != m:
+            raise ValueError(f"{wl.name}: M = {m} but the workload's x has {self.x_host.shape[0]} rows")
         self.x = torch.from_numpy(np.ascontiguousarray(self.x_host)).cuda()
         self.y = torch.empty(m * wl.n, dtype=torch.float32, device="cuda")
         self.fn = uq.uq_gemv_a8 if a8 else (uq.uq_gemv if wl.path == "gemv" else uq.uq_gemm)
@@ -435,7 +437,10 @@ def main() -> None:
         norm_rope_line(args)
         return
     wl = workloads.WORKLOADS[args.workload]
-    m = args.m or wl.ms[0]
+    m = args.m if args.m is not None else wl.ms[0]
+    if not 1 <= m <= wl.mmax:
+        # x is generated with wl.mmax rows; the kernels read M rows of it.
+        raise SystemExit(f"{wl.name}: --m must be between 1 and {wl.mmax} (the rows of its activations)")
     if args.traffic_parse:
         traffic_parse(wl, m, args.traffic_parse[0], args.traffic_parse[1], args.traffic_cmd)
         return
