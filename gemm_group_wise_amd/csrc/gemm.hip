@@ -217,6 +217,12 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const uint8_t* __restrict
   constexpr int PBYTES = T::BN * WIN * 4;         // one window: a dword slot per group
   static_assert(SPW >= kDC && PPW >= 1, "parameter window shape");
   static_assert(G >= kKW / 2, "a lane's 16 codes lie in one group");
+  // VALU instructions the scheduler places between consecutive MFMAs of a
+  // sub-step, over the 2 * TM MFMAs: per scheme, as measured at M = 256
+  // (INT8 N = 4096 29.4 / 28.1 us per call with 48 / 32, NF4 N = 14336
+  // 60.3 / 58.8 us with 48 / 72; INT4 N = 11008 46.4 us with 48, 47.4-48.1
+  // with 32, 72 or 96).
+  constexpr int kShare = S == UQ_INT8 ? 32 : S == UQ_NF4 ? 72 : 48;
   // Activation buffers: three when they fit next to the code ring (the tile
   // of step st + 2 is copied during step st), else two (st + 1).  Copies
   // complete in issue order, so the activation look-ahead also bounds how
@@ -482,7 +488,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const uint8_t* __restrict
 #pragma unroll
         for (int q = 0; q < 2 * T::TM; ++q) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                    // one MFMA
-          __builtin_amdgcn_sched_group_barrier(0x002, 48 / (2 * T::TM), 0);     // a share of the VALU
+          __builtin_amdgcn_sched_group_barrier(0x002, kShare / (2 * T::TM), 0);  // a share of the VALU
           if (q < T::TM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // and an LDS read
         }
 #pragma unroll
