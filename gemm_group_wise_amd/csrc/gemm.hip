@@ -218,11 +218,11 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(const uint8_t* __restrict
   static_assert(SPW >= kDC && PPW >= 1, "parameter window shape");
   static_assert(G >= kKW / 2, "a lane's 16 codes lie in one group");
   // VALU instructions the scheduler places between consecutive MFMAs of a
-  // sub-step, over the 2 * TM MFMAs: per scheme, as measured at M = 256
-  // (INT8 N = 4096 29.4 / 28.1 us per call with 48 / 32, NF4 N = 14336
-  // 60.3 / 58.8 us with 48 / 72; INT4 N = 11008 46.4 us with 48, 47.4-48.1
-  // with 32, 72 or 96).
-  constexpr int kShare = S == UQ_INT8 ? 32 : S == UQ_NF4 ? 72 : 48;
+  // sub-step, over the 2 * TM MFMAs: for 128-row tiles per scheme, as
+  // measured at M = 256 (INT8 N = 4096 29.4 / 28.1 us per call with 48 / 32,
+  // NF4 N = 14336 60.3 / 58.8 us with 48 / 72; INT4 N = 11008 46.4 us with
+  // 48, 47.4-48.1 with 32, 72 or 96); 32 for row tiles of up to 64.
+  constexpr int kShare = T::TM <= 2 ? 32 : S == UQ_INT8 ? 32 : S == UQ_NF4 ? 72 : 48;
   // Activation buffers: three when they fit next to the code ring (the tile
   // of step st + 2 is copied during step st), else two (st + 1).  Copies
   // complete in issue order, so the activation look-ahead also bounds how
