@@ -344,7 +344,11 @@ class NormRopeSetup:
 
 
 def report_all(uq, steps: int, warmup: int, path: str | None) -> None:
-    rows = ["| workload | path | M | weight MB | us/launch | weight GB/s | % HBM | TFLOP/s | % bf16 MFMA |",
+    cmd = "python bench.py " + " ".join(sys.argv[1:])
+    rows = ["# Every workload and activation count: time per launch", "",
+            "Launches replayed from a HIP graph, weights rotated out of the caches, inputs resident in HBM.", "",
+            "Command (MI355X host, repository root):", "", f"    {cmd}", "",
+            "| workload | path | M | weight MB | us/launch | weight GB/s | % HBM | TFLOP/s | % bf16 MFMA |",
             "|---|---|---|---|---|---|---|---|---|"]
     for name, wl in workloads.WORKLOADS.items():
         for m in wl.ms:
