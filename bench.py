@@ -87,11 +87,16 @@ class Setup:
         self.x = torch.from_numpy(np.ascontiguousarray(self.x_host)).cuda()
         self.y = torch.empty(m * wl.n, dtype=torch.float32, device="cuda")
         self.fn = uq.uq_gemv_a8 if a8 else (uq.uq_gemv if wl.path == "gemv" else uq.uq_gemm)
+        # the GEMM's workspace: allocated zero-filled once, reused by every launch on the one stream
+        self.ws = uq.gemm_workspace(self.lay, m) if self.fn is uq.uq_gemm else None
         torch.cuda.synchronize()
 
     def launch(self, i: int, stream: int) -> None:
         j = i % self.rotate
-        self.fn(self.lay, self.codes[j], self.params[j], self.x, self.y, self.m, stream=stream)
+        if self.ws is not None:
+            self.fn(self.lay, self.codes[j], self.params[j], self.x, self.y, self.m, self.ws, stream=stream)
+        else:
+            self.fn(self.lay, self.codes[j], self.params[j], self.x, self.y, self.m, stream=stream)
 
     def graph(self, count: int, start: int = 0):
         import torch

@@ -1,10 +1,13 @@
 """ctypes binding of libuq (include/uq.h).  Argument marshalling only.
 
-Device buffers are passed as integers or as objects with ``data_ptr()``
-(torch tensors); streams as integers or objects with ``cuda_stream``.  When no
-stream is given the current torch stream is used.  Every non-OK status raises
-:class:`UQError`.  If the library is not built, importing this module raises:
-there is no fallback.
+Device buffers are passed as integers or as torch tensors; streams as
+integers or objects with ``cuda_stream``.  When no stream is given the current
+torch stream is used.  A tensor is checked before the call (on a GPU,
+contiguous, of an accepted dtype and large enough for the layout and m), so a
+CPU tensor or a short buffer raises ValueError instead of reaching a kernel;
+a plain integer is passed through unchecked (the raw escape hatch).  Every
+non-OK status raises :class:`UQError`.  If the library is not built,
+importing this module raises: there is no fallback.
 """
 from __future__ import annotations
 
@@ -24,7 +27,7 @@ GEMV_MAX_M = 8
 GEMM_MAX_M = 65536
 
 STATUS = {0: "UQ_OK", 1: "UQ_ERR_NULL", 2: "UQ_ERR_SHAPE", 3: "UQ_ERR_UNSUPPORTED",
-          4: "UQ_ERR_ALIGN", 5: "UQ_ERR_RANGE", 6: "UQ_ERR_HIP"}
+          4: "UQ_ERR_ALIGN", 5: "UQ_ERR_RANGE", 6: "UQ_ERR_HIP", 7: "UQ_ERR_WORKSPACE"}
 
 
 class UQError(RuntimeError):
@@ -63,7 +66,8 @@ _lib.uq_packed_size.argtypes = [_L, ctypes.POINTER(ctypes.c_size_t), ctypes.POIN
 _lib.uq_pack_weights.argtypes = [_L, _P, _P, _P]
 _lib.uq_import_gguf.argtypes = [ctypes.c_int32, _P, ctypes.c_int64, ctypes.c_int64, _L, _P, _P]
 _lib.uq_gemv.argtypes = [_L, _P, _P, _P, _P, ctypes.c_int64, _P]
-_lib.uq_gemm.argtypes = [_L, _P, _P, _P, _P, ctypes.c_int64, _P]
+_lib.uq_gemm.argtypes = [_L, _P, _P, _P, _P, ctypes.c_int64, _P, ctypes.c_size_t, _P]
+_lib.uq_gemm_workspace_size.argtypes = [_L, ctypes.c_int64, ctypes.POINTER(ctypes.c_size_t)]
 _lib.uq_dequant.argtypes = [_L, _P, _P, _P, _P]
 _lib.uq_gemv_a8.argtypes = [_L, _P, _P, _P, _P, ctypes.c_int64, _P]
 _lib.uq_quantize_activations.argtypes = [ctypes.c_int32, _P, _P, _P, ctypes.c_int64, ctypes.c_int64, _P]
@@ -74,12 +78,13 @@ _lib.uq_rmsnorm_rope.argtypes = [_P, _P, _P, _P, _P, _P, ctypes.c_int64, ctypes.
 _lib.uq_status_str.argtypes = [ctypes.c_int]
 _lib.uq_status_str.restype = ctypes.c_char_p
 for _fn in ("uq_packed_size", "uq_pack_weights", "uq_import_gguf", "uq_gemv", "uq_gemm", "uq_dequant",
-            "uq_nf4_codebook", "uq_rope_table", "uq_rmsnorm_rope", "uq_gemv_a8", "uq_quantize_activations"):
+            "uq_nf4_codebook", "uq_rope_table", "uq_rmsnorm_rope", "uq_gemv_a8", "uq_quantize_activations",
+            "uq_gemm_workspace_size"):
     getattr(_lib, _fn).restype = ctypes.c_int
 
 EXPORTS = ("uq_packed_size", "uq_pack_weights", "uq_import_gguf", "uq_gemv", "uq_gemm", "uq_dequant",
            "uq_nf4_codebook", "uq_rope_table", "uq_rmsnorm_rope", "uq_gemv_a8", "uq_quantize_activations",
-           "uq_status_str")
+           "uq_gemm_workspace_size", "uq_status_str")
 
 
 def _check(fn: str, status: int):
@@ -87,14 +92,39 @@ def _check(fn: str, status: int):
         raise UQError(fn, status)
 
 
-def _ptr(obj) -> int | None:
+def _ptr(obj, what: str = "buffer", nbytes: int = 0, dtypes: tuple = ()) -> int | None:
+    """Device address of `obj`.  An int passes through unchecked; a tensor must
+    be on a GPU, contiguous, of one of `dtypes` (names such as "float16"; any
+    dtype when empty) and hold at least `nbytes` bytes."""
     if obj is None:
         return None
     if isinstance(obj, int):
         return obj
     if hasattr(obj, "data_ptr"):
+        if not getattr(obj, "is_cuda", False):
+            raise ValueError(f"{what}: expected a tensor on a GPU, got one on {getattr(obj, 'device', '?')}")
+        if dtypes and str(obj.dtype).replace("torch.", "") not in dtypes:
+            raise ValueError(f"{what}: dtype {obj.dtype} is not one of {', '.join(dtypes)}")
+        if not obj.is_contiguous():
+            raise ValueError(f"{what}: tensor is not contiguous")
+        have = obj.numel() * obj.element_size()
+        if have < nbytes:
+            raise ValueError(f"{what}: {have} bytes, the call needs {nbytes}")
         return obj.data_ptr()
     raise TypeError(f"expected a device pointer (int) or a tensor, got {type(obj)!r}")
+
+
+_U8 = ("uint8", "int8")
+_F16 = ("float16", "int16", "uint16")
+_F32 = ("float32",)
+
+
+def _product_ptrs(lay: Layout, codes, params, x, y, m: int):
+    """Checked addresses of a product's operands (sizes from the layout and m)."""
+    cb, pb = uq_packed_size(lay)
+    m = max(int(m), 0)
+    return (_ptr(codes, "codes", cb, _U8), _ptr(params, "params", pb, _F16 + ("int32",)),
+            _ptr(x, "x", m * lay.k * 2, _F16), _ptr(y, "y", m * lay.n * 4, _F32))
 
 
 def _stream(stream) -> int | None:
@@ -149,28 +179,54 @@ def uq_import_gguf(gguf_type: str | int, blocks: np.ndarray, n: int, k: int):
 
 
 def uq_gemv(lay: Layout, codes, params, x, y, m: int, stream=None) -> None:
-    _check("uq_gemv", _lib.uq_gemv(ctypes.byref(lay), _ptr(codes), _ptr(params), _ptr(x), _ptr(y),
+    _check("uq_gemv", _lib.uq_gemv(ctypes.byref(lay), *_product_ptrs(lay, codes, params, x, y, m),
                                    int(m), _stream(stream)))
 
 
-def uq_gemm(lay: Layout, codes, params, x, y, m: int, stream=None) -> None:
-    _check("uq_gemm", _lib.uq_gemm(ctypes.byref(lay), _ptr(codes), _ptr(params), _ptr(x), _ptr(y),
-                                   int(m), _stream(stream)))
+def uq_gemm_workspace_size(lay: Layout, m: int) -> int:
+    """Bytes of workspace uq_gemm needs for this layout and m (host call)."""
+    b = ctypes.c_size_t()
+    _check("uq_gemm_workspace_size", _lib.uq_gemm_workspace_size(ctypes.byref(lay), int(m), ctypes.byref(b)))
+    return b.value
+
+
+def gemm_workspace(lay: Layout, m: int, device="cuda"):
+    """A zero-filled uint8 device tensor of uq_gemm_workspace_size(lay, m) bytes
+    (torch allocates it; the library never does).  Reusable for later calls of
+    the same or smaller size on one stream."""
+    import torch
+    return torch.zeros(max(uq_gemm_workspace_size(lay, m), 1), dtype=torch.uint8, device=device)
+
+
+def uq_gemm(lay: Layout, codes, params, x, y, m: int, workspace, stream=None) -> None:
+    """workspace: a tensor (its size is passed along) or (address, bytes)."""
+    if isinstance(workspace, tuple):
+        wp, wb = int(workspace[0]), int(workspace[1])
+    else:
+        wp = _ptr(workspace, "workspace")
+        wb = workspace.numel() * workspace.element_size() if hasattr(workspace, "numel") else 0
+    _check("uq_gemm", _lib.uq_gemm(ctypes.byref(lay), *_product_ptrs(lay, codes, params, x, y, m), int(m),
+                                   wp, wb, _stream(stream)))
 
 
 def uq_gemv_a8(lay: Layout, codes, params, x, y, m: int, stream=None) -> None:
-    _check("uq_gemv_a8", _lib.uq_gemv_a8(ctypes.byref(lay), _ptr(codes), _ptr(params), _ptr(x), _ptr(y),
+    _check("uq_gemv_a8", _lib.uq_gemv_a8(ctypes.byref(lay), *_product_ptrs(lay, codes, params, x, y, m),
                                          int(m), _stream(stream)))
 
 
 def uq_quantize_activations(group: int, x, q, sx, m: int, k: int, stream=None) -> None:
-    _check("uq_quantize_activations", _lib.uq_quantize_activations(int(group), _ptr(x), _ptr(q), _ptr(sx),
-                                                                   int(m), int(k), _stream(stream)))
+    mk = max(int(m), 0) * max(int(k), 0)
+    groups = max(int(m), 0) * (max(int(k), 0) // int(group)) if int(group) > 0 else 0
+    _check("uq_quantize_activations", _lib.uq_quantize_activations(
+        int(group), _ptr(x, "x", 2 * mk, _F16), _ptr(q, "q", mk, ("int8",)), _ptr(sx, "sx", 4 * groups, _F32),
+        int(m), int(k), _stream(stream)))
 
 
 def uq_dequant(lay: Layout, codes, params, w, stream=None) -> None:
-    _check("uq_dequant", _lib.uq_dequant(ctypes.byref(lay), _ptr(codes), _ptr(params), _ptr(w),
-                                         _stream(stream)))
+    cb, pb = uq_packed_size(lay)
+    _check("uq_dequant", _lib.uq_dequant(ctypes.byref(lay), _ptr(codes, "codes", cb, _U8),
+                                         _ptr(params, "params", pb, _F16 + ("int32",)),
+                                         _ptr(w, "w", lay.n * lay.k * 4, _F32), _stream(stream)))
 
 
 def uq_rope_table(theta: float, head_dim: int, max_pos: int) -> tuple[np.ndarray, np.ndarray]:
@@ -185,9 +241,13 @@ def uq_rope_table(theta: float, head_dim: int, max_pos: int) -> tuple[np.ndarray
 def uq_rmsnorm_rope(x, y, gamma, pos, cos, sin, tokens: int, heads: int, head_dim: int, max_pos: int,
                     eps: float, stream=None) -> None:
     """Fused RMSNorm + RoPE on device buffers (x, y fp16 [tokens, heads, head_dim]; y may be x)."""
-    _check("uq_rmsnorm_rope", _lib.uq_rmsnorm_rope(_ptr(x), _ptr(y), _ptr(gamma), _ptr(pos), _ptr(cos),
-                                                   _ptr(sin), int(tokens), int(heads), int(head_dim),
-                                                   int(max_pos), float(eps), _stream(stream)))
+    vec = max(int(tokens), 0) * max(int(heads), 0) * max(int(head_dim), 0) * 2
+    tab = max(int(max_pos), 0) * max(int(head_dim), 0) // 2 * 4
+    _check("uq_rmsnorm_rope", _lib.uq_rmsnorm_rope(
+        _ptr(x, "x", vec, _F16), _ptr(y, "y", vec, _F16), _ptr(gamma, "gamma", 4 * max(int(head_dim), 0), _F32),
+        _ptr(pos, "pos", 4 * max(int(tokens), 0), ("int32",)), _ptr(cos, "cos", tab, _F32),
+        _ptr(sin, "sin", tab, _F32), int(tokens), int(heads), int(head_dim), int(max_pos), float(eps),
+        _stream(stream)))
 
 
 def uq_nf4_codebook() -> np.ndarray:

@@ -52,7 +52,9 @@ hipError_t launch(const uq_layout* L, const void* codes, const void* params, flo
   const uint8_t* c8 = static_cast<const uint8_t*>(codes);
   const uint8_t* p8 = static_cast<const uint8_t*>(params);
   void* args[] = {&c8, &p8, &w, &n_chunks, &chunks_per_row, &ng};
-  const dim3 grid(unsigned((n_chunks + 255) / 256)), block(256);
+  const int64_t blocks = (n_chunks + 255) / 256;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 grid{unsigned(blocks)}, block{256};
   return hipLaunchKernel(reinterpret_cast<const void*>(&dequant_kernel<S, G>), grid, block, args, 0, stream);
 }
 

@@ -44,8 +44,6 @@
 // the B side (any consistent assignment of k within an MFMA gives the same
 // dot product).
 #include <atomic>
-#include <mutex>
-#include <vector>
 
 #include "device_common.hpp"
 
@@ -58,7 +56,6 @@ constexpr int kKW = 32;          // k per wave per step: 16 codes per lane, two 
 constexpr int kSUB = kKW / 16;
 constexpr int kDC = 3;           // codes are copied this many steps ahead (from HBM: long latency)
 constexpr int kNC = kDC + 1;     // code buffers
-constexpr int kMaxSplit = 4;     // workgroups one tile's K steps may be split over
 
 // Groups per parameter window: at least 16, and enough that a window spans
 // kDC or more steps (the next window is copied kDC steps before it is used,
@@ -585,10 +582,10 @@ steps_done:
   auto out_row = [&](int a, int j) __attribute__((always_inline)) { return bm + a * 32 + 8 * (j / 4) + 4 * kh + (j % 4); };
   auto out_col = [&](int t) __attribute__((always_inline)) { return bn + wn * 64 + t * 32 + r32; };
 
-  // (Split only for row tiles up to 64: the summing pass keeps kMaxSplit
+  // (Split only for row tiles up to 64: the summing pass keeps kGemmMaxSplit
   // values of BM * BN / NT elements per thread in registers.)
   if constexpr (BM <= 64) if (ksplit > 1) {
-    // K split over ksplit (<= kMaxSplit) workgroups: each writes its partial
+    // K split over ksplit (<= kGemmMaxSplit) workgroups: each writes its partial
     // tile to part[split], and the last of the tile's workgroups to arrive
     // (counted with one device-scope atomic per tile) adds the ksplit partial
     // tiles in split order and stores y, so the sum does not depend on which
@@ -628,9 +625,9 @@ steps_done:
     // columns), issues the loads of every partial tile at once and then adds
     // them in split order.
     constexpr int E = BM * T::BN / T::NT;
-    float v[kMaxSplit][E];
+    float v[kGemmMaxSplit][E];
 #pragma unroll
-    for (int sp = 0; sp < kMaxSplit; ++sp) {
+    for (int sp = 0; sp < kGemmMaxSplit; ++sp) {
       const int spc = sp < ksplit ? sp : ksplit - 1;  // past ksplit: a valid address, value unused
       const float* src = part + (size_t(spc) * rows + size_t(bm)) * size_t(n);
 #pragma unroll
@@ -645,7 +642,7 @@ steps_done:
     for (int i = 0; i < E; ++i) {
       float sum = v[0][i];
 #pragma unroll
-      for (int sp = 1; sp < kMaxSplit; ++sp) sum = sp < ksplit ? sum + v[sp][i] : sum;
+      for (int sp = 1; sp < kGemmMaxSplit; ++sp) sum = sp < ksplit ? sum + v[sp][i] : sum;
       const int e = i * T::NT + tid;
       const int row = bm + e / T::BN, col = bn + e % T::BN;
       if (row < m && col < n) y[size_t(row) * size_t(n) + col] = sum;
@@ -682,103 +679,6 @@ __global__ __launch_bounds__(256) void to_bf16_kernel(const uint16_t* __restrict
   }
 }
 
-// GEMM workspace, one per (device, stream) so calls on different streams
-// never share it; calls on one stream are ordered by the stream.  It holds
-// the arrival counters of K-split tiles (zeroed once, when the buffer is
-// allocated; every call leaves them at zero again), the bf16 activations and
-// the partial tiles of a K split.  A buffer that is outgrown stays allocated
-// (a captured graph may still name it) until the process ends; growth is at
-// least 2x, so the retired buffers add up to less than the live one.
-struct Workspace {
-  int device;
-  hipStream_t stream;
-  void* ptr;
-  size_t bytes;
-};
-std::mutex g_ws_mutex;
-std::vector<Workspace> g_ws;
-std::vector<void*> g_ws_retired;
-
-hipError_t gemm_workspace(hipStream_t stream, size_t zeroed_bytes, size_t bytes, void** out) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  std::lock_guard<std::mutex> lock(g_ws_mutex);
-  Workspace* w = nullptr;
-  for (auto& it : g_ws)
-    if (it.device == dev && it.stream == stream) w = &it;
-  if (w && w->bytes >= bytes) {
-    *out = w->ptr;
-    return hipSuccess;
-  }
-  // No allocation while the stream is being captured into a graph.
-  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-  e = hipStreamIsCapturing(stream, &cap);
-  if (e != hipSuccess) return e;
-  if (cap != hipStreamCaptureStatusNone) return hipErrorStreamCaptureUnsupported;
-  size_t want = bytes < (size_t(1) << 20) ? (size_t(1) << 20) : bytes;
-  if (w && want < 2 * w->bytes) want = 2 * w->bytes;
-  void* p = nullptr;
-  e = hipMalloc(&p, want);
-  if (e != hipSuccess) return e;
-  e = hipMemsetAsync(p, 0, zeroed_bytes, stream);  // ordered before the first kernel that uses it
-  if (e != hipSuccess) {
-    (void)hipFree(p);
-    return e;
-  }
-  if (w) {
-    g_ws_retired.push_back(w->ptr);
-    w->ptr = p;
-    w->bytes = want;
-  } else {
-    g_ws.push_back(Workspace{dev, stream, p, want});
-  }
-  *out = p;
-  return hipSuccess;
-}
-
-// Tilings: 8 waves (two per SIMD); BM rows of x by BN = 64 * WGN weight
-// rows; up to 64 rows, the K steps of each tile split over ksplit
-// workgroups when the tiles alone would leave CUs idle.
-struct Plan {
-  int bm, wgn, ksplit;
-  bool xf;  // the GEMM stages the caller's fp16 x and rounds it to bf16 itself
-};
-
-// Tiles whose K split is summed by the last workgroup need one arrival
-// counter each; the workspace holds this many.
-constexpr int64_t kMaxSplitTiles = 16384;
-
-// The largest tile that fits M is the cheapest per output (each dequantized
-// fragment feeds BM / 32 M tiles) as long as the grid still gives at least
-// half of the 256 CUs a workgroup; a narrower weight matrix takes the next
-// smaller tile instead (N = 4096, M = 256: 64 workgroups of 128 rows took
-// 49.6 us, 256 of 64 rows 28.3 us; at N = 11008 the 172 large tiles beat 688
-// small ones, 47.8 against 64.8 us).  (A 256-row tile on 4 waves, one per
-// SIMD with the accumulators in AGPRs, halves the dequant work per MFMA but
-// measured slower: a lone wave per SIMD hides neither the copies' waits nor
-// the LDS latency.)
-//
-// Up to 64 rows a workgroup's time is mostly the latency of its K steps
-// (each waits for copies issued one or two steps earlier), so fewer steps
-// per workgroup help as long as the extra workgroups are resident at once:
-// ksplit = the workgroups the chip holds at once (CUs x workgroups per CU,
-// from the kernel's LDS and registers) over the tiles, at most kMaxSplit.
-// Measured per uq_gemm call: INT8 / INT2 at N = 4096, M = 64 (64 tiles, one
-// workgroup per CU) 27.1 / 25.4 us unsplit, 14.5 / 14.3 us in four; INT4 at
-// N = 11008 (172 tiles, one workgroup per CU with three activation buffers
-// in LDS) M = 16 16.4 us unsplit against 22.1 / 24.1 us in two / four, and
-// M = 64 22.6 us on 64-row tiles against 30.4 us on 344 tiles of 32 rows.
-constexpr int64_t kMinTiles = 128;
-
-Plan plan_gemm(int64_t m, int64_t n) {
-  auto tiles = [&](int bm, int bn) { return ((m + bm - 1) / bm) * ((n + bn - 1) / bn); };
-  if (m > 64 && tiles(128, 128) >= kMinTiles) return {128, 2, 1, false};
-  if (m > 64) return {64, 1, 1, false};
-  if (m > 32) return {64, 1, 1, true};
-  return {32, 1, 1, true};
-}
-
 // Workgroups of this kernel one CU holds at once (cached per kernel).
 template <int S, int G, int BM, int WGN, int NW, bool XF>
 int resident_per_cu() {
@@ -805,18 +705,20 @@ int device_cus() {
   return cus;
 }
 
-// K split for a plan: see above.  Row tiles of up to 64 only, at least two
-// K steps per workgroup.
+// K split for a plan (reasons with plan_gemm in uq_internal.h): ksplit = the
+// workgroups the chip holds at once (CUs x workgroups per CU, from the
+// kernel's LDS and registers) over the tiles, at most kGemmMaxSplit.  Row
+// tiles of up to 64 only, at least two K steps per workgroup.
 template <int S, int G>
-int plan_ksplit(const Plan& p, int64_t m, int64_t n, int64_t k) {
+int plan_ksplit(const GemmPlan& p, int64_t m, int64_t n, int64_t k) {
   if (m > 64 || p.bm > 64) return 1;
   const int64_t tiles = ((m + p.bm - 1) / p.bm) * ((n + 64 * p.wgn - 1) / (64 * p.wgn));
-  if (tiles > kMaxSplitTiles) return 1;
+  if (tiles > kGemmMaxSplitTiles) return 1;
   const int64_t ks_step = 32 * 8 / p.wgn;
   const int64_t steps = (k + ks_step - 1) / ks_step;
   const int per_cu = p.bm == 64 ? resident_per_cu<S, G, 64, 1, 8, true>() : resident_per_cu<S, G, 32, 1, 8, true>();
   int64_t ks = int64_t(device_cus()) * per_cu / tiles;
-  if (ks > kMaxSplit) ks = kMaxSplit;
+  if (ks > kGemmMaxSplit) ks = kGemmMaxSplit;
   if (ks > steps / 2) ks = steps / 2;
   return ks > 1 ? int(ks) : 1;
 }
@@ -839,7 +741,7 @@ hipError_t launch(const uq_layout* L, const void* codes, const void* params, con
 }
 
 template <int S, int G>
-hipError_t launch_plan(const Plan& p, const uq_layout* L, const void* codes, const void* params,
+hipError_t launch_plan(const GemmPlan& p, const uq_layout* L, const void* codes, const void* params,
                        const uint16_t* xb, float* y, int m, float* part, unsigned* arrivals, hipStream_t stream) {
   if (p.bm == 128) return launch<S, G, 128, 2, 8, false>(L, codes, params, xb, y, m, p.ksplit, part, arrivals, stream);
   if (p.bm == 64 && !p.xf) return launch<S, G, 64, 1, 8, false>(L, codes, params, xb, y, m, p.ksplit, part, arrivals, stream);
@@ -850,8 +752,8 @@ hipError_t launch_plan(const Plan& p, const uq_layout* L, const void* codes, con
 }  // namespace
 
 hipError_t launch_gemm(const uq_layout* L, const void* codes, const void* params, const uint16_t* x,
-                       float* y, int m, hipStream_t stream) {
-  Plan plan = plan_gemm(m, L->n);
+                       float* y, int m, void* workspace, hipStream_t stream) {
+  GemmPlan plan = plan_gemm(m, L->n);
 #define UQ_GEMM_CASE(SC, GR) \
   case SC * 1000 + GR: plan.ksplit = plan_ksplit<SC, GR>(plan, m, L->n, L->k); break;
   switch (L->scheme * 1000 + L->group) {
@@ -869,28 +771,23 @@ hipError_t launch_gemm(const uq_layout* L, const void* codes, const void* params
     default: return hipErrorInvalidValue;
   }
 #undef UQ_GEMM_CASE
-  const int64_t count = int64_t(m) * L->k;  // k % 32 == 0: whole 8-value pieces
-  // Workspace: [arrival counters][bf16 x, whole 128-row tiles, unless the
-  // GEMM reads the caller's fp16 x][partial tiles of a K split].  The GEMM
+  // The caller's workspace (validated to hold gemm_workspace(L, m).total
+  // bytes): arrival counters, bf16 x in whole 128-row tiles unless the GEMM
+  // reads the caller's fp16 x, and the partial tiles of a K split.  The GEMM
   // reads workspace rows past M without clamping (their products are never
   // stored).
-  const int64_t rows = (int64_t(m) + 127) / 128 * 128;
-  const size_t counter_bytes = size_t(kMaxSplitTiles) * 4;
-  const size_t act_bytes = plan.xf ? 0 : size_t(rows * L->k) * 2;
-  const size_t part_bytes =
-      plan.ksplit > 1 ? size_t(plan.ksplit) * size_t((m + plan.bm - 1) / plan.bm * plan.bm) * size_t(L->n) * 4 : 0;
-  void* ws = nullptr;
-  hipError_t e = gemm_workspace(stream, counter_bytes, counter_bytes + act_bytes + part_bytes, &ws);
-  if (e != hipSuccess) return e;
-  unsigned* arrivals = static_cast<unsigned*>(ws);
-  uint16_t* xb = plan.xf ? const_cast<uint16_t*>(x) : reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(ws) + counter_bytes);
-  float* part = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + counter_bytes + act_bytes);
+  const GemmWorkspace wl = gemm_workspace(L, m);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  unsigned* arrivals = reinterpret_cast<unsigned*>(ws + wl.counters);
+  uint16_t* xb = plan.xf ? const_cast<uint16_t*>(x) : reinterpret_cast<uint16_t*>(ws + wl.act);
+  float* part = reinterpret_cast<float*>(ws + wl.part);
   if (!plan.xf) {
-    int64_t count8 = count / 8;
+    int64_t count8 = int64_t(m) * L->k / 8;  // k % 32 == 0: whole 8-value pieces
     const int64_t want = (count8 + 255) / 256;
     const unsigned grid = unsigned(want < 1024 ? want : 1024);
     void* args[] = {(void*)&x, &xb, &count8};
-    e = hipLaunchKernel(reinterpret_cast<const void*>(&to_bf16_kernel), dim3(grid), dim3(256), args, 0, stream);
+    const hipError_t e =
+        hipLaunchKernel(reinterpret_cast<const void*>(&to_bf16_kernel), dim3(grid), dim3(256), args, 0, stream);
     if (e != hipSuccess) return e;
   }
 #define UQ_GEMM_CASE(SC, GR) \

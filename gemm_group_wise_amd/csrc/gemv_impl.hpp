@@ -463,8 +463,10 @@ hipError_t launch(const uq_layout* L, const void* codes, const void* params, con
   if (int64_t(MT) * (kb_max / Gm::GP) > int64_t(kMaxIPT) * kThreads) kb_max = kMaxIPT * kThreads * Gm::GP / MT;
   const size_t shmem = (Gm::NF ? 2048 : 0) + size_t(MT) * kb_max * 2 +
                        (Gm::NF ? 0 : size_t(MT) * (kb_max / Gm::GP) * 8);
-  const int rows_per_block = kWaves * R;
-  const dim3 grid(unsigned((n + rows_per_block - 1) / rows_per_block));
+  const int64_t rows_per_block = kWaves * R;
+  const int64_t blocks = (int64_t(n) + rows_per_block - 1) / rows_per_block;  // n < 2^31: no overflow in int64
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 grid{unsigned(blocks)};
   const uint8_t* c8 = static_cast<const uint8_t*>(codes);
   const uint8_t* p8 = static_cast<const uint8_t*>(params);
   void* args[] = {&c8, &p8, (void*)&x, &y, (void*)&n, (void*)&k, &m, &kb_max};

@@ -22,7 +22,9 @@ namespace {
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 template <int D>
-__global__ __launch_bounds__(256) void rmsnorm_rope_kernel(const uint16_t* __restrict__ x, uint16_t* y,
+// x and y may be the same buffer (in place): neither is declared __restrict__.
+// Each value is read once, before the lane that read it writes it.
+__global__ __launch_bounds__(256) void rmsnorm_rope_kernel(const uint16_t* x, uint16_t* y,
                                                            const float* __restrict__ gamma,
                                                            const int32_t* __restrict__ pos,
                                                            const float* __restrict__ cos_tab,

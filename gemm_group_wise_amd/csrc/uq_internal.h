@@ -62,6 +62,79 @@ inline size_t param_row_bytes(const uq_layout* L) {
   return size_t(L->k / L->group) * size_t(param_bytes_per_group(L->scheme));
 }
 
+// ---- GEMM plan and workspace (shared by the launcher and the host-side
+// validation, so the size a caller is told to allocate is the size used) ----
+
+constexpr int kGemmMaxSplit = 4;              // workgroups one tile's K steps may be split over
+constexpr int64_t kGemmMaxSplitTiles = 16384; // tiles that can have a K split (one counter each)
+constexpr int64_t kGemmMinTiles = 128;        // grids below this take the next smaller row tile
+
+// Tilings: 8 waves (two per SIMD); BM rows of x by BN = 64 * wgn weight rows.
+// The largest tile that fits M is the cheapest per output (each dequantized
+// fragment feeds BM / 32 M tiles) as long as the grid still gives at least
+// half of the 256 CUs a workgroup; a narrower weight matrix takes the next
+// smaller tile instead (N = 4096, M = 256: 64 workgroups of 128 rows took
+// 49.6 us, 256 of 64 rows 28.3 us; at N = 11008 the 172 large tiles beat 688
+// small ones, 47.8 against 64.8 us).  (A 256-row tile on 4 waves, one per
+// SIMD with the accumulators in AGPRs, halves the dequant work per MFMA but
+// measured slower: a lone wave per SIMD hides neither the copies' waits nor
+// the LDS latency.)  Up to 64 rows a workgroup's time is mostly the latency
+// of its K steps (each waits for copies issued one or two steps earlier), so
+// the K steps of a tile may be split over up to kGemmMaxSplit workgroups
+// (the launcher picks the count from the kernel's occupancy).  Measured per
+// call: INT8 / INT2 at N = 4096, M = 64 (64 tiles) 27.1 / 25.4 us unsplit,
+// 14.5 / 14.3 us in four; INT4 at N = 11008 (172 tiles, one workgroup per CU)
+// M = 16 16.4 us unsplit against 22.1 / 24.1 us in two / four, and M = 64
+// 22.6 us on 64-row tiles against 30.4 us on 344 tiles of 32 rows.
+struct GemmPlan {
+  int bm, wgn, ksplit;
+  bool xf;  // the GEMM stages the caller's fp16 x and rounds it to bf16 itself
+};
+
+inline GemmPlan plan_gemm(int64_t m, int64_t n) {
+  auto tiles = [&](int64_t bm, int64_t bn) { return ((m + bm - 1) / bm) * ((n + bn - 1) / bn); };
+  if (m > 64 && tiles(128, 128) >= kGemmMinTiles) return {128, 2, 1, false};
+  if (m > 64) return {64, 1, 1, false};
+  if (m > 32) return {64, 1, 1, true};
+  return {32, 1, 1, true};
+}
+
+// Byte offsets of the regions of a uq_gemm workspace and its total size.
+// Regions start on 256-byte boundaries.  The partial tiles are sized for the
+// largest K split (kGemmMaxSplit), so the size does not depend on the device.
+struct GemmWorkspace {
+  size_t counters;  // kGemmMaxSplitTiles uint32 arrival counters (zero between calls)
+  size_t act;       // bf16 x [m rounded up to 128][k] (empty when the GEMM reads fp16 x)
+  size_t part;      // fp32 partial tiles [kGemmMaxSplit][m rounded up to the row tile][n]
+  size_t total;
+};
+
+inline GemmWorkspace gemm_workspace(const uq_layout* L, int64_t m) {
+  auto up = [](size_t v) { return (v + 255) / 256 * 256; };
+  const GemmPlan p = plan_gemm(m, L->n);
+  GemmWorkspace w;
+  w.counters = 0;
+  w.act = up(size_t(kGemmMaxSplitTiles) * 4);
+  const size_t act_bytes = p.xf ? 0 : size_t((m + 127) / 128 * 128) * size_t(L->k) * 2;
+  w.part = up(w.act + act_bytes);
+  const size_t part_bytes =
+      p.bm <= 64 ? size_t(kGemmMaxSplit) * size_t((m + p.bm - 1) / p.bm * p.bm) * size_t(L->n) * 4 : 0;
+  w.total = up(w.part + part_bytes);
+  return w;
+}
+
+// ---- Argument checks of the device entry points (uq_check.cpp; host only,
+// no HIP call) ----
+uq_status check_product(const uq_layout* L, const void* codes, const void* params, const void* x,
+                        const void* y, int64_t m, int64_t mmax);
+uq_status check_gemm_workspace(const uq_layout* L, int64_t m, const void* workspace, size_t bytes);
+uq_status check_dequant(const uq_layout* L, const void* codes, const void* params, const void* w);
+uq_status check_quantize_activations(int32_t group, const void* x, const void* q, const void* sx, int64_t m,
+                                     int64_t k);
+uq_status check_rmsnorm_rope(const void* x, const void* y, const void* gamma, const void* pos, const void* cos,
+                             const void* sin, int64_t tokens, int32_t heads, int32_t head_dim, int64_t max_pos,
+                             float eps);
+
 // Host packer (uq_pack.cpp).
 uq_status pack_weights(const uq_layout* L, const float* w, uint8_t* codes,
                        uint16_t* params);

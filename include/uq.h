@@ -39,8 +39,9 @@
  *   - The caller owns every buffer it passes.  Calls never synchronize:
  *     device work is enqueued on `stream` (a hipStream_t; NULL means the null
  *     stream) and the call returns at once.  Faults inside a kernel surface
- *     at the caller's next synchronization.  Only uq_gemm allocates (see
- *     there); every other call allocates nothing and keeps no state.
+ *     at the caller's next synchronization.  No call allocates device
+ *     memory or keeps state between calls; uq_gemm works in a workspace the
+ *     caller provides (see there).
  *   - Outputs are overwritten, never accumulated into.
  *   - All functions are thread-safe.
  */
@@ -62,7 +63,8 @@ typedef enum uq_status {
   UQ_ERR_UNSUPPORTED = 3, /* unknown scheme or unsupported (scheme, group)   */
   UQ_ERR_ALIGN = 4,       /* a device pointer is not suitably aligned        */
   UQ_ERR_RANGE = 5,       /* a weight is NaN, infinite, or |w| > 65504       */
-  UQ_ERR_HIP = 6          /* the HIP runtime rejected a kernel launch        */
+  UQ_ERR_HIP = 6,         /* the HIP runtime rejected a kernel launch        */
+  UQ_ERR_WORKSPACE = 7    /* a workspace is smaller than the call needs      */
 } uq_status;
 
 typedef enum uq_scheme {
@@ -112,30 +114,35 @@ uq_status uq_gemv(const uq_layout* layout, const void* codes,
                   const void* params, const uint16_t* x, float* y, int64_t m,
                   void* stream);
 
+/* Bytes of device workspace uq_gemm needs for `layout` and m activation rows
+ * (0 < m <= UQ_GEMM_MAX_M).  Host call; the size depends on (layout, m) only,
+ * not on the device.  Errors as for uq_packed_size, UQ_ERR_SHAPE for m. */
+uq_status uq_gemm_workspace_size(const uq_layout* layout, int64_t m, size_t* bytes);
+
 /* Fused dequant + GEMM on the bf16 matrix cores for batched decode and
  * prefill (Core Components > Fused Kernels, GEMM during batched decode):
  *   y[m][n] = sum_k bf16(x[m][k]) * bf16(w'[n][k])  for 1 <= m <= UQ_GEMM_MAX_M
  * Both casts round to nearest even; products accumulate in fp32, in an order
  * fixed by (layout, m), so repeated calls give identical bits.
- * Arguments as for uq_gemv.
- * For m <= 64 the K dimension is split over several workgroups per output
- * tile; the last of them to finish adds the partial tiles in a fixed order,
- * so results stay bitwise repeatable.
- * Workspace: device memory the library owns, one buffer per (device,
- * stream), holding 64 KiB of arrival counters (zeroed when the buffer is
- * allocated; every call leaves them zero), bf16(x) as m' * k * 2 bytes with
- * m' = m rounded up to a multiple of 128, and for a K split its partial
- * tiles (at most 8 * m'' * n * 4 bytes, m'' = m rounded up to the row tile).
- * It is allocated with hipMalloc by the first call that needs it to be
- * larger (at least doubling) and kept until the process ends.  Calls on one
- * stream are ordered by the stream; calls on different streams use
- * different buffers.  A call that would have to grow the buffer while
- * `stream` is being captured into a graph returns UQ_ERR_HIP without
- * launching: make one call of the largest m * k (and m * n) on that stream
- * before capturing. */
-uq_status uq_gemm(const uq_layout* layout, const void* codes,
-                  const void* params, const uint16_t* x, float* y, int64_t m,
-                  void* stream);
+ * codes, params, x, y as for uq_gemv.
+ * workspace : device memory owned by the caller, 256-byte aligned, of at
+ *   least uq_gemm_workspace_size(layout, m) bytes (workspace_bytes says how
+ *   many it has; fewer gives UQ_ERR_WORKSPACE, NULL UQ_ERR_NULL, misaligned
+ *   UQ_ERR_ALIGN).  It must hold zeros before its first use with uq_gemm
+ *   (allocate it zero-filled once); every call leaves it fit for the next
+ *   one (the arrival counters it keeps in its first 64 KiB back at zero), so
+ *   it is not cleared per call.  It holds bf16(x) for m > 64 and, for
+ *   m <= 64, where the K dimension of a tile may be split over several
+ *   workgroups, their partial tiles and arrival counters; the last
+ *   workgroup of a tile adds the partial tiles in a fixed order, so results
+ *   stay bitwise repeatable.  Calls that share a workspace must be ordered
+ *   (e.g. issued to one stream); calls that may run concurrently need
+ *   different workspaces.  Nothing else may write the workspace between
+ *   calls.  A call may be captured into a HIP graph: it launches kernels
+ *   only. */
+uq_status uq_gemm(const uq_layout* layout, const void* codes, const void* params,
+                  const uint16_t* x, float* y, int64_t m, void* workspace,
+                  size_t workspace_bytes, void* stream);
 
 /* Dequantize the whole matrix (the matching dequantizer of
  * Core Components > Quantization):  w[n][k] = w' exactly (bit for bit).

@@ -51,7 +51,7 @@ __all__ = [
     "dequant_int", "quantize_nf4", "dequant_nf4", "pack_codes", "unpack_codes",
     "pack_params_int", "unpack_params_int", "pack_params_nf4",
     "unpack_params_nf4", "quantize_pack", "dequant_packed", "gemv_ref",
-    "bf16_rne", "gemm_ref", "dot_exact", "NF4_PSTAR",
+    "bf16_rne", "gemm_ref", "NF4_PSTAR",
 ]
 
 # Scheme names and widths (Ultra LLM Engine, Highlights table, Quantization
@@ -257,13 +257,3 @@ def gemm_ref(x16: np.ndarray, wdq: np.ndarray) -> np.ndarray:
     xb = bf16_rne(x16.astype(np.float32)).astype(np.float64)
     wb = bf16_rne(wdq).astype(np.float64)
     return xb @ wb.T
-
-
-def dot_exact(x16: np.ndarray, wdq: np.ndarray) -> list:
-    """Exact rational y[m][n] by brute force; for tiny shapes only (k <= 64)."""
-    m, k = x16.shape
-    n = wdq.shape[0]
-    xf = [[Fraction(float(v)) for v in row] for row in x16.astype(np.float64)]
-    wf = [[Fraction(float(v)) for v in row] for row in wdq.astype(np.float64)]
-    return [[sum(xf[i][j] * wf[c][j] for j in range(k)) for c in range(n)]
-            for i in range(m)]

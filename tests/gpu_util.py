@@ -52,6 +52,14 @@ class Guarded:
         return out
 
 
+def product(lib, fn, lay, codes, params, x, y, m, stream=None):
+    """Call uq_gemv / uq_gemm / uq_gemv_a8; uq_gemm gets a fresh zero-filled workspace."""
+    if fn == "uq_gemm":
+        lib.uq_gemm(lay, codes, params, x, y, m, lib.gemm_workspace(lay, m), stream=stream)
+    else:
+        getattr(lib, fn)(lay, codes, params, x, y, m, stream=stream)
+
+
 def packed_on_device(lib, scheme, group, w):
     """Pack with the library's host packer and copy to the GPU."""
     lay = lib.layout(scheme, group, w.shape[0], w.shape[1])

@@ -139,6 +139,17 @@ def test_layout_errors(lib):
     assert lib.raw_call("uq_packed_size", None, None, None) == 1
 
 
+def test_largest_layout_sizes(lib):
+    """n = 2^31 - 1 rows (the largest accepted) at the largest k: sizes are formed
+    in 64 bits on the host (no int overflow on the way to a grid or a byte count)."""
+    n, k = 0x7FFFFFFF, 1 << 24
+    for scheme, group, bits, pbytes in (("int4", 64, 4, 4), ("int2", 16, 2, 4), ("nf4", 64, 4, 2)):
+        cb, pb = lib.uq_packed_size(lib.layout(scheme, group, n, k))
+        assert cb == n * k * bits // 8 and pb == n * (k // group) * pbytes
+    lay = lib.layout("int4", 128, n, 4096)
+    assert lib.uq_gemm_workspace_size(lay, 64) == (65536 + 4 * 64 * n * 4 + 255) // 256 * 256
+
+
 def test_pack_rejects_non_finite_and_huge(lib):
     lay = lib.layout("int4", 32, 2, 64)
     for bad in (np.nan, np.inf, -np.inf, 65505.0, -70000.0):
@@ -157,19 +168,133 @@ def test_product_validation(lib, fn):
     lay = lib.layout("int4", 64, 128, 256)
     A = 1 << 20  # fake, 16-byte aligned addresses: never dereferenced
     s = ctypes.byref
-    assert lib.raw_call(fn, None, A, A, A, A, 1, None) == 1                      # null layout
-    assert lib.raw_call(fn, s(lay), None, A, A, A, 1, None) == 1                 # null codes
-    assert lib.raw_call(fn, s(lay), A, A, A, None, 1, None) == 1                 # null y
-    assert lib.raw_call(fn, s(lay), A, A, A, A, 0, None) == 2                    # m = 0
+    # uq_gemm takes (workspace, bytes) before the stream: a valid, large enough pair
+    tail = (A, 1 << 40, None) if fn == "uq_gemm" else (None,)
+    call = lambda *a: lib.raw_call(fn, *a, *tail)  # noqa: E731
+    assert call(None, A, A, A, A, 1) == 1                      # null layout
+    assert call(s(lay), None, A, A, A, 1) == 1                 # null codes
+    assert call(s(lay), A, A, A, None, 1) == 1                 # null y
+    assert call(s(lay), A, A, A, A, 0) == 2                    # m = 0
     mmax = 8 if fn in ("uq_gemv", "uq_gemv_a8") else 65536
-    assert lib.raw_call(fn, s(lay), A, A, A, A, mmax + 1, None) == 2             # m too big
-    assert lib.raw_call(fn, s(lay), A + 4, A, A, A, 1, None) == 4                # misaligned
-    assert lib.raw_call(fn, s(lay), A, A, A + 2, A, 1, None) == 4
-    assert lib.raw_call(fn, s(lay), A, A, A, A + 8, 1, None) == 4
+    assert call(s(lay), A, A, A, A, mmax + 1) == 2             # m too big
+    assert call(s(lay), A + 4, A, A, A, 1) == 4                # misaligned
+    assert call(s(lay), A, A, A + 2, A, 1) == 4
+    assert call(s(lay), A, A, A, A + 8, 1) == 4
     bad = lib.layout("int4", 64, 128, 96)
-    assert lib.raw_call(fn, s(bad), A, A, A, A, 1, None) == 2
+    assert call(s(bad), A, A, A, A, 1) == 2
     badg = lib.layout("int4", 16, 128, 256)
-    assert lib.raw_call(fn, s(badg), A, A, A, A, 1, None) == 3
+    assert call(s(badg), A, A, A, A, 1) == 3
+
+
+@pytest.mark.parametrize("m", [1, 16, 33, 64, 65, 256, 4097])
+def test_gemm_workspace_validation(lib, m):
+    """A missing, misaligned or short workspace is refused before any HIP call."""
+    lay = lib.layout("int4", 128, 11008, 4096)
+    A = 1 << 20
+    need = lib.uq_gemm_workspace_size(lay, m)
+    assert need > 0 and need % 256 == 0
+    call = lambda ws, b: lib.raw_call("uq_gemm", ctypes.byref(lay), A, A, A, A, m, ws, b, None)  # noqa: E731
+    assert call(None, need) == 1                                 # UQ_ERR_NULL
+    assert call(A + 16, need) == 4                               # UQ_ERR_ALIGN (256-byte)
+    assert call(A + 128, need) == 4
+    assert call(A, need - 1) == 7                                # UQ_ERR_WORKSPACE
+    assert call(A, 0) == 7
+    assert lib.uq_status_str(7) == "UQ_ERR_WORKSPACE"
+
+
+def test_gemm_workspace_size(lib):
+    """Sizes follow the documented regions: 64 KiB of counters, bf16 x in whole
+    128-row tiles for m > 64, and four partial tiles of fp32 outputs for m <= 64."""
+    n, k = 11008, 4096
+    lay = lib.layout("int4", 128, n, k)
+    up = lambda v: (v + 255) // 256 * 256  # noqa: E731
+    assert lib.uq_gemm_workspace_size(lay, 16) == up(65536 + 4 * 32 * n * 4)
+    assert lib.uq_gemm_workspace_size(lay, 64) == up(65536 + 4 * 64 * n * 4)
+    assert lib.uq_gemm_workspace_size(lay, 256) == up(65536 + 256 * k * 2)
+    assert lib.uq_gemm_workspace_size(lay, 300) == up(65536 + 384 * k * 2)
+    for bad in (0, -1, 65537):
+        with pytest.raises(lib.UQError) as e:
+            lib.uq_gemm_workspace_size(lay, bad)
+        assert e.value.name == "UQ_ERR_SHAPE"
+    with pytest.raises(lib.UQError):
+        lib.uq_gemm_workspace_size(lib.layout("int4", 16, n, k), 16)
+    assert lib.raw_call("uq_gemm_workspace_size", ctypes.byref(lay), 16, None) == 1
+
+
+class _FakeTensor:
+    """Stands in for a device tensor in the binding's argument checks (never passed on)."""
+
+    def __init__(self, nbytes, dtype="float16", is_cuda=True, contiguous=True):
+        import torch
+        self.dtype = getattr(torch, dtype)
+        self.is_cuda = is_cuda
+        self.device = "cuda:0" if is_cuda else "cpu"
+        self._contig = contiguous
+        self._size = torch.empty(0, dtype=self.dtype).element_size()
+        self._n = nbytes // self._size
+
+    def data_ptr(self):
+        return 1 << 20
+
+    def is_contiguous(self):
+        return self._contig
+
+    def numel(self):
+        return self._n
+
+    def element_size(self):
+        return self._size
+
+
+def test_binding_rejects_bad_tensors_before_the_call(lib):
+    """CPU tensors, wrong dtypes, strided views and short buffers raise ValueError
+    in the binding; none of them reaches the library."""
+    import torch
+    lay = lib.layout("int4", 64, 128, 256)
+    cb, pb = lib.uq_packed_size(lay)
+    m = 4
+    good = dict(codes=_FakeTensor(cb, "uint8"), params=_FakeTensor(pb, "int16"),
+                x=_FakeTensor(m * 256 * 2, "float16"), y=_FakeTensor(m * 128 * 4, "float32"))
+
+    def args(**kw):
+        a = dict(good)
+        a.update(kw)
+        return a["codes"], a["params"], a["x"], a["y"]
+
+    cases = [dict(codes=torch.zeros(cb, dtype=torch.uint8)),                 # host tensor
+             dict(codes=_FakeTensor(cb - 1, "uint8")),                       # short codes
+             dict(params=_FakeTensor(pb - 2, "int16")),                      # short params
+             dict(x=_FakeTensor(m * 256 * 2 - 2, "float16")),                # x shorter than m * k
+             dict(x=_FakeTensor(m * 256 * 4, "float32")),                    # x not fp16
+             dict(y=_FakeTensor(m * 128 * 2, "float16")),                    # y fp16, not fp32
+             dict(y=_FakeTensor(m * 128 * 4 - 4, "float32")),                # y shorter than m * n
+             dict(y=_FakeTensor(m * 128 * 4, "float32", contiguous=False))]  # strided
+    for fn in ("uq_gemv", "uq_gemv_a8"):
+        for kw in cases:
+            with pytest.raises(ValueError):
+                getattr(lib, fn)(lay, *args(**kw), m, stream=0)
+    ws = _FakeTensor(lib.uq_gemm_workspace_size(lay, m), "uint8")
+    for kw in cases:
+        with pytest.raises(ValueError):
+            lib.uq_gemm(lay, *args(**kw), m, ws, stream=0)
+    with pytest.raises(ValueError):
+        lib.uq_dequant(lay, good["codes"], good["params"], _FakeTensor(128 * 256 * 4 - 4, "float32"), stream=0)
+    with pytest.raises(ValueError):
+        lib.uq_quantize_activations(64, good["x"], _FakeTensor(m * 256, "uint8"), _FakeTensor(64, "float32"),
+                                    m, 256, stream=0)
+
+
+def test_binding_passes_the_workspace_size(lib):
+    """A workspace tensor's byte count reaches the library: a short one is refused there."""
+    lay = lib.layout("int4", 64, 128, 256)
+    cb, pb = lib.uq_packed_size(lay)
+    need = lib.uq_gemm_workspace_size(lay, 16)
+    with pytest.raises(lib.UQError) as e:
+        lib.uq_gemm(lay, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 16, _FakeTensor(need - 256, "uint8"), stream=0)
+    assert e.value.name == "UQ_ERR_WORKSPACE"
+    with pytest.raises(lib.UQError) as e:
+        lib.uq_gemm(lay, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 16, ((1 << 20) + 64, need), stream=0)
+    assert e.value.name == "UQ_ERR_ALIGN"
 
 
 def test_gemv_a8_rejects_nf4(lib):

@@ -9,7 +9,7 @@ import pytest
 
 import oracle as o
 import workloads
-from tests.gpu_util import Guarded, dev, gate, note, oracle_dequant, packed_on_device
+from tests.gpu_util import Guarded, dev, gate, note, oracle_dequant, packed_on_device, product
 
 pytestmark = pytest.mark.gpu
 
@@ -26,7 +26,7 @@ def gpu():
 
 def run(lib, fn, lay, codes, params, x, m):
     y = Guarded(m * lay.n)
-    getattr(lib, fn)(lay, codes, params, dev(x[:m]), y.ptr, m)
+    product(lib, fn, lay, codes, params, dev(x[:m]), y.ptr, m)
     return y.result().reshape(m, lay.n)
 
 

@@ -10,7 +10,7 @@ import pytest
 
 import oracle as o
 import workloads
-from tests.gpu_util import Guarded, dev, gate, note
+from tests.gpu_util import Guarded, dev, gate, note, product
 
 pytestmark = pytest.mark.gpu
 
@@ -36,7 +36,7 @@ def imported(lib, t, n, k, seed, dmax=0.01):
 
 def run(lib, fn, lay, codes, params, x, m):
     y = Guarded(m * lay.n)
-    getattr(lib, fn)(lay, codes, params, dev(x[:m]), y.ptr, m)
+    product(lib, fn, lay, codes, params, dev(x[:m]), y.ptr, m)
     return y.result().reshape(m, lay.n)
 
 

@@ -38,9 +38,9 @@ def run_gemv(lib, lay, codes, params, x, m):
     return y.result().reshape(m, lay.n)
 
 
-def run_gemm(lib, lay, codes, params, x, m):
+def run_gemm(lib, lay, codes, params, x, m, ws=None):
     y = Guarded(m * lay.n)
-    lib.uq_gemm(lay, codes, params, dev(x[:m]), y.ptr, m)
+    lib.uq_gemm(lay, codes, params, dev(x[:m]), y.ptr, m, lib.gemm_workspace(lay, m) if ws is None else ws)
     return y.result().reshape(m, lay.n)
 
 
@@ -291,38 +291,41 @@ def test_gemm_deterministic(lib):
 
 
 def test_gemm_graph_replay(lib):
-    """A call captured in a HIP graph (after a warm-up call on the capture
-    stream, which sizes the activation workspace) replays the eager result,
-    replay after replay, with eager work on the same buffers in between.
+    """A call captured into a HIP graph on a fresh stream, with no call made
+    before the capture, replays the eager result bit for bit, replay after
+    replay, with eager work on the same buffers and workspace in between.
     N = 384 makes six tiles, so K is split over two workgroups per tile: the
     replays also check that each call leaves the arrival counters at zero."""
     import torch
     w, x = workloads.make_random(384, 1024, 64, seed=17)
     lay, codes, params = packed_on_device(lib, "int4", 64, w)
+    wdq = oracle_dequant(w, "int4", 64)
     xd = dev(x)
     y = torch.empty(64 * 384, dtype=torch.float32, device="cuda")
+    ws = lib.gemm_workspace(lay, 64)
     torch.cuda.synchronize()
     s = torch.cuda.Stream()
-    note("gemm graph: warm-up and capture")
-    with torch.cuda.stream(s):
-        lib.uq_gemm(lay, codes, params, xd, y, 64, stream=s.cuda_stream)
-    s.synchronize()
-    want = y.cpu().numpy().copy()
     g = torch.cuda.CUDAGraph()
+    note("gemm graph: capture on a fresh stream")
     with torch.cuda.graph(g, stream=s):
-        lib.uq_gemm(lay, codes, params, xd, y, 64, stream=s.cuda_stream)
+        lib.uq_gemm(lay, codes, params, xd, y, 64, ws, stream=s.cuda_stream)
+    want = None
     for r in range(4):
         note(f"gemm graph: replay {r}")
         y.fill_(float("nan"))
         g.replay()
         torch.cuda.synchronize()
-        assert np.array_equal(y.cpu().numpy().view(np.uint32), want.view(np.uint32)), r
-        lib.uq_gemm(lay, codes, params, xd, y, 16)  # eager work in between
+        got = y.cpu().numpy().copy()
+        if want is None:
+            want = run_gemm(lib, lay, codes, params, x, 64)
+            gate(want, o.gemm_ref(x, wdq), o.bf16_rne(x.astype(np.float32)), o.bf16_rne(wdq), "graph eager")
+        assert np.array_equal(got.view(np.uint32), want.reshape(-1).view(np.uint32)), r
+        lib.uq_gemm(lay, codes, params, xd, y, 16, ws)  # eager work in between, same workspace
         torch.cuda.synchronize()
 
 
 def test_gemm_two_streams(lib):
-    """Concurrent calls on two streams use separate workspaces."""
+    """Concurrent calls on two streams, each with its own workspace."""
     import torch
     w, x = workloads.make_random(512, 2048, 200, seed=18)
     lay, codes, params = packed_on_device(lib, "int4", 128, w)
@@ -331,15 +334,31 @@ def test_gemm_two_streams(lib):
     xa, xb = dev(x), dev(x[100:])
     ya = torch.empty(200 * 512, dtype=torch.float32, device="cuda")
     yb = torch.empty(100 * 512, dtype=torch.float32, device="cuda")
+    wa, wb = lib.gemm_workspace(lay, 200), lib.gemm_workspace(lay, 100)
     torch.cuda.synchronize()
     s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
     note("gemm two streams")
     for _ in range(3):
-        lib.uq_gemm(lay, codes, params, xa, ya, 200, stream=s1.cuda_stream)
-        lib.uq_gemm(lay, codes, params, xb, yb, 100, stream=s2.cuda_stream)
+        lib.uq_gemm(lay, codes, params, xa, ya, 200, wa, stream=s1.cuda_stream)
+        lib.uq_gemm(lay, codes, params, xb, yb, 100, wb, stream=s2.cuda_stream)
     torch.cuda.synchronize()
     assert np.array_equal(ya.cpu().numpy().reshape(200, 512).view(np.uint32), want_a.view(np.uint32))
     assert np.array_equal(yb.cpu().numpy().reshape(100, 512).view(np.uint32), want_b.view(np.uint32))
+
+
+def test_gemm_workspace_reused_across_sizes(lib):
+    """One workspace sized for the largest call serves smaller and split calls in
+    turn on one stream (the counters are back at zero after each call)."""
+    import torch
+    w, x = workloads.make_random(700, 2048, 256, seed=19)
+    lay, codes, params = packed_on_device(lib, "int4", 128, w)
+    big = max(lib.uq_gemm_workspace_size(lay, m) for m in (1, 16, 64, 256))
+    ws = torch.zeros(big, dtype=torch.uint8, device="cuda")
+    for m in (64, 1, 256, 16, 64):
+        note(f"gemm shared workspace m={m}")
+        got = run_gemm(lib, lay, codes, params, x, m, ws=ws)
+        want = run_gemm(lib, lay, codes, params, x, m)
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), m
 
 
 # ---------------------------------------------------------------------------
