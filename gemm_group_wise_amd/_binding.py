@@ -67,6 +67,7 @@ _lib.uq_pack_weights.argtypes = [_L, _P, _P, _P]
 _lib.uq_import_gguf.argtypes = [ctypes.c_int32, _P, ctypes.c_int64, ctypes.c_int64, _L, _P, _P]
 _lib.uq_gemv.argtypes = [_L, _P, _P, _P, _P, ctypes.c_int64, _P]
 _lib.uq_gemm.argtypes = [_L, _P, _P, _P, _P, ctypes.c_int64, _P, ctypes.c_size_t, _P]
+_lib.uq_gemm_noalloc.argtypes = [_L, _P, _P, _P, _P, ctypes.c_int64, _P]
 _lib.uq_gemm_workspace_size.argtypes = [_L, ctypes.c_int64, ctypes.POINTER(ctypes.c_size_t)]
 _lib.uq_dequant.argtypes = [_L, _P, _P, _P, _P]
 _lib.uq_gemv_a8.argtypes = [_L, _P, _P, _P, _P, ctypes.c_int64, _P]
@@ -79,12 +80,13 @@ _lib.uq_status_str.argtypes = [ctypes.c_int]
 _lib.uq_status_str.restype = ctypes.c_char_p
 for _fn in ("uq_packed_size", "uq_pack_weights", "uq_import_gguf", "uq_gemv", "uq_gemm", "uq_dequant",
             "uq_nf4_codebook", "uq_rope_table", "uq_rmsnorm_rope", "uq_gemv_a8", "uq_quantize_activations",
-            "uq_gemm_workspace_size"):
+            "uq_gemm_workspace_size", "uq_gemm_noalloc"):
     getattr(_lib, _fn).restype = ctypes.c_int
 
 EXPORTS = ("uq_packed_size", "uq_pack_weights", "uq_import_gguf", "uq_gemv", "uq_gemm", "uq_dequant",
            "uq_nf4_codebook", "uq_rope_table", "uq_rmsnorm_rope", "uq_gemv_a8", "uq_quantize_activations",
-           "uq_gemm_workspace_size", "uq_status_str")
+           "uq_gemm_workspace_size", "uq_gemm_noalloc", "uq_status_str")
+GEMM_NOALLOC_MAX_BYTES = 32 << 20
 
 
 def _check(fn: str, status: int):
@@ -207,6 +209,13 @@ def uq_gemm(lay: Layout, codes, params, x, y, m: int, workspace, stream=None) ->
         wb = workspace.numel() * workspace.element_size() if hasattr(workspace, "numel") else 0
     _check("uq_gemm", _lib.uq_gemm(ctypes.byref(lay), *_product_ptrs(lay, codes, params, x, y, m), int(m),
                                    wp, wb, _stream(stream)))
+
+
+def uq_gemm_noalloc(lay: Layout, codes, params, x, y, m: int, stream=None) -> None:
+    """uq_gemm in the library's fixed per-GPU scratch (no workspace argument;
+    calls on one GPU must not overlap)."""
+    _check("uq_gemm_noalloc", _lib.uq_gemm_noalloc(ctypes.byref(lay), *_product_ptrs(lay, codes, params, x, y, m),
+                                                   int(m), _stream(stream)))
 
 
 def uq_gemv_a8(lay: Layout, codes, params, x, y, m: int, stream=None) -> None:

@@ -44,6 +44,7 @@
 // the B side (any consistent assignment of k within an MFMA gives the same
 // dot product).
 #include <atomic>
+#include <mutex>
 
 #include "device_common.hpp"
 
@@ -750,6 +751,53 @@ hipError_t launch_plan(const GemmPlan& p, const uq_layout* L, const void* codes,
 }
 
 }  // namespace
+
+// ---- Fixed scratch for uq_gemm_noalloc (callers that cannot allocate) ----
+//
+// One file-scope device array per GPU the library runs on, held until the
+// process ends.  In host code the array's name is not a device address: its
+// address on each device comes from hipGetSymbolAddress, taken once per
+// device (with that device current) and kept; only that pointer is passed to
+// kernels.  Every uq_gemm_noalloc call on a device shares the array, so such
+// calls must not overlap on one device.
+static __device__ __align__(256) uint8_t scratch[kGemmScratchBytes];
+
+// Zero `words` 16-byte words at p (the arrival counters, once per device).
+__global__ __launch_bounds__(256) void zero_kernel(uint4* __restrict__ p, int64_t words) {
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i < words) p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch[kMaxDevices];  // per device: the array's device address, once initialised
+}  // namespace
+
+hipError_t gemm_scratch(hipStream_t stream, void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    // The counters must start at zero (each call leaves them so); clear them
+    // once, by a kernel on the call's stream, ahead of the first GEMM.
+    int64_t words = int64_t(kGemmMaxSplitTiles) * 4 / 16;
+    uint4* p = static_cast<uint4*>(ptr);
+    void* args[] = {&p, &words};
+    e = hipLaunchKernel(reinterpret_cast<const void*>(&zero_kernel), dim3(unsigned((words + 255) / 256)), dim3(256),
+                        args, 0, stream);
+    if (e != hipSuccess) return e;
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_gemm(const uq_layout* L, const void* codes, const void* params, const uint16_t* x,
                        float* y, int m, void* workspace, hipStream_t stream) {

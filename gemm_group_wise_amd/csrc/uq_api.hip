@@ -11,6 +11,7 @@ hipError_t launch_gemv(const uq_layout* L, const void* codes, const void* params
                        float* y, int m, hipStream_t stream);
 hipError_t launch_gemm(const uq_layout* L, const void* codes, const void* params, const uint16_t* x,
                        float* y, int m, void* workspace, hipStream_t stream);
+hipError_t gemm_scratch(hipStream_t stream, void** out);
 hipError_t launch_dequant(const uq_layout* L, const void* codes, const void* params, float* w,
                           hipStream_t stream);
 hipError_t launch_gemv_a8(const uq_layout* L, const void* codes, const void* params, const uint16_t* x,
@@ -43,6 +44,17 @@ uq_status uq_gemm(const uq_layout* layout, const void* codes, const void* params
   if (st != UQ_OK) return st;
   return uq::launched(
       uq::launch_gemm(layout, codes, params, x, y, int(m), workspace, static_cast<hipStream_t>(stream)));
+}
+
+uq_status uq_gemm_noalloc(const uq_layout* layout, const void* codes, const void* params, const uint16_t* x,
+                          float* y, int64_t m, void* stream) {
+  const uq_status st = uq::check_product(layout, codes, params, x, y, m, UQ_GEMM_MAX_M);
+  if (st != UQ_OK) return st;
+  if (uq::gemm_workspace(layout, m).total > uq::kGemmScratchBytes) return UQ_ERR_WORKSPACE;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  if (uq::gemm_scratch(s, &ws) != hipSuccess) return UQ_ERR_HIP;
+  return uq::launched(uq::launch_gemm(layout, codes, params, x, y, int(m), ws, s));
 }
 
 uq_status uq_dequant(const uq_layout* layout, const void* codes, const void* params, float* w, void* stream) {

@@ -123,6 +123,9 @@ inline GemmWorkspace gemm_workspace(const uq_layout* L, int64_t m) {
   return w;
 }
 
+// Size of the fixed device scratch uq_gemm_noalloc works in (one per GPU).
+constexpr size_t kGemmScratchBytes = size_t(UQ_GEMM_NOALLOC_MAX_BYTES);
+
 // ---- Argument checks of the device entry points (uq_check.cpp; host only,
 // no HIP call) ----
 uq_status check_product(const uq_layout* L, const void* codes, const void* params, const void* x,

@@ -144,6 +144,22 @@ uq_status uq_gemm(const uq_layout* layout, const void* codes, const void* params
                   const uint16_t* x, float* y, int64_t m, void* workspace,
                   size_t workspace_bytes, void* stream);
 
+/* uq_gemm for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same product, kernels and results as uq_gemm, with the workspace taken
+ * from a fixed device array of UQ_GEMM_NOALLOC_MAX_BYTES that the library
+ * holds on each GPU it runs on until the process ends.  Calls whose
+ * workspace (uq_gemm_workspace_size) would exceed that return
+ * UQ_ERR_WORKSPACE before any HIP call.  Every call on a GPU shares that
+ * GPU's array: calls that may overlap on one GPU (concurrent streams, or
+ * threads) race and must not be made.  The first call on a device also
+ * clears the array's arrival counters, by a kernel on `stream`.  Arguments
+ * otherwise as for uq_gemm; allocates nothing. */
+#define UQ_GEMM_NOALLOC_MAX_BYTES (32u << 20) /* 32 MiB per GPU */
+uq_status uq_gemm_noalloc(const uq_layout* layout, const void* codes,
+                          const void* params, const uint16_t* x, float* y,
+                          int64_t m, void* stream);
+
 /* Dequantize the whole matrix (the matching dequantizer of
  * Core Components > Quantization):  w[n][k] = w' exactly (bit for bit).
  *   w : device fp32 [n][k] row-major, 16-byte aligned, overwritten */

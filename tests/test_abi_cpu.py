@@ -202,6 +202,22 @@ def test_gemm_workspace_validation(lib, m):
     assert lib.uq_status_str(7) == "UQ_ERR_WORKSPACE"
 
 
+def test_gemm_noalloc_validation(lib):
+    """uq_gemm_noalloc checks its arguments like uq_gemm and refuses calls whose
+    workspace exceeds its fixed scratch, all before any HIP call."""
+    A = 1 << 20
+    lay = lib.layout("int4", 128, 11008, 4096)
+    call = lambda lay_, m, y=A: lib.raw_call("uq_gemm_noalloc", ctypes.byref(lay_), A, A, A, y, m, None)  # noqa: E731
+    assert call(lay, 1, y=None) == 1
+    assert call(lay, 0) == 2 and call(lay, 65537) == 2
+    assert call(lay, 16, y=A + 4) == 4
+    big = 4097  # bf16 x of 4224 rows x 4096 = 34.6 MB > 32 MiB
+    assert lib.uq_gemm_workspace_size(lay, big) > lib.GEMM_NOALLOC_MAX_BYTES
+    assert call(lay, big) == 7
+    assert lib.uq_gemm_workspace_size(lay, 256) <= lib.GEMM_NOALLOC_MAX_BYTES
+    assert lib.uq_gemm_workspace_size(lay, 64) <= lib.GEMM_NOALLOC_MAX_BYTES
+
+
 def test_gemm_workspace_size(lib):
     """Sizes follow the documented regions: 64 KiB of counters, bf16 x in whole
     128-row tiles for m > 64, and four partial tiles of fp32 outputs for m <= 64."""
