@@ -59,6 +59,61 @@ def kernel_source_hash(path: str) -> str:
     return h.hexdigest()[:16]
 
 
+def graph_of(launch, count: int, start: int = 0):
+    """A HIP graph of `count` calls launch(i, stream) on a side stream (one
+    call made first, outside the capture, to warm the launch path)."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        launch(start, s.cuda_stream)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            for i in range(count):
+                launch(start + i, s.cuda_stream)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(launch, rotate: int, steps: int, warmup: int) -> float:
+    """ms per call over exactly `steps` calls replayed from graphs of `rotate`
+    calls, between HIP events recorded on the stream the replays run on."""
+    import torch
+    full = graph_of(launch, rotate)
+    rem = graph_of(launch, steps % rotate) if steps % rotate else None
+    stream = torch.cuda.current_stream()
+    for _ in range(max(1, math.ceil(warmup / rotate))):
+        full.replay()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(steps // rotate):
+        full.replay()
+    if rem is not None:
+        rem.replay()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps
+
+
+def per_launch_stats(launch, count: int) -> dict:
+    """Eager launches, each between its own pair of HIP events on the launch
+    stream: median / min / p90 of the per-launch durations in us."""
+    import torch
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(count)]
+    for i, (a, b) in enumerate(ev):
+        a.record(stream)
+        launch(i, stream.cuda_stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    us = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+    return {"median_us": round(statistics.median(us), 3), "min_us": round(us[0], 3),
+            "p90_us": round(us[min(len(us) - 1, int(0.9 * len(us)))], 3), "launches": count}
+
+
 class Setup:
     """Packed weights (rotated device copies), activations and output for one workload."""
 
@@ -98,43 +153,14 @@ class Setup:
         else:
             self.fn(self.lay, self.codes[j], self.params[j], self.x, self.y, self.m, stream=stream)
 
-    def graph(self, count: int, start: int = 0):
-        import torch
-        g = torch.cuda.CUDAGraph()
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):
-            self.launch(start, s.cuda_stream)  # warm the launch path outside capture
-            torch.cuda.synchronize()
-            with torch.cuda.graph(g, stream=s):
-                for i in range(count):
-                    self.launch(start + i, s.cuda_stream)
-        torch.cuda.current_stream().wait_stream(s)
-        torch.cuda.synchronize()
-        return g
-
     def time(self, steps: int, warmup: int):
         """(ms per step, eager ms per step) over exactly `steps` launches."""
         import torch
-        R = self.rotate
-        full = self.graph(R)
-        rem = self.graph(steps % R) if steps % R else None
-        stream = torch.cuda.current_stream()
-        for _ in range(max(1, math.ceil(warmup / R))):
-            full.replay()
-        torch.cuda.synchronize()
-        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t0.record(stream)
-        for _ in range(steps // R):
-            full.replay()
-        if rem is not None:
-            rem.replay()
-        t1.record(stream)
-        torch.cuda.synchronize()
-        ms = t0.elapsed_time(t1) / steps
+        ms = time_graph(self.launch, self.rotate, steps, warmup)
         # eager cross-check (host launch overhead included)
+        stream = torch.cuda.current_stream()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        n_eager = min(steps, 4 * R)
+        n_eager = min(steps, 4 * self.rotate)
         sp = stream.cuda_stream
         e0.record(stream)
         for i in range(n_eager):
@@ -210,7 +236,7 @@ def cpu_baseline(wl: workloads.Workload, m: int, nbytes: int) -> dict:
     except Exception:  # threadpoolctl missing: report the pool size numpy was built with
         blas = os.cpu_count() or 1
     return {"value": round(nbytes / med / 1e9, 4), "unit": "GB/s", "cores": int(blas),
-            "kind": "oracle",
+            "host_cores": os.cpu_count(), "blas_threads": int(blas), "kind": "oracle",
             "sample": (f"whole {wl.name} matrix, M={m}: NumPy unpack + dequant + fp64 product, "
                        f"median of {len(times)} runs after 1 warm-up ({med * 1e3:.0f} ms each); "
                        f"elementwise steps single-threaded, product on {blas} BLAS threads")}
@@ -307,6 +333,210 @@ def traffic_parse(wl: workloads.Workload, m: int, fetch_dir: str, write_dir: str
     return t
 
 
+class ReadProbe:
+    """The streaming-read ceiling: uq_probe_read over rotated device buffers of a given size."""
+
+    def __init__(self, uq, nbytes: int, rotate: int):
+        import torch
+        self.uq, self.nbytes, self.rotate = uq, nbytes, rotate
+        g = torch.Generator(device="cuda").manual_seed(0)
+        self.bufs = [torch.randint(0, 256, (max(nbytes, 1024),), dtype=torch.uint8, device="cuda", generator=g)
+                     for _ in range(rotate)]
+        self.sink = torch.zeros(4 << 20, dtype=torch.int32, device="cuda")
+        self.wg, self.un = 1024, 8
+
+    def launch(self, i: int, stream: int) -> None:
+        self.uq.uq_probe_read(self.bufs[i % self.rotate], self.nbytes, self.wg, self.un, self.sink, stream=stream)
+
+    def time(self, wg: int, un: int, steps: int, warmup: int) -> float:
+        self.wg, self.un = wg, un
+        return time_graph(self.launch, self.rotate, steps, warmup)
+
+
+def probe_grids(nbytes: int) -> list:
+    """Workgroup counts to try for a read of nbytes: whole multiples of the 256
+    CUs, and the GEMV's own grid shape (one workgroup per 16 weight rows of 2304 B)."""
+    grids = [256, 512, 768, 1024, 2048, 4096]
+    gemv_like = math.ceil(nbytes / (16 * 2304))
+    return sorted(set(g for g in grids + [gemv_like] if 4 * g <= nbytes // 1024 or g == 256))
+
+
+def ceiling_line(uq, nbytes: int, steps: int, warmup: int) -> dict:
+    """The best plain read of nbytes (rotated copies, graph-timed like the GEMV)
+    over a few grid shapes, plus an empty launch; for the JSON line."""
+    rotate = max(16, math.ceil(320e6 / nbytes))
+    pr = ReadProbe(uq, nbytes, rotate)
+    best = None
+    for wg in (256, 512, 688, 1024):
+        for un in (8, 16):
+            ms = pr.time(wg, un, steps, warmup)
+            if best is None or ms < best[0]:
+                best = (ms, wg, un)
+    empty = ReadProbe(uq, 0, 1)
+    ms_empty = empty.time(256, 8, steps, warmup)
+    del pr, empty
+    ms, wg, un = best
+    return {"plain_read_us": round(ms * 1e3, 3), "plain_read_gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "workgroups": wg, "loads_in_flight": un, "empty_launch_us": round(ms_empty * 1e3, 3),
+            "bytes": nbytes, "rotated_copies": rotate}
+
+
+def report_ceiling(uq, steps: int, warmup: int, path: str | None) -> dict:
+    """Plain reads of the headline's weight bytes and of 1 GiB, an empty launch,
+    and the headline GEMV, all timed the same way in one run (markdown)."""
+    cmd = "python bench.py " + " ".join(sys.argv[1:])
+    wl = workloads.WORKLOADS[workloads.HEADLINE]
+    nbytes = weight_bytes(wl)
+    rows = ["# Streaming-read ceiling of one launch", "",
+            "uq_probe_read reads every byte once with the GEMV's load pattern (wave-wide 128-bit non-temporal "
+            "loads, 1 KB per wave instruction, equal contiguous runs per wave).  Buffers are rotated so every "
+            "launch streams from HBM; each time is HIP events around graph-replayed launches, like the bench line.",
+            "", "Command (MI355X host, repository root):", "", f"    {cmd}", "",
+            "| read | bytes | workgroups | loads in flight per lane | us/launch | GB/s | % of 8 TB/s |",
+            "|---|---|---|---|---|---|---|"]
+    out = {}
+    for label, size in (("headline weight bytes", nbytes), ("1 GiB", 1 << 30)):
+        rotate = max(2, math.ceil(320e6 / size)) if size < (1 << 30) else 2
+        rotate = max(rotate, 16) if size < (1 << 30) else rotate
+        pr = ReadProbe(uq, size, rotate)
+        st = steps if size < (1 << 30) else max(20, steps // 100)
+        best = None
+        for wg in probe_grids(size):
+            for un in (4, 8, 16, 32):
+                ms = pr.time(wg, un, st, min(warmup, st))
+                gbs = size / (ms * 1e-3) / 1e9
+                rows.append(f"| {label} | {size:,} | {wg} | {un} | {ms * 1e3:.3f} | {gbs:.0f} | "
+                            f"{100 * gbs / HBM_PEAK_GBS:.1f} |")
+                log(rows[-1])
+                if best is None or ms < best[0]:
+                    best = (ms, wg, un)
+        out[label] = {"us": round(best[0] * 1e3, 3), "gbs": round(size / (best[0] * 1e-3) / 1e9, 1),
+                      "workgroups": best[1], "loads_in_flight": best[2]}
+        del pr
+    pr = ReadProbe(uq, 0, 1)
+    ms = pr.time(256, 8, steps, warmup)
+    rows.append(f"| empty launch (reads nothing) | 0 | 256 | - | {ms * 1e3:.3f} | - | - |")
+    out["empty launch us"] = round(ms * 1e3, 3)
+    del pr
+    st = Setup(uq, wl, 1, None)
+    ms_gemv, _ = st.time(steps, warmup)
+    gbs = nbytes / (ms_gemv * 1e-3) / 1e9
+    best = out["headline weight bytes"]
+    rows += ["", f"Headline GEMV ({wl.name}, M=1) in the same run: {ms_gemv * 1e3:.3f} us/launch, {gbs:.0f} GB/s = "
+             f"{100 * gbs / HBM_PEAK_GBS:.1f} % of 8 TB/s = {100 * best['us'] / (ms_gemv * 1e3):.1f} % of the best "
+             f"plain read of the same bytes ({best['us']:.3f} us, {best['workgroups']} workgroups, "
+             f"{best['loads_in_flight']} loads in flight per lane)."]
+    out["gemv_us"] = round(ms_gemv * 1e3, 3)
+    text = "\n".join(rows) + "\n"
+    log(text)
+    if path:
+        with open(path, "w") as f:
+            f.write(text)
+    return out
+
+
+def trace_summary(directory: str, name: str, cmds: list[str], kernel_hint: str, path_key: str | None) -> None:
+    """Per-kernel duration statistics (count, median, min, p90, mean) and
+    resources (VGPR, AGPR, SGPR, LDS, scratch, grid) from a rocprofv3
+    --kernel-trace CSV, written to profiles/NAME.md and .json.  With path_key
+    (gemv / gemm) the kernel-source hash is stored, so the bench line can tell
+    whether the trace still describes the built kernel."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(directory, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_trace.csv under {directory}")
+    by = {}
+    for fn in files:
+        with open(fn) as f:
+            for r in csv.DictReader(f):
+                k = r["Kernel_Name"]
+                d = by.setdefault(k, {"ns": [], "res": r})
+                d["ns"].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    kernels = {}
+    for k, d in by.items():
+        ns = sorted(d["ns"])
+        r = d["res"]
+        kernels[k] = {"dispatches": len(ns), "median_us": round(statistics.median(ns) / 1e3, 3),
+                      "min_us": round(ns[0] / 1e3, 3), "p90_us": round(ns[min(len(ns) - 1, int(0.9 * len(ns)))] / 1e3, 3),
+                      "mean_us": round(statistics.fmean(ns) / 1e3, 3),
+                      "vgpr": int(r.get("VGPR_Count", 0) or 0), "agpr": int(r.get("Accum_VGPR_Count", 0) or 0),
+                      "sgpr": int(r.get("SGPR_Count", 0) or 0), "lds_bytes": int(r.get("LDS_Block_Size", 0) or 0),
+                      "scratch_bytes": int(r.get("Scratch_Size", 0) or 0),
+                      "workgroup": int(r.get("Workgroup_Size_X", 0) or 0), "grid": int(r.get("Grid_Size_X", 0) or 0)}
+    order = sorted(kernels, key=lambda k: -kernels[k]["dispatches"] * kernels[k]["median_us"])
+    t = {"name": name, "commands": cmds, "kernels": kernels}
+    if path_key:
+        t["kernel_source_hash"] = kernel_source_hash(path_key)
+        hits = [k for k in order if kernel_hint in k]
+        t["main_kernel"] = hits[0] if hits else None
+    with open(os.path.join(ROOT, "profiles", f"{name}.json"), "w") as f:
+        json.dump(t, f, indent=1)
+    md = [f"# Kernel trace: {name}", "", "Commands (MI355X host, repository root):", ""] + \
+         [f"    {c}" for c in cmds] + ["",
+         "Durations from rocprofv3 --kernel-trace (End - Start per dispatch, warm-up and capture launches "
+         "included); resources as the trace records them per kernel (VGPR counts in registers per lane, "
+         "LDS in bytes per workgroup; grid in threads).", "",
+         "| kernel | dispatches | median us | min us | p90 us | mean us | VGPR | AGPR | SGPR | LDS B | scratch B | "
+         "wg | grid |", "|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    for k in order:
+        v = kernels[k]
+        md.append(f"| `{k[:110]}` | {v['dispatches']} | {v['median_us']} | {v['min_us']} | {v['p90_us']} | "
+                  f"{v['mean_us']} | {v['vgpr']} | {v['agpr']} | {v['sgpr']} | {v['lds_bytes']} | "
+                  f"{v['scratch_bytes']} | {v['workgroup']} | {v['grid']} |")
+    with open(os.path.join(ROOT, "profiles", f"{name}.md"), "w") as f:
+        f.write("\n".join(md) + "\n")
+    log("\n".join(md))
+
+
+def counter_summary(dirs: list[str], name: str, cmds: list[str], kernel_hint: str, title: str) -> None:
+    """Median per-dispatch value of every counter collected for the kernels whose
+    name contains kernel_hint, over one or more rocprofv3 --pmc output folders
+    (one per pass); written to profiles/NAME.md and .json."""
+    import csv
+    import glob
+    vals = {}
+    for d in dirs:
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise SystemExit(f"no counter_collection.csv under {d}")
+        for fn in files:
+            with open(fn) as f:
+                for r in csv.DictReader(f):
+                    if kernel_hint in r["Kernel_Name"]:
+                        vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    if not vals:
+        raise SystemExit(f"no dispatch of a kernel matching {kernel_hint!r}")
+    med = {c: statistics.median(v) for c, v in vals.items()}
+    with open(os.path.join(ROOT, "profiles", f"{name}.json"), "w") as f:
+        json.dump({"name": name, "kernel_hint": kernel_hint, "commands": cmds,
+                   "median_per_dispatch": med, "dispatches": {c: len(v) for c, v in vals.items()}}, f, indent=1)
+    md = [f"# Counters: {title}", "", "Commands (MI355X host, repository root), one pass each:", ""] + \
+         [f"    {c}" for c in cmds] + ["", f"Median per dispatch of kernels matching `{kernel_hint}`:", "",
+                                      "| counter | median per dispatch | dispatches |", "|---|---|---|"]
+    for c in sorted(med):
+        md.append(f"| {c} | {med[c]:,.0f} | {len(vals[c])} |")
+    with open(os.path.join(ROOT, "profiles", f"{name}.md"), "w") as f:
+        f.write("\n".join(md) + "\n")
+    log("\n".join(md))
+
+
+def committed_trace(wl, m: int):
+    """Median / min / p90 of the timed kernel from the committed trace summary,
+    if it was taken from the kernel sources as they are now."""
+    path = os.path.join(ROOT, "profiles", f"trace_{wl.name}_m{m}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_hash") != kernel_source_hash(wl.path) or not t.get("main_kernel"):
+        return None
+    k = t["kernels"][t["main_kernel"]]
+    return {"median_us": k["median_us"], "min_us": k["min_us"], "p90_us": k["p90_us"],
+            "dispatches": k["dispatches"], "vgpr": k["vgpr"], "lds_bytes": k["lds_bytes"],
+            "source": f"profiles/trace_{wl.name}_m{m}.md"}
+
+
 class NormRopeSetup:
     """Fused RMSNorm + RoPE inputs (rotated device copies of x and y) for one workload."""
 
@@ -334,7 +564,6 @@ class NormRopeSetup:
         self.uq.uq_rmsnorm_rope(self.x[j], self.y[j], self.gamma, self.pos, self.cos, self.sin, wl.tokens,
                                 wl.heads, wl.head_dim, wl.max_pos, wl.eps, stream=stream)
 
-    graph = Setup.graph
     time = Setup.time
 
     def check_sample(self) -> float:
@@ -437,11 +666,31 @@ def main() -> None:
     ap.add_argument("--traffic-parse", nargs=2, default=None, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc outputs (FETCH_SIZE, WRITE_SIZE) into profiles/traffic_*")
     ap.add_argument("--traffic-cmd", action="append", default=[], help="command lines recorded with the result")
+    ap.add_argument("--ceiling", action="store_true",
+                    help="plain reads of the headline's bytes and of 1 GiB, an empty launch and the headline GEMV "
+                         "(markdown to stderr and --report)")
+    ap.add_argument("--trace-summary", nargs=2, default=None, metavar=("TRACE_DIR", "NAME"),
+                    help="turn a rocprofv3 --kernel-trace output into profiles/NAME.md|json")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the live plain-read ceiling in the JSON line")
+    ap.add_argument("--counter-summary", nargs="+", default=None, metavar="ARG",
+                    help="NAME KERNEL_HINT TITLE DIR [DIR ...]: median counters per dispatch into profiles/NAME.md")
     args = ap.parse_args()
 
     if args.gpus != 1:
         raise SystemExit("bench.py measures one GPU: the library has no multi-GPU path "
                          "(the sharding plan is documented, not built); run with --gpus 1")
+    if args.counter_summary:
+        name, hint, title, *dirs = args.counter_summary
+        counter_summary(dirs, name, args.traffic_cmd, hint, title)
+        return
+    if args.trace_summary:
+        wl_ = workloads.WORKLOADS.get(args.workload)
+        hint = "gemv_kernel" if wl_ is not None and wl_.path == "gemv" else "gemm_kernel"
+        if args.a8:
+            hint = "gemv_a8_kernel"
+        trace_summary(args.trace_summary[0], args.trace_summary[1], args.traffic_cmd, hint,
+                      None if wl_ is None or args.a8 else wl_.path)
+        return
     if args.workload in workloads.NORM_ROPE:
         norm_rope_line(args)
         return
@@ -460,6 +709,9 @@ def main() -> None:
 
     if args.traffic_run:
         traffic_run(uq, wl, m, args.traffic_run)
+        return
+    if args.ceiling:
+        print(json.dumps({"ceiling": report_ceiling(uq, args.steps, args.warmup, args.report)}), flush=True)
         return
     if args.a8 and (wl.path != "gemv" or wl.scheme == "nf4"):
         raise SystemExit("--a8 applies to the INT GEMV workloads")
@@ -500,6 +752,15 @@ def main() -> None:
         out["roofline"] = {"bound": "mfma", "achieved": round(tfl, 3), "peak": BF16_PEAK_TFLOPS,
                            "unit": "TFLOP/s", "frac": round(tfl / BF16_PEAK_TFLOPS, 4),
                            "traffic": traffic_for(wl, m)}
+    out["launch_stats"] = dict(per_launch_stats(st.launch, min(args.steps, 200)),
+                               note="eager launches, each between its own pair of HIP events")
+    trace = committed_trace(wl, m) if not args.a8 else None
+    if trace is not None:
+        out["kernel_trace"] = trace
+    if wl.path == "gemv" and not args.no_ceiling:
+        c = ceiling_line(uq, st.bytes // 1024 * 1024, min(args.steps, 400), min(args.warmup, 40))
+        c["gemv_frac_of_plain_read"] = round(c["plain_read_us"] / (ms * 1e3), 4)
+        out["ceiling"] = c
     if not args.no_cpu_baseline and not args.a8:
         log("timing the oracle on the host (cpu_baseline) ...")
         out["cpu_baseline"] = cpu_baseline(wl, m, st.bytes)

@@ -68,6 +68,7 @@ _lib.uq_import_gguf.argtypes = [ctypes.c_int32, _P, ctypes.c_int64, ctypes.c_int
 _lib.uq_gemv.argtypes = [_L, _P, _P, _P, _P, ctypes.c_int64, _P]
 _lib.uq_gemm.argtypes = [_L, _P, _P, _P, _P, ctypes.c_int64, _P, ctypes.c_size_t, _P]
 _lib.uq_gemm_noalloc.argtypes = [_L, _P, _P, _P, _P, ctypes.c_int64, _P]
+_lib.uq_probe_read.argtypes = [_P, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int32, _P, _P]
 _lib.uq_gemm_workspace_size.argtypes = [_L, ctypes.c_int64, ctypes.POINTER(ctypes.c_size_t)]
 _lib.uq_dequant.argtypes = [_L, _P, _P, _P, _P]
 _lib.uq_gemv_a8.argtypes = [_L, _P, _P, _P, _P, ctypes.c_int64, _P]
@@ -80,12 +81,12 @@ _lib.uq_status_str.argtypes = [ctypes.c_int]
 _lib.uq_status_str.restype = ctypes.c_char_p
 for _fn in ("uq_packed_size", "uq_pack_weights", "uq_import_gguf", "uq_gemv", "uq_gemm", "uq_dequant",
             "uq_nf4_codebook", "uq_rope_table", "uq_rmsnorm_rope", "uq_gemv_a8", "uq_quantize_activations",
-            "uq_gemm_workspace_size", "uq_gemm_noalloc"):
+            "uq_gemm_workspace_size", "uq_gemm_noalloc", "uq_probe_read"):
     getattr(_lib, _fn).restype = ctypes.c_int
 
 EXPORTS = ("uq_packed_size", "uq_pack_weights", "uq_import_gguf", "uq_gemv", "uq_gemm", "uq_dequant",
            "uq_nf4_codebook", "uq_rope_table", "uq_rmsnorm_rope", "uq_gemv_a8", "uq_quantize_activations",
-           "uq_gemm_workspace_size", "uq_gemm_noalloc", "uq_status_str")
+           "uq_gemm_workspace_size", "uq_gemm_noalloc", "uq_probe_read", "uq_status_str")
 GEMM_NOALLOC_MAX_BYTES = 32 << 20
 
 
@@ -257,6 +258,13 @@ def uq_rmsnorm_rope(x, y, gamma, pos, cos, sin, tokens: int, heads: int, head_di
         _ptr(pos, "pos", 4 * max(int(tokens), 0), ("int32",)), _ptr(cos, "cos", tab, _F32),
         _ptr(sin, "sin", tab, _F32), int(tokens), int(heads), int(head_dim), int(max_pos), float(eps),
         _stream(stream)))
+
+
+def uq_probe_read(src, nbytes: int, workgroups: int, loads_in_flight: int, sink, stream=None) -> None:
+    """Measurement hook: read nbytes of src once with the GEMV's load pattern."""
+    _check("uq_probe_read", _lib.uq_probe_read(_ptr(src, "src", int(nbytes)), int(nbytes), int(workgroups),
+                                               int(loads_in_flight), _ptr(sink, "sink", 16 * int(workgroups)),
+                                               _stream(stream)))
 
 
 def uq_nf4_codebook() -> np.ndarray:

@@ -22,6 +22,9 @@ hipError_t launch_rmsnorm_rope(const uint16_t* x, uint16_t* y, const float* gamm
                                const float* cos_tab, const float* sin_tab, int64_t tokens, int32_t heads,
                                int32_t head_dim, int64_t max_pos, float eps, hipStream_t stream);
 
+hipError_t launch_probe_read(const void* src, size_t bytes, int32_t workgroups, int32_t loads_in_flight,
+                             uint32_t* sink, hipStream_t stream);
+
 namespace {
 uq_status launched(hipError_t e) { return e == hipSuccess ? UQ_OK : UQ_ERR_HIP; }
 }  // namespace
@@ -86,6 +89,14 @@ uq_status uq_rmsnorm_rope(const uint16_t* x, uint16_t* y, const float* gamma, co
   if (tokens == 0) return UQ_OK;
   return uq::launched(uq::launch_rmsnorm_rope(x, y, gamma, pos, cos, sin, tokens, heads, head_dim, max_pos, eps,
                                               static_cast<hipStream_t>(stream)));
+}
+
+uq_status uq_probe_read(const void* src, size_t bytes, int32_t workgroups, int32_t loads_in_flight,
+                        uint32_t* sink, void* stream) {
+  const uq_status st = uq::check_probe_read(src, bytes, workgroups, loads_in_flight, sink);
+  if (st != UQ_OK) return st;
+  return uq::launched(
+      uq::launch_probe_read(src, bytes, workgroups, loads_in_flight, sink, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

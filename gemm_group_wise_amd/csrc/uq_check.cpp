@@ -61,4 +61,14 @@ uq_status check_rmsnorm_rope(const void* x, const void* y, const void* gamma, co
   return UQ_OK;
 }
 
+uq_status check_probe_read(const void* src, size_t bytes, int32_t workgroups, int32_t loads_in_flight,
+                           const void* sink) {
+  if ((!src && bytes) || !sink) return UQ_ERR_NULL;
+  if (bytes % 1024 || workgroups < 1 || workgroups > (1 << 20)) return UQ_ERR_SHAPE;
+  if (loads_in_flight != 4 && loads_in_flight != 8 && loads_in_flight != 16 && loads_in_flight != 32)
+    return UQ_ERR_UNSUPPORTED;
+  if (!aligned(src, 16) || !aligned(sink, 4)) return UQ_ERR_ALIGN;
+  return UQ_OK;
+}
+
 }  // namespace uq

@@ -137,6 +137,8 @@ uq_status check_quantize_activations(int32_t group, const void* x, const void* q
 uq_status check_rmsnorm_rope(const void* x, const void* y, const void* gamma, const void* pos, const void* cos,
                              const void* sin, int64_t tokens, int32_t heads, int32_t head_dim, int64_t max_pos,
                              float eps);
+uq_status check_probe_read(const void* src, size_t bytes, int32_t workgroups, int32_t loads_in_flight,
+                           const void* sink);
 
 // Host packer (uq_pack.cpp).
 uq_status pack_weights(const uq_layout* L, const float* w, uint8_t* codes,

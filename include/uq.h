@@ -256,6 +256,20 @@ uq_status uq_rmsnorm_rope(const uint16_t* x, uint16_t* y, const float* gamma,
                           int64_t tokens, int32_t heads, int32_t head_dim,
                           int64_t max_pos, float eps, void* stream);
 
+/* Measurement hook (not part of the product path): the streaming-read
+ * ceiling of the decode GEMV, which reads each packed weight byte once
+ * (Core Components > Fused Kernels, GEMV during single-token decode).
+ * Reads every byte of [src, src + bytes) once with the GEMV's load pattern
+ * (wave-wide 128-bit non-temporal loads, 1 KB per wave instruction,
+ * `loads_in_flight` loads per lane before any is used), over `workgroups`
+ * workgroups of 4 waves that each take an equal contiguous run of 1 KB
+ * blocks; bytes = 0 launches a kernel that reads nothing.
+ *   src  : device, 16-byte aligned; bytes a multiple of 1024
+ *   sink : device uint32 [workgroups * 4], written with per-wave XORs of the data
+ *   workgroups in 1 .. 2^20; loads_in_flight in {4, 8, 16, 32} */
+uq_status uq_probe_read(const void* src, size_t bytes, int32_t workgroups,
+                        int32_t loads_in_flight, uint32_t* sink, void* stream);
+
 /* Static, NUL-terminated name of a status code ("UQ_OK", ...). */
 const char* uq_status_str(uq_status status);
 

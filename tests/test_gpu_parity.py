@@ -111,29 +111,51 @@ def test_gemv_one_hot_nf4(lib):
 
 
 def test_gemv_batched_equivalence(lib):
-    """Row i of an M-row GEMV equals the single-row GEMV of x[i].
-
-    Bit for bit while K fits one LDS block of activations for every M and a
-    wave reduces the same number of partial sums (weight rows x activation
-    rows) across its lanes -- then the lanes sum the same chunks in the same
-    order; within the gate when more activation rows split K into more
-    blocks, and for INT8, whose single-row GEMV takes two weight rows per wave
-    (two partial sums, not four).
+    """Row i of an M-row GEMV equals the single-row GEMV of x[i] within the gate
+    (the pages' batched-decode equivalence; not bitwise, since the orders of
+    the fp32 sums differ).  INT2 / INT4 / INT8 calls with 2 to 8 rows run on
+    the matrix cores, whose sum order does not depend on M: their rows agree
+    bit for bit across M.  NF4 keeps the dot-product kernel for every M; with
+    K in one LDS block of activations its rows agree with the single-row call
+    bit for bit.
     """
-    for scheme, group in (("int4", 64), ("int2", 16), ("int8", 128), ("nf4", 64)):
-        for k, exact in ((1024, scheme != "int8"), (4096, False)):
+    for scheme, group in (("int4", 64), ("int2", 16), ("int8", 128), ("nf4", 64), ("int4", 32), ("int2", 64)):
+        for k in (1024, 4096):
             w, x = workloads.make_random(300, k, 8, seed=8, outliers=True)
             lay, codes, params = packed_on_device(lib, scheme, group, w)
+            wdq = oracle_dequant(w, scheme, group)
             ys = [run_gemv(lib, lay, codes, params, x[i:i + 1], 1)[0] for i in range(8)]
-            for m in (2, 4, 8):
+            full = {}
+            for m in (2, 3, 4, 5, 8):
                 note(f"gemv batched equivalence {scheme} G{group} k={k} m={m}")
                 y = run_gemv(lib, lay, codes, params, x, m)
-                if exact:
+                full[m] = y
+                gate(y, np.stack(ys[:m]).astype(np.float64), x[:m], wdq, f"equiv {scheme} m={m}")
+                gate(y, o.gemv_ref(x[:m], wdq), x[:m], wdq, f"oracle {scheme} m={m}")
+                if scheme == "nf4" and k == 1024:
                     for i in range(m):
                         assert np.array_equal(y[i], ys[i]), (scheme, group, m, i)
-                else:
-                    wdq = oracle_dequant(w, scheme, group)
-                    gate(y, np.stack(ys[:m]).astype(np.float64), x[:m], wdq, f"equiv {scheme} m={m}")
+            if scheme != "nf4":
+                for m in (2, 3, 4, 5):
+                    assert np.array_equal(full[m].view(np.uint32), full[8][:m].view(np.uint32)), (scheme, group, k, m)
+
+
+@pytest.mark.parametrize("scheme,group,n,k", [
+    ("int4", 64, 300, 4096), ("int4", 128, 777, 4096), ("int4", 64, 11008, 4096), ("int4", 64, 37, 1024),
+    ("int4", 128, 129, 2560), ("int4", 64, 100, 16384), ("int8", 32, 333, 1024), ("int8", 64, 45, 2048),
+    ("int8", 128, 4096, 4096), ("int8", 128, 61, 8192), ("int8", 32, 17, 3968)])
+def test_gemv_matrix_core_shapes(lib, scheme, group, n, k):
+    """The matrix-core GEMV (2 to 8 activation rows, INT4 groups of 64 / 128 and
+    INT8): one to eight 128-byte blocks per wave, four and eight waves, K
+    padded up to whole blocks (zero activations, groups past K ignored), a
+    ragged last 16-row tile, and 2 / 4 / 8 staged activation rows."""
+    w, x = workloads.make_random(n, k, 8, seed=42, outliers=True)
+    lay, codes, params = packed_on_device(lib, scheme, group, w)
+    wdq = oracle_dequant(w, scheme, group)
+    for m in (2, 3, 4, 6, 8):
+        note(f"gemv matrix-core {scheme} G{group} n={n} k={k} m={m}")
+        y = run_gemv(lib, lay, codes, params, x, m)
+        gate(y, o.gemv_ref(x[:m], wdq), x[:m], wdq, f"mfma gemv {scheme} G{group} {n}x{k} m={m}")
 
 
 @pytest.mark.parametrize("m,k", [(1, 36864), (8, 8192), (4, 8320)])
