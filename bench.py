@@ -34,7 +34,7 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix cores, published
 METRIC = "dequant-GEMV weight GB/s & % HBM peak, INT4 g64 K=4096 N=11008 M=1"
 _CSRC = "gemm_group_wise_amd/csrc/"
 KERNEL_SOURCES = {  # what the timed kernel of each path is built from
-    "gemv": [_CSRC + f for f in ("gemv_impl.hpp", "device_common.hpp", "gemv.hip", "gemv_int2.hip",
+    "gemv": [_CSRC + f for f in ("gemv_impl.hpp", "gemv_mfma.hpp", "device_common.hpp", "gemv.hip", "gemv_int2.hip",
                                  "gemv_int4.hip", "gemv_int8.hip", "gemv_nf4.hip")],
     "gemm": [_CSRC + f for f in ("gemm.hip", "device_common.hpp")],
 }

@@ -123,6 +123,26 @@ template <> __device__ __forceinline__ void pair_activations<UQ_INT2>(const uint
   }
 }
 
+// The same pairs without the division by the class (a permutation only); the
+// caller scales each class itself (INT4 / INT2, see gemv_impl.hpp).
+template <int S> __device__ __forceinline__ void pair_perm(const uint32_t (&d)[Fmt<S>::WPD / 2],
+                                                           f16x2 (&p)[Fmt<S>::PPD]);
+template <> __device__ __forceinline__ void pair_perm<UQ_INT4>(const uint32_t (&d)[4], f16x2 (&p)[4]) {
+  p[0] = as_h2(__builtin_amdgcn_perm(d[2], d[0], 0x05040100u));  // (x0, x4)
+  p[1] = as_h2(__builtin_amdgcn_perm(d[3], d[1], 0x05040100u));  // (x2, x6)
+  p[2] = as_h2(__builtin_amdgcn_perm(d[2], d[0], 0x07060302u));  // (x1, x5)
+  p[3] = as_h2(__builtin_amdgcn_perm(d[3], d[1], 0x07060302u));  // (x3, x7)
+}
+template <> __device__ __forceinline__ void pair_perm<UQ_INT2>(const uint32_t (&d)[8], f16x2 (&p)[8]) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j)  // (x_j, x_{j+8})
+    p[j] = as_h2(__builtin_amdgcn_perm(d[4 + j / 2], d[j / 2], (j & 1) ? 0x07060302u : 0x05040100u));
+}
+// log2 of the class of pair j (the power of two its activations are divided by).
+template <int S> __device__ __forceinline__ constexpr int pair_log2_class(int j) {
+  return S == UQ_INT4 ? (j >= 2 ? 4 : 0) : S == UQ_INT2 ? 2 * (j & 3) : 0;
+}
+
 template <> __device__ __forceinline__ void pair_activations<UQ_INT8>(const uint32_t (&d)[2], f16x2 (&p)[2]) {
   p[0] = as_h2(d[0]);
   p[1] = as_h2(d[1]);

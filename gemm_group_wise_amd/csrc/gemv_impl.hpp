@@ -19,6 +19,12 @@
 //     s*t + z*SX, which is sum x*(q*s + z).  NF4: a * sum (H[q] + L[q])*x,
 //     the codebook split into fp16 high and low parts (two dot products, no
 //     rounding of the codebook in the products).
+//   * INT4 and INT2 divide activations by up to 16 / 64 for the class trick,
+//     so each (activation row, K block) is first scaled by a power of two
+//     2^e that puts its largest |x| in [2^14, 2^15): every staged value then
+//     keeps the fp16 bits it came with (no subnormal results for small
+//     activations), and the group's term is multiplied back by 2^-e in fp32,
+//     exactly.
 //   * Lane partials are summed across the wave with DPP and lane swizzles.
 #pragma once
 
@@ -137,9 +143,12 @@ __device__ __forceinline__ void unpack_nf4(uint32_t w, const uint2* lut, f16x2 (
 
 // y += s * t + z * SX for one group part (t = the accumulator, which started
 // at -C); NF4: y += a * t.
-template <bool NF, int MT, int PPC>
+// y += s * t + z * SX for one group part (t = the accumulator, which started
+// at -C, times the row's back-scale 2^-e when the activations were scaled);
+// NF4: y += a * t.
+template <bool NF, bool GAIN, int MT, int PPC>
 __device__ __forceinline__ void apply_group(uint32_t par, const float (&acc)[MT], const float2 (&cv)[MT][PPC],
-                                            int pp, float (&acc_y)[MT]) {
+                                            int pp, const float (&rs)[MT], float (&acc_y)[MT]) {
   if constexpr (NF) {
     const float a = h2f(uint16_t(par));
 #pragma unroll
@@ -149,10 +158,28 @@ __device__ __forceinline__ void apply_group(uint32_t par, const float (&acc)[MT]
     const float z = h2f(uint16_t(par >> 16));
 #pragma unroll
     for (int mm = 0; mm < MT; ++mm) {
-      acc_y[mm] = __builtin_fmaf(s, acc[mm], acc_y[mm]);
+      const float t = GAIN ? acc[mm] * rs[mm] : acc[mm];
+      acc_y[mm] = __builtin_fmaf(s, t, acc_y[mm]);
       acc_y[mm] = __builtin_fmaf(z, cv[mm][pp].y, acc_y[mm]);
     }
   }
+}
+
+// Gain exponent e for a staged block whose largest |x| has fp16 bits `mb`:
+// max |x| * 2^e in [2^14, 2^15) (or e = 0 for an all-zero block), within
+// [-1, 30] (below 2^-16 the block's values are scaled by 2^30 only).
+__device__ __forceinline__ int gain_exp(uint32_t mb) {
+  if (mb == 0u) return 0;
+  const float mx = h2f(uint16_t(mb));
+  const int ex = int((__builtin_bit_cast(uint32_t, mx) >> 23) & 0xFFu) - 126;  // mx in [2^(ex-1), 2^ex)
+  const int e = 15 - ex;
+  return e < -1 ? -1 : e > 30 ? 30 : e;
+}
+
+// fp16 splat of 2^t for -14 <= t <= 15.
+__device__ __forceinline__ f16x2 pow2_h2(int t) {
+  const uint32_t b = uint32_t(t + 15) << 10;
+  return as_h2(b | (b << 16));
 }
 
 // ONE: the whole K range fits one LDS block of activations and one group of
@@ -178,6 +205,9 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
   uint2* lut = reinterpret_cast<uint2*>(lds);       // NF4: 256 x (high pair, low pair)
   uint32_t* xs = lds + (NF ? 512 : 0);              // [MT][kb_max/2] fp16 pairs
   float2* cs = reinterpret_cast<float2*>(xs + MT * (kb_max / 2));  // [MT][kb_max/GP]
+  constexpr bool GAIN = (S == UQ_INT4 || S == UQ_INT2);  // schemes whose staging divides by a class
+  uint32_t* gmax = reinterpret_cast<uint32_t*>(cs + (NF ? 0 : MT * (kb_max / GP)));  // [MT] largest |x| bits
+  float* rsc = reinterpret_cast<float*>(gmax + MT);                                 // [MT] 2^-e
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -251,7 +281,31 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
     __builtin_amdgcn_sched_barrier(0);  // and all weight loads ahead of the staging work
 
     // (3) stage: pair, pre-scale, sum; write LDS
+    if constexpr (GAIN) {
+      if (tid < MT) gmax[tid] = 0u;  // (no thread still reads it: the last read precedes the previous barrier)
+    }
     __syncthreads();  // LDS free (previous K block done)
+    if constexpr (GAIN) {
+      // largest |x| of each activation row in this block (fp16 magnitudes
+      // order like their bit patterns)
+      typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+      for (int s = 0; s < kIPT; ++s) {
+        const int it0 = tid + s * kThreads;
+        const int it = it0 < n_items ? it0 : n_items - 1;
+        const int mm = it / (nch * PPC);
+        u16x2 mv = {0, 0};
+#pragma unroll
+        for (int v = 0; v < XV; ++v)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            mv = __builtin_elementwise_max(mv, __builtin_bit_cast(u16x2, dword_of(xr[s][v], q) & 0x7FFF7FFFu));
+        const uint32_t mb = uint32_t(mv.x > mv.y ? mv.x : mv.y);
+        if (mm < m) atomicMax(gmax + mm, mb);
+      }
+      __syncthreads();
+      if (tid < MT) rsc[tid] = __builtin_bit_cast(float, uint32_t(127 - gain_exp(gmax[tid])) << 23);  // 2^-e
+    }
     // Threads past the last item redo the last one (same values, same LDS
     // words), so the staging has no branch for the loads to sink into.
 #pragma unroll
@@ -272,7 +326,18 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
 #pragma unroll
           for (int j = 0; j < WPD / 2; ++j) d[j] = live ? dword_of(xr[s][(dl * WPD / 2 + j) >> 2], (dl * WPD / 2 + j) & 3) : 0u;
           f16x2 pr[PPD];
-          pair_activations<S>(d, pr);
+          if constexpr (GAIN) {
+            // pairs scaled by 2^(e - class) in two exact fp16 steps (each factor <= 2^15)
+            const int e = gain_exp(gmax[mm < m ? mm : 0]);
+            pair_perm<S>(d, pr);
+#pragma unroll
+            for (int j = 0; j < PPD; ++j) {
+              const int t = e - pair_log2_class<S>(j);
+              pr[j] = pr[j] * pow2_h2(t < 15 ? t : 15) * pow2_h2(t > 15 ? t - 15 : 0);
+            }
+          } else {
+            pair_activations<S>(d, pr);
+          }
           if constexpr (!NF) {
 #pragma unroll
             for (int j = 0; j < WPD / 2; ++j) sx = __builtin_amdgcn_fdot2(as_h2(d[j]), one2, sx, false);
@@ -294,6 +359,10 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
     }
     __builtin_amdgcn_sched_barrier(0);  // no weight-dependent math above the barrier
     __syncthreads();
+
+    float rs[MT];  // per activation row: 2^-e of this block (1 without a gain)
+#pragma unroll
+    for (int mm = 0; mm < MT; ++mm) rs[mm] = GAIN ? rsc[mm] : 1.0f;
 
     // (4) compute; K blocks wider than 64*U chunks load each further group
     //     just before using it (many waves per SIMD cover that latency)
@@ -354,7 +423,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
                     if constexpr (NF) acc[mm] = __builtin_amdgcn_fdot2(lp[j], xp[mm][dd][j], acc[mm], false);
                   }
               }
-              apply_group<NF>(valid ? cur[u].par[r][pp] : 0u, acc, cv, pp, acc_y[r]);
+              apply_group<NF, GAIN>(valid ? cur[u].par[r][pp] : 0u, acc, cv, pp, rs, acc_y[r]);
             }
           }
         } else {
@@ -395,7 +464,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
               }
             }
 #pragma unroll
-            for (int r = 0; r < R; ++r) apply_group<NF>(valid ? cur[u].par[r][pp] : 0u, acc[r], cv, pp, acc_y[r]);
+            for (int r = 0; r < R; ++r) apply_group<NF, GAIN>(valid ? cur[u].par[r][pp] : 0u, acc[r], cv, pp, rs, acc_y[r]);
           }
         }
       }
@@ -462,7 +531,7 @@ hipError_t launch(const uq_layout* L, const void* codes, const void* params, con
   // most kMaxIPT * kThreads parts of GP activations across the MT rows.
   if (int64_t(MT) * (kb_max / Gm::GP) > int64_t(kMaxIPT) * kThreads) kb_max = kMaxIPT * kThreads * Gm::GP / MT;
   const size_t shmem = (Gm::NF ? 2048 : 0) + size_t(MT) * kb_max * 2 +
-                       (Gm::NF ? 0 : size_t(MT) * (kb_max / Gm::GP) * 8);
+                       (Gm::NF ? 0 : size_t(MT) * (kb_max / Gm::GP) * 8) + size_t(MT) * 8;
   const int64_t rows_per_block = kWaves * R;
   const int64_t blocks = (int64_t(n) + rows_per_block - 1) / rows_per_block;  // n < 2^31: no overflow in int64
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;

@@ -115,3 +115,39 @@ def test_gemm_largest_m(lib):
     y = run(lib, "uq_gemm", lay, codes, params, x, m)
     xb = o.bf16_rne(x.astype(np.float32))
     gate(y, o.gemm_ref(x, wdq), xb, o.bf16_rne(wdq), "gemm m=65536")
+
+
+@pytest.mark.parametrize("scheme,group", [("int2", 16), ("int2", 64), ("int4", 32), ("int4", 64), ("int4", 128),
+                                          ("int8", 128), ("nf4", 64)])
+def test_small_and_mixed_activations(lib, scheme, group):
+    """Activations far below 1 (x * 1e-3, 1e-4, 2e-5: fp16 values whose
+    division by a code class would fall into fp16 subnormals), activation rows
+    of very different sizes in one call (normal, tiny, largest fp16), through
+    the single-row and multi-row GEMVs and the GEMM, against the oracle."""
+    n, k = 300, 2048
+    w, x = workloads.make_random(n, k, 16, seed=51, outliers=True)
+    lay, codes, params = packed_on_device(lib, scheme, group, w)
+    wdq = oracle_dequant(w, scheme, group)
+    xf = x.astype(np.float32)
+    for scale in (1e-3, 1e-4, 2e-5):
+        xs = (xf * np.float32(scale)).astype(np.float16)
+        for m in (1, 2, 8):
+            note(f"small x {scheme} G{group} scale={scale} m={m}")
+            gate(run(lib, "uq_gemv", lay, codes, params, xs, m), o.gemv_ref(xs[:m], wdq), xs[:m], wdq,
+                 f"{scheme} G{group} x*{scale} m={m}")
+    mixed = xf.copy()
+    mixed[1] *= 1e-4
+    mixed[3] *= 2e-5
+    mixed[5] = np.clip(mixed[5] * 2e4, -65504, 65504)
+    mixed = mixed.astype(np.float16)
+    for m in (2, 4, 8):
+        note(f"mixed rows {scheme} G{group} m={m}")
+        y = run(lib, "uq_gemv", lay, codes, params, mixed, m)
+        ref = o.gemv_ref(mixed[:m], wdq)
+        for i in range(m):  # each row on its own scale
+            gate(y[i:i + 1], ref[i:i + 1], mixed[i:i + 1], wdq, f"{scheme} G{group} mixed m={m} row {i}")
+    note(f"small x gemm {scheme} G{group}")
+    xs = (xf * np.float32(1e-4)).astype(np.float16)
+    xb = o.bf16_rne(xs[:16].astype(np.float32))
+    gate(run(lib, "uq_gemm", lay, codes, params, xs, 16), o.gemm_ref(xs[:16], wdq), xb, o.bf16_rne(wdq),
+         f"{scheme} G{group} small x gemm")
