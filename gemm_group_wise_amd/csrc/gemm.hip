@@ -591,11 +591,16 @@ steps_done:
     // (counted with one device-scope atomic per tile) adds the ksplit partial
     // tiles in split order and stores y, so the sum does not depend on which
     // one arrives last.  Nothing waits on another workgroup.  Each XCD has
-    // its own L2, so the partial tiles are written and read with device-scope
-    // (coherent) accesses instead of fences: a device-scope fence here writes
-    // back and invalidates the whole L2, evicting the activations every other
-    // workgroup on that XCD is streaming.  The last workgroup also returns
-    // the tile's counter to zero for the next call.
+    // its own L2, so the partial tiles are written and read with agent-scope
+    // atomic accesses (coherence bit set: stores write through the L2, loads
+    // do not hit a non-coherent line) instead of fences: an agent-scope
+    // release / acquire fence writes back / invalidates the whole L2, evicting
+    // the activations every other workgroup on that XCD is streaming.  The
+    // ordering that a release / acquire pair would give comes from
+    // s_waitcnt vmcnt(0) (the stores are acknowledged at agent scope) and the
+    // barrier before the counter increment, and on the reader from issuing
+    // the loads only after the increment returned the final count.  The last
+    // workgroup also returns the tile's counter to zero for the next call.
     const size_t rows = size_t(tiles_m) * BM;
     if (wk == 0) {
       float* dst = part + size_t(split) * rows * size_t(n);
