@@ -372,7 +372,7 @@ def ceiling_line(uq, nbytes: int, steps: int, warmup: int) -> dict:
             ms = pr.time(wg, un, steps, warmup)
             if best is None or ms < best[0]:
                 best = (ms, wg, un)
-    empty = ReadProbe(uq, 0, 1)
+    empty = ReadProbe(uq, 0, 16)  # graphs of 16 launches, like the reads: per-launch cost, not replay overhead
     ms_empty = empty.time(256, 8, steps, warmup)
     del pr, empty
     ms, wg, un = best
@@ -413,7 +413,7 @@ def report_ceiling(uq, steps: int, warmup: int, path: str | None) -> dict:
         out[label] = {"us": round(best[0] * 1e3, 3), "gbs": round(size / (best[0] * 1e-3) / 1e9, 1),
                       "workgroups": best[1], "loads_in_flight": best[2]}
         del pr
-    pr = ReadProbe(uq, 0, 1)
+    pr = ReadProbe(uq, 0, 16)  # graphs of 16 launches, like the reads
     ms = pr.time(256, 8, steps, warmup)
     rows.append(f"| empty launch (reads nothing) | 0 | 256 | - | {ms * 1e3:.3f} | - | - |")
     out["empty launch us"] = round(ms * 1e3, 3)

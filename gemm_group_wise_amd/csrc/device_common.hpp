@@ -25,40 +25,44 @@ template <> struct Fmt<UQ_NF4>  { static constexpr int bits = 4, CW = 32, WPD = 
 __device__ __forceinline__ f16x2 as_h2(uint32_t v) { return __builtin_bit_cast(f16x2, v); }
 __device__ __forceinline__ uint32_t as_u32(f16x2 v) { return __builtin_bit_cast(uint32_t, v); }
 
-// fp16 0x6400 is 1024.0 with a zero 10-bit mantissa: OR-ing an integer
-// c < 1024 into the mantissa yields exactly 1024 + c.  The unpackers below
-// turn a dword of codes into fp16 pairs (1024 + cls*q_a, 1024 + cls*q_b) with
-// one AND-OR per pair, where cls is a power of two set by the bit position of
-// the code; the activations are pre-divided by cls so the products carry the
-// right weight, and the constant 1024 is removed with a per-group correction.
-constexpr uint32_t kMagic2 = 0x64006400u;
+// fp16 with biased exponent E and a zero mantissa is 2^(E-15); OR-ing an
+// integer c < 1024 into the 10-bit mantissa gives 2^(E-15) * (1 + c/1024).
+// A code q left in place at mantissa bit b (c = q << b) therefore reads as
+// exactly B + q when the base is B = 2^(10-b): 1024 (0x6400) for bit 0, 256
+// (0x5C00) for bit 2, 64 (0x5400) for bit 4, 16 (0x4C00) for bit 6.  The
+// unpackers below mask codes where they sit, two codes per fp16 pair, with one
+// AND-OR per pair and the base that matches the bit position, so every pair
+// is (B + q_a, B + q_b) exactly and the activations are used as they come;
+// the per-group correction removes B * sum x.
+constexpr uint32_t kMagic2 = 0x64006400u;  // base 1024, code at bit 0 of each half
+constexpr uint32_t kBase256 = 0x5C005C00u, kBase64 = 0x54005400u, kBase16 = 0x4C004C00u;
 
-// Position of dword-local code i among the pairs: pair j, half h, class cls.
+// Position of dword-local code i among the pairs: pair j, half h; base of pair j.
 template <int S> struct Slot;
 template <> struct Slot<UQ_INT4> {
-  // pairs: 0 = (c0, c4), 1 = (c2, c6), 2 = (c1, c5) x16, 3 = (c3, c7) x16
+  // pairs: 0 = (c0, c4), 1 = (c2, c6) base 1024; 2 = (c1, c5), 3 = (c3, c7) base 64
   static __host__ __device__ constexpr int pair(int i) { return (i & 1) ? 2 + ((i & 3) >> 1) : ((i & 3) >> 1); }
   static __host__ __device__ constexpr int half(int i) { return i >> 2; }
-  static __host__ __device__ constexpr float inv_cls(int i) { return (i & 1) ? 0.0625f : 1.0f; }
+  static __host__ __device__ constexpr float base(int j) { return j < 2 ? 1024.0f : 64.0f; }
 };
 template <> struct Slot<UQ_INT2> {
-  // pair j = (c_j, c_{j+8}) scaled by 4^(j mod 4)
+  // pair j = (c_j, c_{j+8}) with base 1024 / 4^(j mod 4)
   static __host__ __device__ constexpr int pair(int i) { return i & 7; }
   static __host__ __device__ constexpr int half(int i) { return i >> 3; }
-  static __host__ __device__ constexpr float inv_cls(int i) {
-    return (i & 3) == 0 ? 1.0f : (i & 3) == 1 ? 0.25f : (i & 3) == 2 ? 0.0625f : 0.015625f;
+  static __host__ __device__ constexpr float base(int j) {
+    return (j & 3) == 0 ? 1024.0f : (j & 3) == 1 ? 256.0f : (j & 3) == 2 ? 64.0f : 16.0f;
   }
 };
 template <> struct Slot<UQ_INT8> {
   // pair j = (c_{2j}, c_{2j+1})
   static __host__ __device__ constexpr int pair(int i) { return i >> 1; }
   static __host__ __device__ constexpr int half(int i) { return i & 1; }
-  static __host__ __device__ constexpr float inv_cls(int) { return 1.0f; }
+  static __host__ __device__ constexpr float base(int) { return 1024.0f; }
 };
 template <> struct Slot<UQ_NF4> {
   static __host__ __device__ constexpr int pair(int i) { return i >> 1; }
   static __host__ __device__ constexpr int half(int i) { return i & 1; }
-  static __host__ __device__ constexpr float inv_cls(int) { return 1.0f; }
+  static __host__ __device__ constexpr float base(int) { return 0.0f; }  // codebook lookup, no base
 };
 
 // (a & mask) | orv in one v_and_or_b32.  gfx9 VOP3 encodings take no literal
@@ -71,76 +75,52 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t o
   return r;
 }
 
-template <int S> __device__ __forceinline__ void unpack_pairs(uint32_t w, uint32_t magic, f16x2 (&p)[Fmt<S>::PPD]);
+template <int S> __device__ __forceinline__ void unpack_pairs(uint32_t w, f16x2 (&p)[Fmt<S>::PPD]);
 
-template <> __device__ __forceinline__ void unpack_pairs<UQ_INT4>(uint32_t w, uint32_t magic, f16x2 (&p)[4]) {
+template <> __device__ __forceinline__ void unpack_pairs<UQ_INT4>(uint32_t w, f16x2 (&p)[4]) {
   const uint32_t w8 = w >> 8;
-  p[0] = as_h2(and_or(w, 0x000F000Fu, magic));
-  p[1] = as_h2(and_or(w8, 0x000F000Fu, magic));
-  p[2] = as_h2(and_or(w, 0x00F000F0u, magic));
-  p[3] = as_h2(and_or(w8, 0x00F000F0u, magic));
+  p[0] = as_h2(and_or(w, 0x000F000Fu, kMagic2));
+  p[1] = as_h2(and_or(w8, 0x000F000Fu, kMagic2));
+  p[2] = as_h2(and_or(w, 0x00F000F0u, kBase64));
+  p[3] = as_h2(and_or(w8, 0x00F000F0u, kBase64));
 }
 
-template <> __device__ __forceinline__ void unpack_pairs<UQ_INT2>(uint32_t w, uint32_t magic, f16x2 (&p)[8]) {
+template <> __device__ __forceinline__ void unpack_pairs<UQ_INT2>(uint32_t w, f16x2 (&p)[8]) {
   const uint32_t w8 = w >> 8;
+  constexpr uint32_t base[4] = {kMagic2, kBase256, kBase64, kBase16};
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    p[j] = as_h2(and_or(w, 0x00030003u << (2 * j), magic));
-    p[4 + j] = as_h2(and_or(w8, 0x00030003u << (2 * j), magic));
+    p[j] = as_h2(and_or(w, 0x00030003u << (2 * j), base[j]));
+    p[4 + j] = as_h2(and_or(w8, 0x00030003u << (2 * j), base[j]));
   }
 }
 
-template <> __device__ __forceinline__ void unpack_pairs<UQ_INT8>(uint32_t w, uint32_t magic, f16x2 (&p)[2]) {
+template <> __device__ __forceinline__ void unpack_pairs<UQ_INT8>(uint32_t w, f16x2 (&p)[2]) {
   // v_perm_b32 selects bytes of {magic : w} (selector 0-3 = w, 4-7 = magic;
   // magic byte 5 is 0x64): (b0, 0x64, b1, 0x64) and (b2, 0x64, b3, 0x64)
-  p[0] = as_h2(__builtin_amdgcn_perm(magic, w, 0x05010500u));
-  p[1] = as_h2(__builtin_amdgcn_perm(magic, w, 0x05030502u));
+  p[0] = as_h2(__builtin_amdgcn_perm(kMagic2, w, 0x05010500u));
+  p[1] = as_h2(__builtin_amdgcn_perm(kMagic2, w, 0x05030502u));
 }
 
 // Activation pairing for the staged layout.  `d` holds WPD activations of one
 // code dword in natural order as fp16 pairs d[j] = (x_{2j}, x_{2j+1}); the
-// result is the PPD pairs the unpacker's output multiplies, pre-divided by the
-// pair's class (see Slot<S>).  v_perm_b32 selector 0x05040100 takes the low
-// halves of {S0 : S1}, 0x07060302 the high halves.
+// result is the PPD pairs the unpacker's output multiplies (a permutation
+// only: the values are not scaled).  v_perm_b32 selector 0x05040100 takes the
+// low halves of {S0 : S1}, 0x07060302 the high halves.
 template <int S> __device__ __forceinline__ void pair_activations(const uint32_t (&d)[Fmt<S>::WPD / 2],
                                                                  f16x2 (&p)[Fmt<S>::PPD]);
 
 template <> __device__ __forceinline__ void pair_activations<UQ_INT4>(const uint32_t (&d)[4], f16x2 (&p)[4]) {
-  const f16x2 sixteenth = {_Float16(0.0625f), _Float16(0.0625f)};
-  p[0] = as_h2(__builtin_amdgcn_perm(d[2], d[0], 0x05040100u));              // (x0, x4)
-  p[1] = as_h2(__builtin_amdgcn_perm(d[3], d[1], 0x05040100u));              // (x2, x6)
-  p[2] = as_h2(__builtin_amdgcn_perm(d[2], d[0], 0x07060302u)) * sixteenth;  // (x1, x5)/16
-  p[3] = as_h2(__builtin_amdgcn_perm(d[3], d[1], 0x07060302u)) * sixteenth;  // (x3, x7)/16
-}
-
-template <> __device__ __forceinline__ void pair_activations<UQ_INT2>(const uint32_t (&d)[8], f16x2 (&p)[8]) {
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    // (x_j, x_{j+8}) / 4^(j mod 4)
-    const f16x2 v = as_h2(__builtin_amdgcn_perm(d[4 + j / 2], d[j / 2], (j & 1) ? 0x07060302u : 0x05040100u));
-    const _Float16 c = _Float16(Slot<UQ_INT2>::inv_cls(j));
-    p[j] = (j & 3) ? v * f16x2{c, c} : v;
-  }
-}
-
-// The same pairs without the division by the class (a permutation only); the
-// caller scales each class itself (INT4 / INT2, see gemv_impl.hpp).
-template <int S> __device__ __forceinline__ void pair_perm(const uint32_t (&d)[Fmt<S>::WPD / 2],
-                                                           f16x2 (&p)[Fmt<S>::PPD]);
-template <> __device__ __forceinline__ void pair_perm<UQ_INT4>(const uint32_t (&d)[4], f16x2 (&p)[4]) {
   p[0] = as_h2(__builtin_amdgcn_perm(d[2], d[0], 0x05040100u));  // (x0, x4)
   p[1] = as_h2(__builtin_amdgcn_perm(d[3], d[1], 0x05040100u));  // (x2, x6)
   p[2] = as_h2(__builtin_amdgcn_perm(d[2], d[0], 0x07060302u));  // (x1, x5)
   p[3] = as_h2(__builtin_amdgcn_perm(d[3], d[1], 0x07060302u));  // (x3, x7)
 }
-template <> __device__ __forceinline__ void pair_perm<UQ_INT2>(const uint32_t (&d)[8], f16x2 (&p)[8]) {
+
+template <> __device__ __forceinline__ void pair_activations<UQ_INT2>(const uint32_t (&d)[8], f16x2 (&p)[8]) {
 #pragma unroll
   for (int j = 0; j < 8; ++j)  // (x_j, x_{j+8})
     p[j] = as_h2(__builtin_amdgcn_perm(d[4 + j / 2], d[j / 2], (j & 1) ? 0x07060302u : 0x05040100u));
-}
-// log2 of the class of pair j (the power of two its activations are divided by).
-template <int S> __device__ __forceinline__ constexpr int pair_log2_class(int j) {
-  return S == UQ_INT4 ? (j >= 2 ? 4 : 0) : S == UQ_INT2 ? 2 * (j & 3) : 0;
 }
 
 template <> __device__ __forceinline__ void pair_activations<UQ_INT8>(const uint32_t (&d)[2], f16x2 (&p)[2]) {

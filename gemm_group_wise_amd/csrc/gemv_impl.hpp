@@ -13,18 +13,13 @@
 //     flight while the activations are paired, pre-scaled and written to
 //     LDS.  Only then the workgroup synchronises and computes.
 //   * The activations sit in LDS paired for the unpacked code layout (see
-//     device_common.hpp), with two sums per group part: SX = sum x and
-//     C = 1024 * sum x'.  The lane forms t = sum (1024 + cls*q) * x/cls - C
-//     = sum q*x with packed fp16 dot products (fp32 accumulation) and adds
-//     s*t + z*SX, which is sum x*(q*s + z).  NF4: a * sum (H[q] + L[q])*x,
-//     the codebook split into fp16 high and low parts (two dot products, no
-//     rounding of the codebook in the products).
-//   * INT4 and INT2 divide activations by up to 16 / 64 for the class trick,
-//     so each (activation row, K block) is first scaled by a power of two
-//     2^e that puts its largest |x| in [2^14, 2^15): every staged value then
-//     keeps the fp16 bits it came with (no subnormal results for small
-//     activations), and the group's term is multiplied back by 2^-e in fp32,
-//     exactly.
+//     device_common.hpp), unscaled, with two sums per group part: SX = sum x
+//     and C = sum B*x, B the fp16 base each code position unpacks with.  The
+//     lane forms t = sum (B + q) * x - C = sum q*x with packed fp16 dot
+//     products (exact products, fp32 accumulation) and adds s*t + z*SX,
+//     which is sum x*(q*s + z).  NF4: a * sum (H[q] + L[q])*x, the codebook
+//     split into fp16 high and low parts (two dot products, no rounding of
+//     the codebook in the products).
 //   * Lane partials are summed across the wave with DPP and lane swizzles.
 #pragma once
 
@@ -126,8 +121,8 @@ __device__ __forceinline__ void load_pairs(const uint32_t* src, f16x2 (&xp)[PPD]
 }
 
 template <int S>
-__device__ __forceinline__ void unpack_dword(uint32_t w, uint32_t magic, f16x2 (&hp)[Fmt<S>::PPD]) {
-  unpack_pairs<S>(w, magic, hp);
+__device__ __forceinline__ void unpack_dword(uint32_t w, f16x2 (&hp)[Fmt<S>::PPD]) {
+  unpack_pairs<S>(w, hp);
 }
 
 // NF4: byte j of w -> the high and low fp16 parts of its two codes' values
@@ -143,12 +138,9 @@ __device__ __forceinline__ void unpack_nf4(uint32_t w, const uint2* lut, f16x2 (
 
 // y += s * t + z * SX for one group part (t = the accumulator, which started
 // at -C); NF4: y += a * t.
-// y += s * t + z * SX for one group part (t = the accumulator, which started
-// at -C, times the row's back-scale 2^-e when the activations were scaled);
-// NF4: y += a * t.
-template <bool NF, bool GAIN, int MT, int PPC>
+template <bool NF, int MT, int PPC>
 __device__ __forceinline__ void apply_group(uint32_t par, const float (&acc)[MT], const float2 (&cv)[MT][PPC],
-                                            int pp, const float (&rs)[MT], float (&acc_y)[MT]) {
+                                            int pp, float (&acc_y)[MT]) {
   if constexpr (NF) {
     const float a = h2f(uint16_t(par));
 #pragma unroll
@@ -158,28 +150,10 @@ __device__ __forceinline__ void apply_group(uint32_t par, const float (&acc)[MT]
     const float z = h2f(uint16_t(par >> 16));
 #pragma unroll
     for (int mm = 0; mm < MT; ++mm) {
-      const float t = GAIN ? acc[mm] * rs[mm] : acc[mm];
-      acc_y[mm] = __builtin_fmaf(s, t, acc_y[mm]);
+      acc_y[mm] = __builtin_fmaf(s, acc[mm], acc_y[mm]);
       acc_y[mm] = __builtin_fmaf(z, cv[mm][pp].y, acc_y[mm]);
     }
   }
-}
-
-// Gain exponent e for a staged block whose largest |x| has fp16 bits `mb`:
-// max |x| * 2^e in [2^14, 2^15) (or e = 0 for an all-zero block), within
-// [-1, 30] (below 2^-16 the block's values are scaled by 2^30 only).
-__device__ __forceinline__ int gain_exp(uint32_t mb) {
-  if (mb == 0u) return 0;
-  const float mx = h2f(uint16_t(mb));
-  const int ex = int((__builtin_bit_cast(uint32_t, mx) >> 23) & 0xFFu) - 126;  // mx in [2^(ex-1), 2^ex)
-  const int e = 15 - ex;
-  return e < -1 ? -1 : e > 30 ? 30 : e;
-}
-
-// fp16 splat of 2^t for -14 <= t <= 15.
-__device__ __forceinline__ f16x2 pow2_h2(int t) {
-  const uint32_t b = uint32_t(t + 15) << 10;
-  return as_h2(b | (b << 16));
 }
 
 // ONE: the whole K range fits one LDS block of activations and one group of
@@ -204,10 +178,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
   uint32_t* lds = reinterpret_cast<uint32_t*>(lds4);
   uint2* lut = reinterpret_cast<uint2*>(lds);       // NF4: 256 x (high pair, low pair)
   uint32_t* xs = lds + (NF ? 512 : 0);              // [MT][kb_max/2] fp16 pairs
-  float2* cs = reinterpret_cast<float2*>(xs + MT * (kb_max / 2));  // [MT][kb_max/GP]
-  constexpr bool GAIN = (S == UQ_INT4 || S == UQ_INT2);  // schemes whose staging divides by a class
-  uint32_t* gmax = reinterpret_cast<uint32_t*>(cs + (NF ? 0 : MT * (kb_max / GP)));  // [MT] largest |x| bits
-  float* rsc = reinterpret_cast<float*>(gmax + MT);                                 // [MT] 2^-e
+  float2* cs = reinterpret_cast<float2*>(xs + MT * (kb_max / 2));  // [MT][kb_max/GP]: (-C, SX)
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -225,7 +196,6 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
     roff[r] = rr * int64_t(rowb);
     poff[r] = rr * int64_t(ng) * (NF ? 2 : 4);
   }
-  const uint32_t magic = kMagic2;
 
   if constexpr (NF) {
     static_assert(kThreads == 256, "the NF4 byte table takes one entry per thread");
@@ -280,32 +250,8 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
     }
     __builtin_amdgcn_sched_barrier(0);  // and all weight loads ahead of the staging work
 
-    // (3) stage: pair, pre-scale, sum; write LDS
-    if constexpr (GAIN) {
-      if (tid < MT) gmax[tid] = 0u;  // (no thread still reads it: the last read precedes the previous barrier)
-    }
+    // (3) stage: pair, sum; write LDS
     __syncthreads();  // LDS free (previous K block done)
-    if constexpr (GAIN) {
-      // largest |x| of each activation row in this block (fp16 magnitudes
-      // order like their bit patterns)
-      typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-#pragma unroll
-      for (int s = 0; s < kIPT; ++s) {
-        const int it0 = tid + s * kThreads;
-        const int it = it0 < n_items ? it0 : n_items - 1;
-        const int mm = it / (nch * PPC);
-        u16x2 mv = {0, 0};
-#pragma unroll
-        for (int v = 0; v < XV; ++v)
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            mv = __builtin_elementwise_max(mv, __builtin_bit_cast(u16x2, dword_of(xr[s][v], q) & 0x7FFF7FFFu));
-        const uint32_t mb = uint32_t(mv.x > mv.y ? mv.x : mv.y);
-        if (mm < m) atomicMax(gmax + mm, mb);
-      }
-      __syncthreads();
-      if (tid < MT) rsc[tid] = __builtin_bit_cast(float, uint32_t(127 - gain_exp(gmax[tid])) << 23);  // 2^-e
-    }
     // Threads past the last item redo the last one (same values, same LDS
     // words), so the staging has no branch for the loads to sink into.
 #pragma unroll
@@ -318,7 +264,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
         const int c = rem / PPC, pp = rem - c * PPC;
         const bool live = mm < m;
         const f16x2 one2 = {_Float16(1.0f), _Float16(1.0f)};
-        float sx = 0.0f, sxp = 0.0f;
+        float sx = 0.0f, sxb = 0.0f;  // sum x, sum B*x
 #pragma unroll
         for (int dl = 0; dl < DPG; ++dl) {
           const int dd = pp * DPG + dl;
@@ -326,23 +272,15 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
 #pragma unroll
           for (int j = 0; j < WPD / 2; ++j) d[j] = live ? dword_of(xr[s][(dl * WPD / 2 + j) >> 2], (dl * WPD / 2 + j) & 3) : 0u;
           f16x2 pr[PPD];
-          if constexpr (GAIN) {
-            // pairs scaled by 2^(e - class) in two exact fp16 steps (each factor <= 2^15)
-            const int e = gain_exp(gmax[mm < m ? mm : 0]);
-            pair_perm<S>(d, pr);
-#pragma unroll
-            for (int j = 0; j < PPD; ++j) {
-              const int t = e - pair_log2_class<S>(j);
-              pr[j] = pr[j] * pow2_h2(t < 15 ? t : 15) * pow2_h2(t > 15 ? t - 15 : 0);
-            }
-          } else {
-            pair_activations<S>(d, pr);
-          }
+          pair_activations<S>(d, pr);
           if constexpr (!NF) {
 #pragma unroll
             for (int j = 0; j < WPD / 2; ++j) sx = __builtin_amdgcn_fdot2(as_h2(d[j]), one2, sx, false);
 #pragma unroll
-            for (int j = 0; j < PPD; ++j) sxp = __builtin_amdgcn_fdot2(pr[j], one2, sxp, false);
+            for (int j = 0; j < PPD; ++j) {
+              const _Float16 b = _Float16(Slot<S>::base(j));  // a power of two: exact products
+              sxb = __builtin_amdgcn_fdot2(pr[j], f16x2{b, b}, sxb, false);
+            }
           }
           uint32_t* dst = xs + mm * (kb_max / 2) + (dd * nch + c) * PPD;
           if constexpr (PPD == 8) {
@@ -354,15 +292,11 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
             reinterpret_cast<uint2*>(dst)[0] = make_uint2(as_u32(pr[0]), as_u32(pr[1]));
           }
         }
-        if constexpr (!NF) cs[mm * (kb_max / GP) + pp * nch + c] = make_float2(-1024.0f * sxp, sx);
+        if constexpr (!NF) cs[mm * (kb_max / GP) + pp * nch + c] = make_float2(-sxb, sx);
       }
     }
     __builtin_amdgcn_sched_barrier(0);  // no weight-dependent math above the barrier
     __syncthreads();
-
-    float rs[MT];  // per activation row: 2^-e of this block (1 without a gain)
-#pragma unroll
-    for (int mm = 0; mm < MT; ++mm) rs[mm] = GAIN ? rsc[mm] : 1.0f;
 
     // (4) compute; K blocks wider than 64*U chunks load each further group
     //     just before using it (many waves per SIMD cover that latency)
@@ -413,7 +347,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
                 const int dd = pp * DPG + dl;
                 f16x2 hp[PPD], lp[NF ? PPD : 1];
                 if constexpr (NF) unpack_nf4(dword_of(cur[u].code[r], dd), lut, hp, lp);
-                else unpack_dword<S>(dword_of(cur[u].code[r], dd), magic, hp);
+                else unpack_dword<S>(dword_of(cur[u].code[r], dd), hp);
                 // (the same order of additions as the dword-outer path below)
 #pragma unroll
                 for (int mm = 0; mm < MT; ++mm)
@@ -423,7 +357,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
                     if constexpr (NF) acc[mm] = __builtin_amdgcn_fdot2(lp[j], xp[mm][dd][j], acc[mm], false);
                   }
               }
-              apply_group<NF, GAIN>(valid ? cur[u].par[r][pp] : 0u, acc, cv, pp, rs, acc_y[r]);
+              apply_group<NF>(valid ? cur[u].par[r][pp] : 0u, acc, cv, pp, acc_y[r]);
             }
           }
         } else {
@@ -448,7 +382,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
 #pragma unroll
               for (int r = 0; r < R; ++r) {
                 if constexpr (NF) unpack_nf4(dword_of(cur[u].code[r], dd), lut, hp[r], lp[r]);
-                else unpack_dword<S>(dword_of(cur[u].code[r], dd), magic, hp[r]);
+                else unpack_dword<S>(dword_of(cur[u].code[r], dd), hp[r]);
               }
 #pragma unroll
               for (int mm = 0; mm < MT; ++mm) {
@@ -464,7 +398,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
               }
             }
 #pragma unroll
-            for (int r = 0; r < R; ++r) apply_group<NF, GAIN>(valid ? cur[u].par[r][pp] : 0u, acc[r], cv, pp, rs, acc_y[r]);
+            for (int r = 0; r < R; ++r) apply_group<NF>(valid ? cur[u].par[r][pp] : 0u, acc[r], cv, pp, acc_y[r]);
           }
         }
       }
@@ -530,8 +464,7 @@ hipError_t launch(const uq_layout* L, const void* codes, const void* params, con
   // At most 8 staged activation parts per thread (kMaxIPT): a block holds at
   // most kMaxIPT * kThreads parts of GP activations across the MT rows.
   if (int64_t(MT) * (kb_max / Gm::GP) > int64_t(kMaxIPT) * kThreads) kb_max = kMaxIPT * kThreads * Gm::GP / MT;
-  const size_t shmem = (Gm::NF ? 2048 : 0) + size_t(MT) * kb_max * 2 +
-                       (Gm::NF ? 0 : size_t(MT) * (kb_max / Gm::GP) * 8) + size_t(MT) * 8;
+  const size_t shmem = (Gm::NF ? 2048 : 0) + size_t(MT) * kb_max * 2 + (Gm::NF ? 0 : size_t(MT) * (kb_max / Gm::GP) * 8);
   const int64_t rows_per_block = kWaves * R;
   const int64_t blocks = (int64_t(n) + rows_per_block - 1) / rows_per_block;  // n < 2^31: no overflow in int64
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;

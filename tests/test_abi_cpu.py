@@ -479,3 +479,19 @@ def test_import_gguf_errors(lib):
         assert (codes == 0xAB).all() and (params == 0xABAB).all(), "written before the check"
     with pytest.raises(ValueError):
         lib.uq_import_gguf("q4_0", good[:-1], 2, 64)               # short buffer refused in Python
+
+
+def test_fp16_base_decode_is_exact():
+    """The dot-product GEMV decodes a code q sitting at bit b of an fp16 half by
+    OR-ing in the bits of B = 2^(10-b) (0x6400, 0x5C00, 0x5400, 0x4C00): the
+    result must read exactly B + q for every code that fits its field (INT2
+    fields at bits 0/2/4/6, INT4 at bits 0/4, INT8 at bit 0), in both halves
+    of the dword."""
+    bases = {0: 0x6400, 2: 0x5C00, 4: 0x5400, 6: 0x4C00}
+    for bits, positions in ((2, (0, 2, 4, 6)), (4, (0, 4)), (8, (0,))):
+        for b in positions:
+            q = np.arange(1 << bits, dtype=np.uint32)
+            word = ((q << b) | bases[b]) | (((q[::-1] << b) | bases[b]) << 16)
+            halves = word.astype("<u4").view("<f2").astype(np.float64).reshape(-1, 2)
+            assert np.array_equal(halves[:, 0], 2.0 ** (10 - b) + q)
+            assert np.array_equal(halves[:, 1], 2.0 ** (10 - b) + q[::-1])
