@@ -49,6 +49,10 @@
 #include "device_common.hpp"
 
 namespace uq {
+
+hipError_t launch_gemm_codes(const uq_layout* L, const void* codes, const void* params, const uint16_t* x, float* y,
+                             int m, float* part, unsigned* arrivals, void* act, int cus, hipStream_t stream);
+
 namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -806,6 +810,12 @@ hipError_t gemm_scratch(hipStream_t stream, void** out) {
 
 hipError_t launch_gemm(const uq_layout* L, const void* codes, const void* params, const uint16_t* x,
                        float* y, int m, void* workspace, hipStream_t stream) {
+  if (gemm_uses_codes(L)) {
+    const GemmWorkspace wl = gemm_workspace(L, m);
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    return launch_gemm_codes(L, codes, params, x, y, m, reinterpret_cast<float*>(ws + wl.part),
+                             reinterpret_cast<unsigned*>(ws + wl.counters), ws + wl.act, device_cus(), stream);
+  }
   GemmPlan plan = plan_gemm(m, L->n);
 #define UQ_GEMM_CASE(SC, GR) \
   case SC * 1000 + GR: plan.ksplit = plan_ksplit<SC, GR>(plan, m, L->n, L->k); break;
