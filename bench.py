@@ -191,10 +191,8 @@ class Setup:
         elif self.wl.path == "gemv":
             ref, xs, ws = o.gemv_ref(self.x_host, wdq), self.x_host, wdq
         else:
-            scheme, group = self.wl.scheme, self.wl.group  # GGUF workloads carry their INT layout
-            ref = o.gemm_layout_ref(self.x_host, wdq, scheme, group)
-            xs = o.bf16_rne(self.x_host.astype(np.float32))
-            ws = wdq if o.gemm_contracts_codes(scheme, group) else o.bf16_rne(wdq)
+            ref = o.gemm_ref(self.x_host, wdq)
+            xs, ws = o.bf16_rne(self.x_host.astype(np.float32)), o.bf16_rne(wdq)
         got = torch_y[:, idx].astype(np.float64)
         err = got - ref
         rel = float(np.linalg.norm(err) / np.linalg.norm(ref))
@@ -207,11 +205,7 @@ class Setup:
 def cpu_baseline(wl: workloads.Workload, m: int, nbytes: int) -> dict:
     """The oracle (unpack + dequant + fp64 product) on the same matrix, on host cores."""
     import oracle as o
-    if wl.path == "gemv":
-        ref = o.gemv_ref
-    else:
-        def ref(xs_, wdq_):
-            return o.gemm_layout_ref(xs_, wdq_, wl.scheme, wl.group)
+    ref = o.gemv_ref if wl.path == "gemv" else o.gemm_ref
     if wl.gguf:
         blob, x = workloads.make_gguf_workload(wl)
         xs = x[:m]

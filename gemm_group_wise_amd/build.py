@@ -23,7 +23,7 @@ LIB = os.path.join(PKG, "libuq.so")
 
 ARCH = "gfx950"
 HIP_SOURCES = ["uq_api.hip", "gemv.hip", "gemv_int2.hip", "gemv_int4.hip", "gemv_int8.hip",
-               "gemv_nf4.hip", "gemm.hip", "gemm_codes.hip", "dequant.hip", "rmsnorm_rope.hip", "gemv_a8.hip", "probe.hip"]
+               "gemv_nf4.hip", "gemm.hip", "dequant.hip", "rmsnorm_rope.hip", "gemv_a8.hip", "probe.hip"]
 CXX_SOURCES = ["uq_pack.cpp", "uq_gguf.cpp", "rope_table.cpp", "uq_check.cpp", "uq_host_api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -49,10 +49,6 @@
 #include "device_common.hpp"
 
 namespace uq {
-
-hipError_t launch_gemm_codes(const uq_layout* L, const void* codes, const void* params, const uint16_t* x, float* y,
-                             int m, float* part, unsigned* arrivals, void* act, int cus, hipStream_t stream);
-
 namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -105,6 +101,18 @@ struct CodeTile {
   __device__ static int swz(int r) { return (r / SWZ_DIV) & (PPR - 1); }
 };
 
+// Workgroup barrier for LDS only: this wave's LDS accesses complete
+// (lgkmcnt(0)), then s_barrier.  __syncthreads() also fences global memory,
+// which on gfx9 means waiting for every outstanding vector-memory load,
+// including loads meant to stay in flight.  The empty asm statements stop
+// the compiler from moving LDS accesses across.
+__device__ __forceinline__ void wait_lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), gfx9 encoding
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Byte I of a dword to fp32 in one instruction.  (Written as shift-and-mask,
 // the compiler emits a bit-field extract plus a byte-0 conversion: two.)
 template <int I>
@@ -148,45 +156,70 @@ __device__ __forceinline__ Codes<S> lds_codes(const uint8_t* p) {
   return c;
 }
 
+// A code q masked in place in a 16-bit half, at bit b with b + bits <= 10,
+// reads as the fp16 subnormal q 2^(b-24): exact, and exact again in fp32.
+// With the group scale taken as s 2^(24-b) (a power-of-two multiple, exact
+// in fp32) one fused multiply-add gives (q 2^(b-24)) (s 2^(24-b)) + z =
+// q s + z rounded once -- fma(q, s, z) bit for bit -- and the compiler
+// reads both the half and z straight from their registers (v_fma_mix_f32),
+// so no conversion of the code is spent.
+__device__ __forceinline__ float f16_lo(uint32_t v) { return float(__builtin_bit_cast(f16x2, v)[0]); }
+__device__ __forceinline__ float f16_hi(uint32_t v) { return float(__builtin_bit_cast(f16x2, v)[1]); }
+
 // Codes 8s..8s+7 of the lane's 16 -> bf16(w') as an MFMA operand, with the
 // lane's group parameters (s, z) -- (a, 0) for NF4 -- in fp32.
 template <int S>
 __device__ __forceinline__ bf16x8 dequant8(const Codes<S>& c, float sc, float zc, int s, const float* nf4) {
   constexpr int bits = Fmt<S>::bits;
+  constexpr float k24 = 16777216.0f, k22 = 4194304.0f, k20 = 1048576.0f, k18 = 262144.0f;
   float w[8];
   if constexpr (bits == 8) {
-    const uint32_t d0 = c.d[2 * s], d1 = c.d[2 * s + 1];
-    w[0] = __builtin_fmaf(ubyte_f32<0>(d0), sc, zc);
-    w[1] = __builtin_fmaf(ubyte_f32<1>(d0), sc, zc);
-    w[2] = __builtin_fmaf(ubyte_f32<2>(d0), sc, zc);
-    w[3] = __builtin_fmaf(ubyte_f32<3>(d0), sc, zc);
-    w[4] = __builtin_fmaf(ubyte_f32<0>(d1), sc, zc);
-    w[5] = __builtin_fmaf(ubyte_f32<1>(d1), sc, zc);
-    w[6] = __builtin_fmaf(ubyte_f32<2>(d1), sc, zc);
-    w[7] = __builtin_fmaf(ubyte_f32<3>(d1), sc, zc);
+    // code 2i + h of a dword: byte h of half i
+    const float s24 = sc * k24;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const uint32_t d = c.d[2 * s + t];
+      const uint32_t e = d & 0x00FF00FFu, o = (d >> 8) & 0x00FF00FFu;
+      w[4 * t + 0] = __builtin_fmaf(f16_lo(e), s24, zc);
+      w[4 * t + 1] = __builtin_fmaf(f16_lo(o), s24, zc);
+      w[4 * t + 2] = __builtin_fmaf(f16_hi(e), s24, zc);
+      w[4 * t + 3] = __builtin_fmaf(f16_hi(o), s24, zc);
+    }
   } else if constexpr (bits == 4) {
     const uint32_t d = c.d[s];
-    const uint32_t lo = d & 0x0F0F0F0Fu, hi = (d >> 4) & 0x0F0F0F0Fu;  // codes 0,2,4,6 | 1,3,5,7
     if constexpr (S == UQ_NF4) {
+      const uint32_t lo = d & 0x0F0F0F0Fu, hi = (d >> 4) & 0x0F0F0F0Fu;  // codes 0,2,4,6 | 1,3,5,7
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         w[2 * i] = nf4[(lo >> (8 * i)) & 0xFu] * sc;
         w[2 * i + 1] = nf4[(hi >> (8 * i)) & 0xFu] * sc;
       }
     } else {
-      w[0] = __builtin_fmaf(ubyte_f32<0>(lo), sc, zc);
-      w[1] = __builtin_fmaf(ubyte_f32<0>(hi), sc, zc);
-      w[2] = __builtin_fmaf(ubyte_f32<1>(lo), sc, zc);
-      w[3] = __builtin_fmaf(ubyte_f32<1>(hi), sc, zc);
-      w[4] = __builtin_fmaf(ubyte_f32<2>(lo), sc, zc);
-      w[5] = __builtin_fmaf(ubyte_f32<2>(hi), sc, zc);
-      w[6] = __builtin_fmaf(ubyte_f32<3>(lo), sc, zc);
-      w[7] = __builtin_fmaf(ubyte_f32<3>(hi), sc, zc);
+      // nibble j of the dword is code j: halves hold codes (0,4) (1,5) at
+      // bits 0 and 4, and after a shift by 8 codes (2,6) (3,7)
+      const float s24 = sc * k24, s20 = sc * k20;
+      const uint32_t d8 = d >> 8;
+      const uint32_t m0 = d & 0x000F000Fu, m1 = d & 0x00F000F0u, m2 = d8 & 0x000F000Fu, m3 = d8 & 0x00F000F0u;
+      w[0] = __builtin_fmaf(f16_lo(m0), s24, zc);
+      w[4] = __builtin_fmaf(f16_hi(m0), s24, zc);
+      w[1] = __builtin_fmaf(f16_lo(m1), s20, zc);
+      w[5] = __builtin_fmaf(f16_hi(m1), s20, zc);
+      w[2] = __builtin_fmaf(f16_lo(m2), s24, zc);
+      w[6] = __builtin_fmaf(f16_hi(m2), s24, zc);
+      w[3] = __builtin_fmaf(f16_lo(m3), s20, zc);
+      w[7] = __builtin_fmaf(f16_hi(m3), s20, zc);
     }
-  } else {  // 2 bits: codes 8s..8s+7 are 16 bits of the lane's dword
-    const uint32_t d = c.d[0] >> (16 * s);
+  } else {
+    // 2 bits: codes 8s..8s+7 are bytes 2s, 2s+1 of the lane's dword; spread
+    // them to the low bytes of the two halves, codes (j, 4+j) at bit 2j
+    const uint32_t p = __builtin_amdgcn_perm(0u, c.d[0], s ? 0x0C030C02u : 0x0C010C00u);
+    const float sj[4] = {sc * k24, sc * k22, sc * k20, sc * k18};
 #pragma unroll
-    for (int i = 0; i < 8; ++i) w[i] = __builtin_fmaf(float((d >> (2 * i)) & 3u), sc, zc);
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t mj = p & (0x00030003u << (2 * j));
+      w[j] = __builtin_fmaf(f16_lo(mj), sj[j], zc);
+      w[4 + j] = __builtin_fmaf(f16_hi(mj), sj[j], zc);
+    }
   }
   const uint4 v = make_uint4(pack_bf16(w[0], w[1]), pack_bf16(w[2], w[3]), pack_bf16(w[4], w[5]),
                              pack_bf16(w[6], w[7]));
@@ -750,6 +783,257 @@ hipError_t launch(const uq_layout* L, const void* codes, const void* params, con
                          dim3(T::NT), args, 0, stream);
 }
 
+// ---- Up to 32 activation rows: codes streamed straight into registers ----
+//
+// Up to 32 rows the GEMM is bound by memory traffic and latency, not by the
+// matrix cores, so it is organised like the GEMV: a workgroup of four waves
+// owns 64 weight rows (16 per wave) and a K range (the K split), and per
+// block of XB activations of that range it
+//   * issues the loads of the block's activations and of its rows' group
+//     parameters (consecutive lanes, consecutive groups of a row), then the
+//     codes each lane multiplies, directly in the MFMA layout: lane l takes
+//     weight row l % 16, and of the row's 16-byte pieces of the block the
+//     pieces 4 q + l / 16, so the four lanes of a row read 64 contiguous
+//     bytes per load -- within an MFMA any k order serves as long as A and B
+//     agree, and the activations are staged in the same order,
+//   * stages the activations in LDS (fp16 -> bf16, round to nearest even) and
+//     the parameters,
+//   * synchronises once and runs v_mfma_f32_16x16x32_bf16 over the block,
+//     each B operand dequantized from the lane's codes exactly as in the
+//     pipelined kernel (bf16(fma(q, s, z))), so the products are the same.
+// No workgroup barrier sits between a block's loads and its products.
+template <int S, int G, int TM>
+struct SGeo {
+  static constexpr int BM = 16 * TM, BN = 64, NT = 256;
+  static constexpr int bits = Fmt<S>::bits;
+  static constexpr int PB = param_bytes_per_group(S);
+  static constexpr int XB = 1024 / TM;          // K per block: the activations are BM x XB bf16 = 32 KB
+  static constexpr int Q = XB / 4;              // codes of one lane per block
+  static constexpr int CP = 128 / bits;         // codes in a 16-byte piece
+  static constexpr int NJ = Q / 8;              // MFMAs per block
+  static constexpr int QW = Q * bits / 32;      // code dwords of a lane per block
+  static constexpr int XPITCH = XB * 2 + 16;
+  static constexpr int XI = BM * XB / 8;        // 8-activation pieces staged per block
+  static constexpr int XPT = XI / NT;
+  static constexpr int NGB = XB / G;            // groups per block
+  static constexpr int PPB = BN * NGB;          // parameters per block
+  static constexpr int PPT = (PPB + NT - 1) / NT;
+  static_assert(XI % NT == 0 && QW % 4 == 0 && NJ % 2 == 0 && Q % G == 0, "block geometry");
+};
+
+template <int S, int G, int TM>
+__global__ __launch_bounds__(256) void gemm_stream_kernel(const uint8_t* __restrict__ codes,
+                                                          const uint8_t* __restrict__ params,
+                                                          const uint16_t* __restrict__ x, float* __restrict__ y,
+                                                          int n, int k, int m, int tiles_m, int ksplit,
+                                                          float* __restrict__ part, unsigned* __restrict__ arrivals) {
+  using Ge = SGeo<S, G, TM>;
+  constexpr int bits = Ge::bits, BM = Ge::BM, BN = Ge::BN, NT = Ge::NT, XB = Ge::XB, NJ = Ge::NJ;
+  constexpr int QW = Ge::QW, NGB = Ge::NGB;
+  __shared__ __attribute__((aligned(16))) uint8_t xs[BM * Ge::XPITCH];
+  __shared__ __attribute__((aligned(16))) uint32_t ps[Ge::PPB];
+  __shared__ float nf4[16];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int b = blockIdx.x;
+  const int split = b % ksplit, tile = b / ksplit;
+  const int tile_m = tile % tiles_m, tile_n = tile / tiles_m;
+  const int bm = tile_m * BM, bn = tile_n * BN;
+  const int nblk = k / XB;  // whole blocks only (the launcher sends other K to the pipelined kernel)
+  const int b0 = split * nblk / ksplit, b1 = (split + 1) * nblk / ksplit;
+  const int rowb = k * bits / 8;
+  const int ng = k / G;
+  const int l16 = lane & 15, kb = lane >> 4;
+  int wr = bn + 16 * wave + l16;
+  wr = wr < n ? wr : n - 1;  // rows past N: computed, not stored
+  const uint8_t* crow = codes + size_t(wr) * size_t(rowb) + 16 * kb;
+  if constexpr (S == UQ_NF4) {
+    if (tid < 16) nf4[tid] = nf4_value(tid);
+  }
+
+  f32x4 yacc[TM];
+#pragma unroll
+  for (int a = 0; a < TM; ++a) yacc[a] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  for (int blk = b0; blk < b1; ++blk) {
+    const int k0 = blk * XB;
+    // (1) loads: activations and parameters for staging, then the lane's codes
+    uint4 xv[Ge::XPT];
+#pragma unroll
+    for (int i = 0; i < Ge::XPT; ++i) {
+      const int it = i * NT + tid;
+      const int row = it / (XB / 8), c = it % (XB / 8);
+      int mr = bm + row;
+      mr = mr < m ? mr : m - 1;
+      xv[i] = *reinterpret_cast<const uint4*>(x + size_t(mr) * size_t(k) + k0 + 8 * c);
+    }
+    uint32_t pv[Ge::PPT];
+#pragma unroll
+    for (int i = 0; i < Ge::PPT; ++i) {
+      int q = i * NT + tid;
+      q = q < Ge::PPB ? q : Ge::PPB - 1;
+      int pr = bn + q / NGB;
+      pr = pr < n ? pr : n - 1;
+      const uint8_t* src = params + (size_t(pr) * size_t(ng) + k0 / G + q % NGB) * Ge::PB;
+      if constexpr (Ge::PB == 4) pv[i] = load_stream<uint32_t>(src);
+      else pv[i] = load_stream<uint16_t>(src);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    uint32_t run[QW];
+#pragma unroll
+    for (int q = 0; q < QW / 4; ++q) {
+      const uint4 v = load_stream<uint4>(crow + size_t(k0) * bits / 8 + 64 * q);
+      run[4 * q] = v.x; run[4 * q + 1] = v.y; run[4 * q + 2] = v.z; run[4 * q + 3] = v.w;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // (2) stage: 8 activations -> bf16 at slot 32 j + 8 kb of its row, where
+    //     position p of the block is in piece p / CP, read by k-block
+    //     (p / CP) % 4 as its code c = (p / CP / 4) CP + p % CP, of MFMA c / 8
+    wait_lds_barrier();
+#pragma unroll
+    for (int i = 0; i < Ge::XPT; ++i) {
+      const int it = i * NT + tid;
+      const int row = it / (XB / 8), c = it % (XB / 8);
+      const int p = 8 * c, kbs = (p / Ge::CP) % 4, j = ((p / Ge::CP / 4) * Ge::CP + p % Ge::CP) / 8;
+      const uint4 h = xv[i];
+      const uint4 v = make_uint4(pack_bf16(h2f(uint16_t(h.x)), h2f(uint16_t(h.x >> 16))),
+                                 pack_bf16(h2f(uint16_t(h.y)), h2f(uint16_t(h.y >> 16))),
+                                 pack_bf16(h2f(uint16_t(h.z)), h2f(uint16_t(h.z >> 16))),
+                                 pack_bf16(h2f(uint16_t(h.w)), h2f(uint16_t(h.w >> 16))));
+      *reinterpret_cast<uint4*>(xs + row * Ge::XPITCH + (32 * j + 8 * kbs) * 2) = v;
+    }
+#pragma unroll
+    for (int i = 0; i < Ge::PPT; ++i) {
+      const int q = i * NT + tid;
+      if (q < Ge::PPB) ps[q] = pv[i];
+    }
+    wait_lds_barrier();
+    // (3) the block's MFMAs, two at a time (one Codes of 16 codes each pair)
+    const uint32_t* prw = ps + (16 * wave + l16) * NGB;
+#pragma unroll
+    for (int jp = 0; jp < NJ / 2; ++jp) {
+      Codes<S> cc;
+#pragma unroll
+      for (int w = 0; w < Codes<S>::W; ++w) cc.d[w] = run[jp * Codes<S>::W + w];
+      const uint32_t pw = prw[((4 * (16 * jp / Ge::CP) + kb) * Ge::CP + (16 * jp) % Ge::CP) / G];
+      float sc, zc;
+      if constexpr (S == UQ_NF4) {
+        sc = h2f(uint16_t(pw));
+        zc = 0.0f;
+      } else {
+        sc = h2f(uint16_t(pw & 0xFFFFu));
+        zc = h2f(uint16_t(pw >> 16));
+      }
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        const bf16x8 bv = dequant8<S>(cc, sc, zc, sub, nf4);
+        const int j = 2 * jp + sub;
+#pragma unroll
+        for (int a = 0; a < TM; ++a) {
+          const bf16x8 av =
+              *reinterpret_cast<const bf16x8*>(xs + (16 * a + l16) * Ge::XPITCH + (32 * j + 8 * kb) * 2);
+          yacc[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, yacc[a], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // D layout: lane l, element i -> activation row 4 (l / 16) + i of tile a, weight row l % 16 of the wave.
+  const int col = bn + 16 * wave + l16;
+  if (ksplit > 1) {
+    // K split: as in the pipelined kernel (partial tiles with agent-scope
+    // atomic stores, one arrival counter per tile, the last workgroup adds
+    // the partial tiles in split order and returns the counter to zero).
+    const size_t rows = size_t(tiles_m) * BM;
+    float* dst = part + size_t(split) * rows * size_t(n);
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (col < n)
+          __hip_atomic_store(dst + size_t(bm + 16 * a + 4 * kb + i) * size_t(n) + col, yacc[a][i], __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the partial tile has been written
+    __syncthreads();
+    __shared__ unsigned last;
+    if (tid == 0) {
+      const unsigned before = atomicAdd(arrivals + tile, 1u);
+      last = before == unsigned(ksplit - 1);
+      if (last) atomicExch(arrivals + tile, 0u);
+    }
+    __syncthreads();
+    if (!last) return;
+    constexpr int E = BM * BN / NT;
+    float v[kGemmMaxSplit][E];
+#pragma unroll
+    for (int sp = 0; sp < kGemmMaxSplit; ++sp) {
+      const int spc = sp < ksplit ? sp : ksplit - 1;
+      const float* src = part + (size_t(spc) * rows + size_t(bm)) * size_t(n);
+#pragma unroll
+      for (int i = 0; i < E; ++i) {
+        const int e = i * NT + tid;
+        const int c = min(bn + e % BN, n - 1);
+        v[sp][i] = __hip_atomic_load(src + size_t(e / BN) * size_t(n) + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      float sum = v[0][i];
+#pragma unroll
+      for (int sp = 1; sp < kGemmMaxSplit; ++sp) sum = sp < ksplit ? sum + v[sp][i] : sum;
+      const int e = i * NT + tid;
+      const int row = bm + e / BN, c = bn + e % BN;
+      if (row < m && c < n) y[size_t(row) * size_t(n) + c] = sum;
+    }
+    return;
+  }
+#pragma unroll
+  for (int a = 0; a < TM; ++a)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = bm + 16 * a + 4 * kb + i;
+      if (row < m && col < n) y[size_t(row) * size_t(n) + col] = yacc[a][i];
+    }
+}
+
+int device_cus();
+
+template <int S, int G, int TM>
+hipError_t launch_stream_t(const uq_layout* L, const void* codes, const void* params, const uint16_t* x, float* y,
+                           int m, float* part, unsigned* arrivals, hipStream_t stream) {
+  using Ge = SGeo<S, G, TM>;
+  int n = int(L->n), k = int(L->k);
+  int tiles_m = (m + Ge::BM - 1) / Ge::BM;
+  const int64_t tiles = int64_t(tiles_m) * ((int64_t(n) + Ge::BN - 1) / Ge::BN);
+  // K split: the workgroups the chip holds at once over the tiles, at most
+  // kGemmMaxSplit (the workspace holds that many partial tiles of 32 rows),
+  // at least one block each.
+  int ksplit = 1;
+  if (tiles <= kGemmMaxSplitTiles) {
+    static std::atomic<int> cached{0};
+    int occ = cached.load(std::memory_order_relaxed);
+    if (occ <= 0) {
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+              &occ, reinterpret_cast<const void*>(&gemm_stream_kernel<S, G, TM>), Ge::NT, 0) != hipSuccess ||
+          occ < 1)
+        occ = 1;
+      cached.store(occ, std::memory_order_relaxed);
+    }
+    int64_t ks = int64_t(device_cus()) * occ / tiles;
+    if (ks > kGemmMaxSplit) ks = kGemmMaxSplit;
+    if (ks > k / Ge::XB) ks = k / Ge::XB;
+    ksplit = ks > 1 ? int(ks) : 1;
+  }
+  const int64_t nb = tiles * ksplit;
+  if (nb > 0x7fffffff) return hipErrorInvalidValue;
+  const uint8_t* c8 = static_cast<const uint8_t*>(codes);
+  const uint8_t* p8 = static_cast<const uint8_t*>(params);
+  void* args[] = {&c8, &p8, (void*)&x, &y, &n, &k, &m, &tiles_m, &ksplit, &part, &arrivals};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&gemm_stream_kernel<S, G, TM>), dim3(unsigned(nb)),
+                         dim3(Ge::NT), args, 0, stream);
+}
+
 template <int S, int G>
 hipError_t launch_plan(const GemmPlan& p, const uq_layout* L, const void* codes, const void* params,
                        const uint16_t* xb, float* y, int m, float* part, unsigned* arrivals, hipStream_t stream) {
@@ -810,12 +1094,6 @@ hipError_t gemm_scratch(hipStream_t stream, void** out) {
 
 hipError_t launch_gemm(const uq_layout* L, const void* codes, const void* params, const uint16_t* x,
                        float* y, int m, void* workspace, hipStream_t stream) {
-  if (gemm_uses_codes(L)) {
-    const GemmWorkspace wl = gemm_workspace(L, m);
-    uint8_t* ws = static_cast<uint8_t*>(workspace);
-    return launch_gemm_codes(L, codes, params, x, y, m, reinterpret_cast<float*>(ws + wl.part),
-                             reinterpret_cast<unsigned*>(ws + wl.counters), ws + wl.act, device_cus(), stream);
-  }
   GemmPlan plan = plan_gemm(m, L->n);
 #define UQ_GEMM_CASE(SC, GR) \
   case SC * 1000 + GR: plan.ksplit = plan_ksplit<SC, GR>(plan, m, L->n, L->k); break;
@@ -844,6 +1122,29 @@ hipError_t launch_gemm(const uq_layout* L, const void* codes, const void* params
   unsigned* arrivals = reinterpret_cast<unsigned*>(ws + wl.counters);
   uint16_t* xb = plan.xf ? const_cast<uint16_t*>(x) : reinterpret_cast<uint16_t*>(ws + wl.act);
   float* part = reinterpret_cast<float*>(ws + wl.part);
+  if (m <= 32 && L->k % 1024 == 0) {
+    // the streaming kernel (16- or 32-row tiles; its partial tiles fit the
+    // region sized for the pipelined kernel's 32-row tiles)
+#define UQ_STREAM_CASE(SC, GR)                                                                 \
+  case SC * 1000 + GR:                                                                         \
+    return m <= 16 ? launch_stream_t<SC, GR, 1>(L, codes, params, x, y, m, part, arrivals, stream) \
+                   : launch_stream_t<SC, GR, 2>(L, codes, params, x, y, m, part, arrivals, stream);
+    switch (L->scheme * 1000 + L->group) {
+      UQ_STREAM_CASE(UQ_INT2, 16)
+      UQ_STREAM_CASE(UQ_INT2, 32)
+      UQ_STREAM_CASE(UQ_INT2, 64)
+      UQ_STREAM_CASE(UQ_INT2, 128)
+      UQ_STREAM_CASE(UQ_INT4, 32)
+      UQ_STREAM_CASE(UQ_INT4, 64)
+      UQ_STREAM_CASE(UQ_INT4, 128)
+      UQ_STREAM_CASE(UQ_INT8, 32)
+      UQ_STREAM_CASE(UQ_INT8, 64)
+      UQ_STREAM_CASE(UQ_INT8, 128)
+      UQ_STREAM_CASE(UQ_NF4, 64)
+      default: return hipErrorInvalidValue;
+    }
+#undef UQ_STREAM_CASE
+  }
   if (!plan.xf) {
     int64_t count8 = int64_t(m) * L->k / 8;  // k % 32 == 0: whole 8-value pieces
     const int64_t want = (count8 + 255) / 256;

@@ -99,34 +99,6 @@ inline GemmPlan plan_gemm(int64_t m, int64_t n) {
   return {32, 1, 1, true};
 }
 
-// Layouts whose GEMM multiplies the integer codes on the matrix cores and
-// applies each group's scale and zero afterwards (reading R-GF: y = bf16(x) .
-// w'^T): INT2 / INT4 / INT8 with groups of 64 or 128.  The others dequantize
-// every weight to bf16 (y = bf16(x) . bf16(w')^T).
-inline bool gemm_uses_codes(const uq_layout* L) {
-  return (L->scheme == UQ_INT2 || L->scheme == UQ_INT4 || L->scheme == UQ_INT8) && L->group >= 64;
-}
-
-// Tiling of the code-multiplying GEMM (gemm_codes.hip): four waves, BM rows
-// of x by BN weight rows; cfg 0: 16 x 64, 1: 32 x 64, 2: 64 x 128,
-// 3: 128 x 128.  Tiles of up to 64 rows may split K (kGemmMaxSplit).
-struct CodesPlan {
-  int cfg, bm;
-};
-
-inline CodesPlan plan_gemm_codes(int64_t m) {
-  if (m <= 16) return {0, 16};
-  if (m <= 32) return {1, 32};
-  if (m <= 64) return {2, 64};
-  return {3, 128};
-}
-
-// Byte offset, within the activation region of the code-multiplying GEMM
-// (m > 64), of its (X, -128 X) table: after bf16 x of m rounded up to 128 rows.
-inline size_t gemm_codes_act_table(const uq_layout* L, int64_t m) {
-  return (size_t((m + 127) / 128 * 128) * size_t(L->k) * 2 + 255) / 256 * 256;
-}
-
 // Byte offsets of the regions of a uq_gemm workspace and its total size.
 // Regions start on 256-byte boundaries.  The partial tiles are sized for the
 // largest K split (kGemmMaxSplit), so the size does not depend on the device.
@@ -139,23 +111,10 @@ struct GemmWorkspace {
 
 inline GemmWorkspace gemm_workspace(const uq_layout* L, int64_t m) {
   auto up = [](size_t v) { return (v + 255) / 256 * 256; };
+  const GemmPlan p = plan_gemm(m, L->n);
   GemmWorkspace w;
   w.counters = 0;
   w.act = up(size_t(kGemmMaxSplitTiles) * 4);
-  if (gemm_uses_codes(L)) {
-    // up to 64 rows: the caller's fp16 x and partial tiles of a K split;
-    // above: bf16 x in chain order and its (X, -128 X) table
-    const CodesPlan c = plan_gemm_codes(m);
-    const size_t act_bytes = c.bm > 64 ? gemm_codes_act_table(L, m) +
-                                             size_t((m + 127) / 128 * 128) * size_t(L->k / L->group) * 8
-                                       : 0;
-    w.part = up(w.act + act_bytes);
-    const size_t part_bytes =
-        c.bm <= 64 ? size_t(kGemmMaxSplit) * size_t((m + c.bm - 1) / c.bm * c.bm) * size_t(L->n) * 4 : 0;
-    w.total = up(w.part + part_bytes);
-    return w;
-  }
-  const GemmPlan p = plan_gemm(m, L->n);
   const size_t act_bytes = p.xf ? 0 : size_t((m + 127) / 128 * 128) * size_t(L->k) * 2;
   w.part = up(w.act + act_bytes);
   const size_t part_bytes =

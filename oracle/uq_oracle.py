@@ -36,14 +36,8 @@ page leaves open is a *reading*; each is named where it is used:
         are (s, z) fp16 pairs per group, interleaved [n, k/G, 2]; NF4 params are
         one fp16 absmax per group [n, k/64].
   R-Y   GEMV:  y = x . w'^T in fp64 from fp16 x.
-        GEMM (bf16 matrix-core path): x is cast to bf16 (round to nearest
-        even from fp32).  R-GF: for INT2 / INT4 / INT8 layouts whose groups
-        hold 64 or more codes, the matrix cores take the integer codes, which
-        bf16 holds exactly, and each group's scale and zero are applied in
-        fp32 afterwards, so the weights enter unrounded:
-        y = bf16(x) . w'^T.  For the other layouts (groups of 16 or 32, and
-        NF4, whose codebook values are not integers) the dequantized weights
-        are cast to bf16 as well: y = bf16(x) . bf16(w')^T.  All in fp64.
+        GEMM (bf16 matrix-core path): y = bf16(x) . bf16(w')^T in fp64, both
+        casts round-to-nearest-even from fp32.
 """
 from __future__ import annotations
 
@@ -57,8 +51,7 @@ __all__ = [
     "dequant_int", "quantize_nf4", "dequant_nf4", "pack_codes", "unpack_codes",
     "pack_params_int", "unpack_params_int", "pack_params_nf4",
     "unpack_params_nf4", "quantize_pack", "dequant_packed", "gemv_ref",
-    "bf16_rne", "gemm_ref", "gemm_ref_codes", "gemm_contracts_codes",
-    "gemm_layout_ref", "NF4_PSTAR",
+    "bf16_rne", "gemm_ref", "NF4_PSTAR",
 ]
 
 # Scheme names and widths (Ultra LLM Engine, Highlights table, Quantization
@@ -260,25 +253,7 @@ def bf16_rne(a: np.ndarray) -> np.ndarray:
 
 
 def gemm_ref(x16: np.ndarray, wdq: np.ndarray) -> np.ndarray:
-    """y = bf16(x) . bf16(w')^T in fp64 (bf16 matrix-core path, weights cast)."""
+    """y = bf16(x) . bf16(w')^T in fp64 (bf16 matrix-core path)."""
     xb = bf16_rne(x16.astype(np.float32)).astype(np.float64)
     wb = bf16_rne(wdq).astype(np.float64)
     return xb @ wb.T
-
-
-def gemm_ref_codes(x16: np.ndarray, wdq: np.ndarray) -> np.ndarray:
-    """y = bf16(x) . w'^T in fp64 (bf16 matrix-core path on the integer codes,
-    reading R-GF: only the activations are cast)."""
-    xb = bf16_rne(x16.astype(np.float32)).astype(np.float64)
-    return xb @ wdq.astype(np.float64).T
-
-
-def gemm_contracts_codes(scheme: str, group: int) -> bool:
-    """Reading R-GF: the GEMM multiplies the integer codes (not bf16(w')) for
-    INT2 / INT4 / INT8 layouts with groups of 64 or more codes."""
-    return scheme in ("int2", "int4", "int8") and group >= 64
-
-
-def gemm_layout_ref(x16: np.ndarray, wdq: np.ndarray, scheme: str, group: int) -> np.ndarray:
-    """The GEMM reference of a layout: gemm_ref_codes or gemm_ref (R-GF)."""
-    return gemm_ref_codes(x16, wdq) if gemm_contracts_codes(scheme, group) else gemm_ref(x16, wdq)

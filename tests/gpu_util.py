@@ -80,26 +80,6 @@ def workload_on_device(lib, wl):
     return lay, codes, params, oracle_dequant(w, wl.scheme, wl.group), x
 
 
-SCHEME_NAMES = {1: "int2", 2: "int4", 3: "int8", 4: "nf4"}
-
-
-def lay_names(lay):
-    """(scheme name, group) of a layout struct."""
-    return SCHEME_NAMES[lay.scheme], lay.group
-
-
-def gemm_weights(wdq, scheme, group):
-    """The weights as the GEMM multiplies them (reading R-GF): w' itself for
-    the layouts that contract integer codes, bf16(w') for the others."""
-    return wdq if o.gemm_contracts_codes(scheme, group) else o.bf16_rne(wdq)
-
-
-def gemm_gate(y, x, wdq, scheme, group, label=""):
-    """A GEMM output against its layout's oracle reading, under the gate."""
-    return gate(y, o.gemm_layout_ref(x, wdq, scheme, group), o.bf16_rne(x.astype(np.float32)),
-                gemm_weights(wdq, scheme, group), label)
-
-
 def oracle_dequant(w, scheme, group):
     codes, params = o.quantize_pack(w, scheme, group)
     return o.dequant_packed(codes, params, scheme, group, w.shape[1])

@@ -232,10 +232,9 @@ def check_products_exact(o, seed=0, m=3, n=5, k=48):
     rng = np.random.default_rng(seed)
     x = rng.standard_normal((m, k)).astype(np.float16)
     w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
-    xb = o.bf16_rne(x.astype(np.float32)).astype(np.float64)
     for ref_fn, xs, ws in ((o.gemv_ref, x.astype(np.float64), w.astype(np.float64)),
-                           (o.gemm_ref, xb, o.bf16_rne(w).astype(np.float64)),
-                           (o.gemm_ref_codes, xb, w.astype(np.float64))):
+                           (o.gemm_ref, o.bf16_rne(x.astype(np.float32)).astype(np.float64),
+                            o.bf16_rne(w).astype(np.float64))):
         y = ref_fn(x, w)
         assert y.shape == (m, n)
         for i in range(m):
@@ -246,30 +245,12 @@ def check_products_exact(o, seed=0, m=3, n=5, k=48):
 
 
 def check_one_hot(o, seed=0, n=7, k=64):
-    """x = e_t returns column t of w' (GEMV, and the GEMM on integer codes) and
-    of bf16(w') (the GEMM on cast weights) exactly."""
+    """x = e_t returns column t of w' (GEMV) and of bf16(w') (GEMM) exactly."""
     rng = np.random.default_rng(seed)
     w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
     eye = np.eye(k, dtype=np.float16)
     assert np.array_equal(o.gemv_ref(eye, w), w.astype(np.float64).T)
     assert np.array_equal(o.gemm_ref(eye, w), o.bf16_rne(w).astype(np.float64).T)
-    assert np.array_equal(o.gemm_ref_codes(eye, w), w.astype(np.float64).T)
-
-
-def check_gemm_reading_per_layout(o):
-    """R-GF picks the integer-code GEMM for INT2/INT4/INT8 with groups of 64
-    or more and the cast-weight GEMM otherwise; on activations that bf16 holds
-    exactly, the integer-code GEMM equals the GEMV."""
-    assert [o.gemm_contracts_codes(s, g) for s, g in
-            (("int2", 16), ("int2", 32), ("int2", 64), ("int2", 128), ("int4", 32), ("int4", 64),
-             ("int4", 128), ("int8", 32), ("int8", 64), ("int8", 128), ("nf4", 64))] == \
-        [False, False, True, True, False, True, True, False, True, True, False]
-    rng = np.random.default_rng(3)
-    x = rng.integers(-64, 65, size=(3, 96)).astype(np.float16)  # small integers: exact in bf16
-    w = (rng.standard_normal((5, 96)) * 0.02).astype(np.float32)
-    assert np.array_equal(o.gemm_ref_codes(x, w), o.gemv_ref(x, w))
-    assert np.array_equal(o.gemm_layout_ref(x, w, "int4", 128), o.gemv_ref(x, w))
-    assert np.array_equal(o.gemm_layout_ref(x, w, "nf4", 64), o.gemm_ref(x, w))
 
 
 def check_int8_integer_matmul(o, seed=0, m=4, n=6, k=128, group=64):

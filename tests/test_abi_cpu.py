@@ -211,39 +211,23 @@ def test_gemm_noalloc_validation(lib):
     assert call(lay, 1, y=None) == 1
     assert call(lay, 0) == 2 and call(lay, 65537) == 2
     assert call(lay, 16, y=A + 4) == 4
-    lay32 = lib.layout("int4", 32, 11008, 4096)  # dequantizing GEMM: bf16 x in the workspace
     big = 4097  # bf16 x of 4224 rows x 4096 = 34.6 MB > 32 MiB
-    assert lib.uq_gemm_workspace_size(lay32, big) > lib.GEMM_NOALLOC_MAX_BYTES
-    assert call(lay32, big) == 7
-    for lay_ in (lay, lay32):
-        assert lib.uq_gemm_workspace_size(lay_, 256) <= lib.GEMM_NOALLOC_MAX_BYTES
-        assert lib.uq_gemm_workspace_size(lay_, 64) <= lib.GEMM_NOALLOC_MAX_BYTES
-    assert lib.uq_gemm_workspace_size(lay, 4097) > lib.GEMM_NOALLOC_MAX_BYTES  # codes: bf16 x too
-    assert call(lay, 4097) == 7
+    assert lib.uq_gemm_workspace_size(lay, big) > lib.GEMM_NOALLOC_MAX_BYTES
+    assert call(lay, big) == 7
+    assert lib.uq_gemm_workspace_size(lay, 256) <= lib.GEMM_NOALLOC_MAX_BYTES
+    assert lib.uq_gemm_workspace_size(lay, 64) <= lib.GEMM_NOALLOC_MAX_BYTES
 
 
 def test_gemm_workspace_size(lib):
-    """Sizes follow the documented regions: 64 KiB of counters; for the
-    dequantizing GEMM bf16 x in whole 128-row tiles for m > 64 and four partial
-    tiles of fp32 outputs (32- or 64-row tiles) for m <= 64; for the GEMM on
-    integer codes four partial tiles (16-, 32- or 64-row tiles) for m <= 64
-    and above that bf16 x in chain order with its per-group sums."""
+    """Sizes follow the documented regions: 64 KiB of counters, bf16 x in whole
+    128-row tiles for m > 64, and four partial tiles of fp32 outputs for m <= 64."""
     n, k = 11008, 4096
-    lay = lib.layout("int4", 32, n, k)
+    lay = lib.layout("int4", 128, n, k)
     up = lambda v: (v + 255) // 256 * 256  # noqa: E731
     assert lib.uq_gemm_workspace_size(lay, 16) == up(65536 + 4 * 32 * n * 4)
     assert lib.uq_gemm_workspace_size(lay, 64) == up(65536 + 4 * 64 * n * 4)
     assert lib.uq_gemm_workspace_size(lay, 256) == up(65536 + 256 * k * 2)
     assert lib.uq_gemm_workspace_size(lay, 300) == up(65536 + 384 * k * 2)
-    codes = lib.layout("int4", 128, n, k)
-    assert lib.uq_gemm_workspace_size(codes, 1) == up(65536 + 4 * 16 * n * 4)
-    assert lib.uq_gemm_workspace_size(codes, 16) == up(65536 + 4 * 16 * n * 4)
-    assert lib.uq_gemm_workspace_size(codes, 17) == up(65536 + 4 * 32 * n * 4)
-    assert lib.uq_gemm_workspace_size(codes, 64) == up(65536 + 4 * 64 * n * 4)
-    ng = k // 128
-    for m in (65, 256, 300):  # bf16 x in chain order (whole 128-row tiles), then (X, -128 X) per group
-        mp = (m + 127) // 128 * 128
-        assert lib.uq_gemm_workspace_size(codes, m) == up(65536 + up(mp * k * 2) + mp * ng * 8)
     for bad in (0, -1, 65537):
         with pytest.raises(lib.UQError) as e:
             lib.uq_gemm_workspace_size(lay, bad)

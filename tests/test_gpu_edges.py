@@ -9,7 +9,7 @@ import pytest
 
 import oracle as o
 import workloads
-from tests.gpu_util import Guarded, dev, gate, gemm_gate, lay_names, note, oracle_dequant, packed_on_device, product
+from tests.gpu_util import Guarded, dev, gate, note, oracle_dequant, packed_on_device, product
 
 pytestmark = pytest.mark.gpu
 
@@ -42,7 +42,9 @@ def check_products(lib, lay, codes, params, x, wdq, label, gemv_ms=(1, 8), gemm_
         gate(run(lib, "uq_gemv", lay, codes, params, x, m), o.gemv_ref(x[:m], wdq), x[:m], wdq, f"{label} gemv m={m}")
     for m in gemm_ms:
         note(f"{label} gemm m={m}")
-        gemm_gate(run(lib, "uq_gemm", lay, codes, params, x, m), x[:m], wdq, *lay_names(lay), f"{label} gemm m={m}")
+        xb = o.bf16_rne(x[:m].astype(np.float32))
+        gate(run(lib, "uq_gemm", lay, codes, params, x, m), o.gemm_ref(x[:m], wdq), xb, o.bf16_rne(wdq),
+             f"{label} gemm m={m}")
 
 
 @pytest.mark.parametrize("scheme,group", LAYOUTS)
@@ -111,7 +113,8 @@ def test_gemm_largest_m(lib):
     wdq = oracle_dequant(w, "int4", 32)
     note(f"gemm m={m} n={n} k={k}")
     y = run(lib, "uq_gemm", lay, codes, params, x, m)
-    gemm_gate(y, x, wdq, "int4", 32, "gemm m=65536")
+    xb = o.bf16_rne(x.astype(np.float32))
+    gate(y, o.gemm_ref(x, wdq), xb, o.bf16_rne(wdq), "gemm m=65536")
 
 
 @pytest.mark.parametrize("scheme,group", [("int2", 16), ("int2", 64), ("int4", 32), ("int4", 64), ("int4", 128),
@@ -145,5 +148,6 @@ def test_small_and_mixed_activations(lib, scheme, group):
             gate(y[i:i + 1], ref[i:i + 1], mixed[i:i + 1], wdq, f"{scheme} G{group} mixed m={m} row {i}")
     note(f"small x gemm {scheme} G{group}")
     xs = (xf * np.float32(1e-4)).astype(np.float16)
-    gemm_gate(run(lib, "uq_gemm", lay, codes, params, xs, 16), xs[:16], wdq, scheme, group,
-              f"{scheme} G{group} small x gemm")
+    xb = o.bf16_rne(xs[:16].astype(np.float32))
+    gate(run(lib, "uq_gemm", lay, codes, params, xs, 16), o.gemm_ref(xs[:16], wdq), xb, o.bf16_rne(wdq),
+         f"{scheme} G{group} small x gemm")

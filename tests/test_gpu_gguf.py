@@ -10,7 +10,7 @@ import pytest
 
 import oracle as o
 import workloads
-from tests.gpu_util import Guarded, dev, gate, gemm_gate, lay_names, note, product
+from tests.gpu_util import Guarded, dev, gate, note, product
 
 pytestmark = pytest.mark.gpu
 
@@ -60,8 +60,9 @@ def test_gguf_products(lib, fmt, t):
                  f"gguf gemv {fmt} {n}x{k} m={m}")
         for m in (16, 130):
             note(f"gguf gemm {fmt} n={n} k={k} m={m}")
-            gemm_gate(run(lib, "uq_gemm", lay, codes, params, x, m), x[:m], wdq, *lay_names(lay),
-                      f"gguf gemm {fmt} {n}x{k} m={m}")
+            xb = o.bf16_rne(x[:m].astype(np.float32))
+            gate(run(lib, "uq_gemm", lay, codes, params, x, m), o.gemm_ref(x[:m], wdq), xb, o.bf16_rne(wdq),
+                 f"gguf gemm {fmt} {n}x{k} m={m}")
         q_w, s16, z16 = o.gguf_as_int(blob, t, n, k)
         q_x, s_x = o.quantize_activations(x[:8], 32)
         y_ref = o.gemv_a8_ref(q_x, s_x, q_w, s16, z16, 32)
@@ -99,6 +100,6 @@ def test_gguf_extreme_scales(lib, fmt, t):
         note(f"gguf extreme scales {fmt} {fn} m={m}")
         y = run(lib, fn, lay, codes, params, xs, m)
         if fn == "uq_gemm":
-            gemm_gate(y, xs[:m], wdq, *lay_names(lay), fn)
+            gate(y, o.gemm_ref(xs[:m], wdq), o.bf16_rne(xs[:m].astype(np.float32)), o.bf16_rne(wdq), fn)
         else:
             gate(y, o.gemv_ref(xs[:m], wdq), xs[:m], wdq, fn)

@@ -9,8 +9,7 @@ import pytest
 
 import oracle as o
 import workloads
-from tests.gpu_util import (Guarded, dev, gate, gemm_gate, gemm_weights, lay_names, note, oracle_dequant,
-                            packed_on_device, workload_on_device)
+from tests.gpu_util import Guarded, dev, gate, note, oracle_dequant, packed_on_device, workload_on_device
 
 pytestmark = pytest.mark.gpu
 
@@ -201,7 +200,8 @@ def test_gemm_parity_small(lib, scheme, group):
         for m in (1, 15, 16, 17, 40, 64, 130):
             note(f"gemm {scheme} G{group} n={n} k={k} m={m}")
             y = run_gemm(lib, lay, codes, params, x, m)
-            gemm_gate(y, x[:m], wdq, scheme, group, f"gemm {scheme} G{group} m={m}")
+            xb = o.bf16_rne(x[:m].astype(np.float32))
+            gate(y, o.gemm_ref(x[:m], wdq), xb, o.bf16_rne(wdq), f"gemm {scheme} G{group} m={m}")
 
 
 @pytest.mark.parametrize("scheme,group", [("int4", 128), ("int2", 16), ("int8", 64), ("nf4", 64)])
@@ -217,14 +217,13 @@ def test_gemm_several_row_tiles(lib, scheme, group):
         for m in (129, 255, 256, 257, 300, 513):
             note(f"gemm row tiles {scheme} G{group} n={n} m={m}")
             y = run_gemm(lib, lay, codes, params, x, m)
-            gemm_gate(y, x[:m], wdq, scheme, group, f"gemm {scheme} G{group} n={n} m={m}")
+            xb = o.bf16_rne(x[:m].astype(np.float32))
+            gate(y, o.gemm_ref(x[:m], wdq), xb, o.bf16_rne(wdq), f"gemm {scheme} G{group} n={n} m={m}")
 
 
 @pytest.mark.parametrize("scheme,group", ALL_LAYOUTS)
 def test_gemm_identity_bit_exact(lib, scheme, group):
-    """X = I (M = K) returns the GEMM's weights transposed exactly: w' for the
-    layouts that contract integer codes (each output is fma(s, q, z)), bf16(w')
-    for the others."""
+    """X = I (M = K) returns bf16(w')^T exactly."""
     n, k = 70, 256
     w, _ = workloads.make_random(n, k, 1, seed=13, outliers=True)
     lay, codes, params = packed_on_device(lib, scheme, group, w)
@@ -232,7 +231,7 @@ def test_gemm_identity_bit_exact(lib, scheme, group):
     x = np.eye(k, dtype=np.float16)
     note(f"gemm identity {scheme} G{group}")
     y = run_gemm(lib, lay, codes, params, x, k)
-    want = gemm_weights(wdq, scheme, group).T
+    want = o.bf16_rne(wdq).T
     assert np.array_equal(y.view(np.uint32), np.ascontiguousarray(want).view(np.uint32))
 
 
@@ -244,26 +243,54 @@ def test_gemm_k_tail(lib, k):
     wdq = oracle_dequant(w, "int4", 32)
     note(f"gemm k-tail k={k}")
     y = run_gemm(lib, lay, codes, params, x, 33)
-    gemm_gate(y, x, wdq, "int4", 32, f"k-tail {k}")
+    gate(y, o.gemm_ref(x, wdq), o.bf16_rne(x.astype(np.float32)), o.bf16_rne(wdq), f"k-tail {k}")
 
 
 def test_gemm_batched_equivalence(lib):
-    """Row i of an M-row GEMM equals the single-row GEMM of x[i] to within
-    fp32 reassociation (the pages' batched-decode equivalence; the row tile
-    and the K split change with M, and with them the order of the fp32 sums).
-    Both layouts: one that contracts the integer codes, one that dequantizes.
-    (GEMM and GEMV rows are not compared under the gate: the bf16 cast of x
-    alone moves the GEMM by ~1.7e-3 relative to the fp16 GEMV, which is why
-    the GEMM's oracle applies the same cast.)
+    """Row i of an M-row GEMM equals the single-row GEMM of x[i].
+
+    Up to M = 16 (with K a multiple of 1024) one streaming kernel with 16-row
+    tiles serves every M, with one K order and one K split, so rows agree bit
+    for bit; above, other tiles cut K differently and rows agree to fp32
+    reassociation.  (GEMM and GEMV rows are not compared under the gate: the
+    bf16 rounding of w' alone moves the GEMM by ~2e-3 relative to the fp16
+    GEMV, which is why the GEMM's oracle applies the same casts.)
     """
-    for scheme, group in (("int4", 128), ("int4", 32)):
-        w, x = workloads.make_random(300, 2048, 130, seed=15)
+    w, x = workloads.make_random(300, 2048, 130, seed=15)
+    lay, codes, params = packed_on_device(lib, "int4", 128, w)
+    ys = np.stack([run_gemm(lib, lay, codes, params, x[i:i + 1], 1)[0] for i in range(130)])
+    for m in (5, 16):
+        note(f"gemm batched equivalence m={m}")
+        y = run_gemm(lib, lay, codes, params, x, m)
+        assert np.array_equal(y.view(np.uint32), ys[:m].view(np.uint32)), m
+    for m in (17, 32, 40, 64, 130):
+        note(f"gemm batched equivalence m={m}")
+        y = run_gemm(lib, lay, codes, params, x, m)
+        assert np.abs(y - ys[:m]).max() <= 1e-5 * np.abs(ys[:m]).max(), m
+
+
+@pytest.mark.parametrize("scheme,group", ALL_LAYOUTS)
+def test_gemm_streaming_rows(lib, scheme, group):
+    """Up to 32 rows with K a multiple of 1024 the GEMM streams codes into
+    registers: 16- and 32-row tiles, N with a ragged last tile of 64 weight
+    rows, K over one block and over several (with and without a K split)."""
+    for n, k, seed in ((77, 1024, 41), (200, 3072, 42), (2100, 2048, 43)):
+        w, x = workloads.make_random(n, k, 32, seed=seed, outliers=True)
         lay, codes, params = packed_on_device(lib, scheme, group, w)
-        ys = np.stack([run_gemm(lib, lay, codes, params, x[i:i + 1], 1)[0] for i in range(130)])
-        for m in (16, 40, 64, 130):
-            note(f"gemm batched equivalence {scheme} G{group} m={m}")
+        wdq = oracle_dequant(w, scheme, group)
+        for m in (1, 7, 16, 17, 31, 32):
+            note(f"gemm streaming {scheme} G{group} n={n} k={k} m={m}")
             y = run_gemm(lib, lay, codes, params, x, m)
-            assert np.abs(y - ys[:m]).max() <= 1e-5 * np.abs(ys).max(), (scheme, group, m)
+            xb = o.bf16_rne(x[:m].astype(np.float32))
+            gate(y, o.gemm_ref(x[:m], wdq), xb, o.bf16_rne(wdq), f"gemm streaming {scheme} G{group} n={n} k={k} m={m}")
+        for m in (16, 32):
+            # rows of I: each output is one product, exact through the K split
+            note(f"gemm streaming identity {scheme} G{group} n={n} k={k} m={m}")
+            e = np.zeros((m, k), dtype=np.float16)
+            e[np.arange(m), (np.arange(m) * 37) % k] = 1.0
+            y = run_gemm(lib, lay, codes, params, e, m)
+            want = o.bf16_rne(wdq).T[(np.arange(m) * 37) % k]
+            assert np.array_equal(y.view(np.uint32), np.ascontiguousarray(want).view(np.uint32)), m
 
 
 @pytest.mark.parametrize("scheme,group", [("int4", 128), ("int2", 16), ("int8", 32), ("nf4", 64), ("int4", 32)])
@@ -279,14 +306,15 @@ def test_gemm_k_split(lib, scheme, group):
         for m in (1, 16, 33, 64):
             note(f"gemm k split {scheme} G{group} n={n} k={k} m={m}")
             y = run_gemm(lib, lay, codes, params, x, m)
-            gemm_gate(y, x[:m], wdq, scheme, group, f"gemm split {scheme} G{group} n={n} k={k} m={m}")
+            xb = o.bf16_rne(x[:m].astype(np.float32))
+            gate(y, o.gemm_ref(x[:m], wdq), xb, o.bf16_rne(wdq), f"gemm split {scheme} G{group} n={n} k={k} m={m}")
 
 
 @pytest.mark.parametrize("scheme,group", [("int4", 128), ("int2", 16), ("int8", 64), ("nf4", 64)])
 def test_gemm_k_split_identity_bit_exact(lib, scheme, group):
     """X = the first 64 rows of I with K = 2560 (K split over four workgroups):
     each output is one product, so the partial tiles and their sum are exact
-    and y is the GEMM's weights (w' or bf16(w'), by layout) transposed, bit for bit."""
+    and y = bf16(w')^T[:64] bit for bit."""
     n, k = 70, 2560
     w, _ = workloads.make_random(n, k, 1, seed=34, outliers=True)
     lay, codes, params = packed_on_device(lib, scheme, group, w)
@@ -294,7 +322,7 @@ def test_gemm_k_split_identity_bit_exact(lib, scheme, group):
     x = np.eye(k, dtype=np.float16)[:64]
     note(f"gemm k split identity {scheme} G{group}")
     y = run_gemm(lib, lay, codes, params, x, 64)
-    want = gemm_weights(wdq, scheme, group).T[:64]
+    want = o.bf16_rne(wdq).T[:64]
     assert np.array_equal(y.view(np.uint32), np.ascontiguousarray(want).view(np.uint32))
 
 
@@ -337,7 +365,7 @@ def test_gemm_graph_replay(lib):
         got = y.cpu().numpy().copy()
         if want is None:
             want = run_gemm(lib, lay, codes, params, x, 64)
-            gemm_gate(want, x, wdq, "int4", 64, "graph eager")
+            gate(want, o.gemm_ref(x, wdq), o.bf16_rne(x.astype(np.float32)), o.bf16_rne(wdq), "graph eager")
         assert np.array_equal(got.view(np.uint32), want.reshape(-1).view(np.uint32)), r
         lib.uq_gemm(lay, codes, params, xd, y, 16, ws)  # eager work in between, same workspace
         torch.cuda.synchronize()
@@ -404,5 +432,6 @@ def test_full_workload(lib, name):
             rel, mx = gate(y, o.gemv_ref(x[:m], wdq), x[:m], wdq, f"{name} m={m}")
         else:
             y = run_gemm(lib, lay, codes, params, x, m)
-            rel, mx = gemm_gate(y, x[:m], wdq, *lay_names(lay), f"{name} m={m}")
+            rel, mx = gate(y, o.gemm_ref(x[:m], wdq), o.bf16_rne(x[:m].astype(np.float32)),
+                           o.bf16_rne(wdq), f"{name} m={m}")
         note(f"  rel-L2 {rel:.3e}  max-abs {mx:.3e}")

@@ -46,10 +46,6 @@ def test_one_hot():
     pins.check_one_hot(o)
 
 
-def test_gemm_reading_per_layout():
-    pins.check_gemm_reading_per_layout(o)
-
-
 def test_int8_unit_scale_is_integer_matmul():
     pins.check_int8_integer_matmul(o)
 

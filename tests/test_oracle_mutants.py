@@ -86,19 +86,6 @@ def gemm_no_x_cast(x16, wdq):
     return x16.astype(np.float64) @ o.bf16_rne(wdq).astype(np.float64).T
 
 
-def gemm_codes_casts_weights(x16, wdq):
-    xb = o.bf16_rne(x16.astype(np.float32)).astype(np.float64)
-    return xb @ o.bf16_rne(wdq).astype(np.float64).T
-
-
-def gemm_codes_no_x_cast(x16, wdq):
-    return x16.astype(np.float64) @ wdq.astype(np.float64).T
-
-
-def codes_rule_includes_g32(scheme, group):
-    return scheme in ("int2", "int4", "int8") and group >= 32
-
-
 def bf16_truncate(a):
     u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
     return (u & np.uint32(0xFFFF0000)).view(np.float32)
@@ -253,12 +240,6 @@ CASES = [
      lambda ns: pins.check_products_exact(ns, k=64)),
     ("GEMM skips the bf16 cast of x", dict(gemm_ref=gemm_no_x_cast),
      lambda ns: pins.check_products_exact(ns)),
-    ("GEMM on codes casts the weights", dict(gemm_ref_codes=gemm_codes_casts_weights),
-     lambda ns: pins.check_products_exact(ns)),
-    ("GEMM on codes skips the bf16 cast of x", dict(gemm_ref_codes=gemm_codes_no_x_cast),
-     lambda ns: pins.check_products_exact(ns)),
-    ("GEMM on codes for groups of 32", dict(gemm_contracts_codes=codes_rule_includes_g32),
-     lambda ns: pins.check_gemm_reading_per_layout(ns)),
     ("bf16 truncates", dict(bf16_rne=bf16_truncate),
      lambda ns: pins.check_bf16(ns)),
     ("RoPE pairs neighbours", dict(rmsnorm_rope=rope_interleaved),

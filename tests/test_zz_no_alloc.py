@@ -8,7 +8,7 @@ import pytest
 
 import oracle as o
 import workloads
-from tests.gpu_util import Guarded, dev, gemm_gate, note, oracle_dequant, packed_on_device
+from tests.gpu_util import Guarded, dev, gate, note, oracle_dequant, packed_on_device
 
 pytestmark = pytest.mark.gpu
 
@@ -44,12 +44,13 @@ def test_noalloc_matches_uq_gemm(lib, scheme, group, n, k, ms):
         note(f"noalloc {scheme} G{group} n={n} k={k} m={m}")
         got, want = _both(lib, lay, codes, params, x, m)
         assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), (scheme, m)
-        gemm_gate(got, x[:m], wdq, scheme, group, f"noalloc {scheme} m={m}")
+        xb = o.bf16_rne(x[:m].astype(np.float32))
+        gate(got, o.gemm_ref(x[:m], wdq), xb, o.bf16_rne(wdq), f"noalloc {scheme} m={m}")
 
 
 def test_noalloc_refuses_more_than_its_scratch(lib):
     """A call whose workspace would not fit the fixed scratch is refused before any HIP call."""
-    lay = lib.layout("int4", 32, 4096, 4096)  # the dequantizing GEMM keeps bf16 x in the workspace
+    lay = lib.layout("int4", 128, 4096, 4096)
     m = 65536
     assert lib.uq_gemm_workspace_size(lay, m) > lib.GEMM_NOALLOC_MAX_BYTES
     with pytest.raises(lib.UQError) as e:
