@@ -785,32 +785,35 @@ hipError_t launch(const uq_layout* L, const void* codes, const void* params, con
 
 // ---- Up to 32 activation rows: codes streamed straight into registers ----
 //
-// Up to 32 rows the GEMM is bound by memory traffic and latency, not by the
-// matrix cores, so it is organised like the GEMV: a workgroup of four waves
-// owns 64 weight rows (16 per wave) and a K range (the K split), and per
-// block of XB activations of that range it
-//   * issues the loads of the block's activations and of its rows' group
+// Up to 32 rows the GEMM is bound by memory traffic and by the dequantizing
+// arithmetic, not by the matrix cores, so it is organised like the GEMV: a
+// workgroup of four waves owns 64 weight rows (16 per wave) and a K range
+// (the K split), which it walks in blocks of XB -- requesting the whole range
+// at once when it is at most NB blocks, else keeping one block's loads in
+// flight while the previous block is multiplied:
+//   * the loads of a block are its activations and its rows' group
 //     parameters (consecutive lanes, consecutive groups of a row), then the
 //     codes each lane multiplies, directly in the MFMA layout: lane l takes
 //     weight row l % 16, and of the row's 16-byte pieces of the block the
 //     pieces 4 q + l / 16, so the four lanes of a row read 64 contiguous
 //     bytes per load -- within an MFMA any k order serves as long as A and B
-//     agree, and the activations are staged in the same order,
-//   * stages the activations in LDS (fp16 -> bf16, round to nearest even) and
-//     the parameters,
-//   * synchronises once and runs v_mfma_f32_16x16x32_bf16 over the block,
-//     each B operand dequantized from the lane's codes exactly as in the
-//     pipelined kernel (bf16(fma(q, s, z))), so the products are the same.
-// No workgroup barrier sits between a block's loads and its products.
-template <int S, int G, int TM>
+//     agree, and the activations are staged in the same order;
+//   * once they land, the activations are staged in LDS (fp16 -> bf16, round
+//     to nearest even) with the parameters, in one of NBUF buffers (with
+//     one, a barrier first lets every wave finish reading the previous
+//     block);
+//   * after one barrier the block's v_mfma_f32_16x16x32_bf16 run, each B
+//     operand dequantized from the lane's codes exactly as in the pipelined
+//     kernel (bf16(fma(q, s, z))), so the products are the same.
+template <int S, int G, int TM, int XB_>
 struct SGeo {
   static constexpr int BM = 16 * TM, BN = 64, NT = 256;
   static constexpr int bits = Fmt<S>::bits;
   static constexpr int PB = param_bytes_per_group(S);
-  static constexpr int XB = 1024 / TM;          // K per block: the activations are BM x XB bf16 = 32 KB
+  static constexpr int XB = XB_;                // K per block
   static constexpr int Q = XB / 4;              // codes of one lane per block
   static constexpr int CP = 128 / bits;         // codes in a 16-byte piece
-  static constexpr int NJ = Q / 8;              // MFMAs per block
+  static constexpr int NJ = Q / 8;              // MFMAs per block and row tile
   static constexpr int QW = Q * bits / 32;      // code dwords of a lane per block
   static constexpr int XPITCH = XB * 2 + 16;
   static constexpr int XI = BM * XB / 8;        // 8-activation pieces staged per block
@@ -818,20 +821,28 @@ struct SGeo {
   static constexpr int NGB = XB / G;            // groups per block
   static constexpr int PPB = BN * NGB;          // parameters per block
   static constexpr int PPT = (PPB + NT - 1) / NT;
-  static_assert(XI % NT == 0 && QW % 4 == 0 && NJ % 2 == 0 && Q % G == 0, "block geometry");
+  static_assert(XI % NT == 0 && QW % 4 == 0 && NJ % 2 == 0 && Q % 16 == 0, "block geometry");
 };
 
-template <int S, int G, int TM>
+// One block's loads, in registers until staged.
+template <class Ge>
+struct StreamLoads {
+  uint4 x[Ge::XPT];
+  uint32_t p[Ge::PPT];
+  uint32_t run[Ge::QW];
+};
+
+template <int S, int G, int TM, int XB, int NB, int NBUF>
 __global__ __launch_bounds__(256) void gemm_stream_kernel(const uint8_t* __restrict__ codes,
                                                           const uint8_t* __restrict__ params,
                                                           const uint16_t* __restrict__ x, float* __restrict__ y,
                                                           int n, int k, int m, int tiles_m, int ksplit,
                                                           float* __restrict__ part, unsigned* __restrict__ arrivals) {
-  using Ge = SGeo<S, G, TM>;
-  constexpr int bits = Ge::bits, BM = Ge::BM, BN = Ge::BN, NT = Ge::NT, XB = Ge::XB, NJ = Ge::NJ;
+  using Ge = SGeo<S, G, TM, XB>;
+  constexpr int bits = Ge::bits, BM = Ge::BM, BN = Ge::BN, NT = Ge::NT, NJ = Ge::NJ;
   constexpr int QW = Ge::QW, NGB = Ge::NGB;
-  __shared__ __attribute__((aligned(16))) uint8_t xs[BM * Ge::XPITCH];
-  __shared__ __attribute__((aligned(16))) uint32_t ps[Ge::PPB];
+  __shared__ __attribute__((aligned(16))) uint8_t xs[NBUF][BM * Ge::XPITCH];
+  __shared__ __attribute__((aligned(16))) uint32_t ps[NBUF][Ge::PPT * NT];  // PPB used, the rest written blindly
   __shared__ float nf4[16];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -852,23 +863,18 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const uint8_t* __restr
     if (tid < 16) nf4[tid] = nf4_value(tid);
   }
 
-  f32x4 yacc[TM];
-#pragma unroll
-  for (int a = 0; a < TM; ++a) yacc[a] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-
-  for (int blk = b0; blk < b1; ++blk) {
+  // issue a block's loads (activation rows past M and weight rows past N
+  // clamped to the last: loaded, never stored)
+  auto issue = [&](StreamLoads<Ge>& ld, int blk) {
     const int k0 = blk * XB;
-    // (1) loads: activations and parameters for staging, then the lane's codes
-    uint4 xv[Ge::XPT];
 #pragma unroll
     for (int i = 0; i < Ge::XPT; ++i) {
       const int it = i * NT + tid;
       const int row = it / (XB / 8), c = it % (XB / 8);
       int mr = bm + row;
       mr = mr < m ? mr : m - 1;
-      xv[i] = *reinterpret_cast<const uint4*>(x + size_t(mr) * size_t(k) + k0 + 8 * c);
+      ld.x[i] = *reinterpret_cast<const uint4*>(x + size_t(mr) * size_t(k) + k0 + 8 * c);
     }
-    uint32_t pv[Ge::PPT];
 #pragma unroll
     for (int i = 0; i < Ge::PPT; ++i) {
       int q = i * NT + tid;
@@ -876,41 +882,50 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const uint8_t* __restr
       int pr = bn + q / NGB;
       pr = pr < n ? pr : n - 1;
       const uint8_t* src = params + (size_t(pr) * size_t(ng) + k0 / G + q % NGB) * Ge::PB;
-      if constexpr (Ge::PB == 4) pv[i] = load_stream<uint32_t>(src);
-      else pv[i] = load_stream<uint16_t>(src);
+      if constexpr (Ge::PB == 4) ld.p[i] = load_stream<uint32_t>(src);
+      else ld.p[i] = load_stream<uint16_t>(src);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    uint32_t run[QW];
 #pragma unroll
     for (int q = 0; q < QW / 4; ++q) {
       const uint4 v = load_stream<uint4>(crow + size_t(k0) * bits / 8 + 64 * q);
-      run[4 * q] = v.x; run[4 * q + 1] = v.y; run[4 * q + 2] = v.z; run[4 * q + 3] = v.w;
+      ld.run[4 * q] = v.x;
+      ld.run[4 * q + 1] = v.y;
+      ld.run[4 * q + 2] = v.z;
+      ld.run[4 * q + 3] = v.w;
     }
-    __builtin_amdgcn_sched_barrier(0);
-    // (2) stage: 8 activations -> bf16 at slot 32 j + 8 kb of its row, where
-    //     position p of the block is in piece p / CP, read by k-block
-    //     (p / CP) % 4 as its code c = (p / CP / 4) CP + p % CP, of MFMA c / 8
-    wait_lds_barrier();
+  };
+
+  f32x4 yacc[TM];
+#pragma unroll
+  for (int a = 0; a < TM; ++a) yacc[a] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // stage a block's activations and parameters in LDS buffer `buf`: 8
+  // activations -> bf16 at slot 32 j + 8 kb of their row, where position p of
+  // the block is in piece p / CP, read by k-block (p / CP) % 4 as its code
+  // c = (p / CP / 4) CP + p % CP, of MFMA c / 8.  (A buffer is written two
+  // blocks after it was last read, past a barrier that follows the reads.)
+  auto stage = [&](const StreamLoads<Ge>& ld, int buf, bool live) {
+    uint8_t* xb = xs[buf];
 #pragma unroll
     for (int i = 0; i < Ge::XPT; ++i) {
       const int it = i * NT + tid;
       const int row = it / (XB / 8), c = it % (XB / 8);
       const int p = 8 * c, kbs = (p / Ge::CP) % 4, j = ((p / Ge::CP / 4) * Ge::CP + p % Ge::CP) / 8;
-      const uint4 h = xv[i];
+      const uint4 h = ld.x[i];
       const uint4 v = make_uint4(pack_bf16(h2f(uint16_t(h.x)), h2f(uint16_t(h.x >> 16))),
                                  pack_bf16(h2f(uint16_t(h.y)), h2f(uint16_t(h.y >> 16))),
                                  pack_bf16(h2f(uint16_t(h.z)), h2f(uint16_t(h.z >> 16))),
                                  pack_bf16(h2f(uint16_t(h.w)), h2f(uint16_t(h.w >> 16))));
-      *reinterpret_cast<uint4*>(xs + row * Ge::XPITCH + (32 * j + 8 * kbs) * 2) = v;
+      *reinterpret_cast<uint4*>(xb + row * Ge::XPITCH + (32 * j + 8 * kbs) * 2) = live ? v : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < Ge::PPT; ++i) {
-      const int q = i * NT + tid;
-      if (q < Ge::PPB) ps[q] = pv[i];
-    }
-    wait_lds_barrier();
-    // (3) the block's MFMAs, two at a time (one Codes of 16 codes each pair)
-    const uint32_t* prw = ps + (16 * wave + l16) * NGB;
+    for (int i = 0; i < Ge::PPT; ++i) ps[buf][i * NT + tid] = ld.p[i];
+  };
+  // a block's MFMAs from LDS buffer `buf`, two at a time (one Codes of 16
+  // codes each pair)
+  auto compute = [&](const uint32_t (&run)[QW], int buf) {
+    const uint8_t* xb = xs[buf];
+    const uint32_t* prw = ps[buf] + (16 * wave + l16) * NGB;
 #pragma unroll
     for (int jp = 0; jp < NJ / 2; ++jp) {
       Codes<S> cc;
@@ -932,10 +947,48 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const uint8_t* __restr
 #pragma unroll
         for (int a = 0; a < TM; ++a) {
           const bf16x8 av =
-              *reinterpret_cast<const bf16x8*>(xs + (16 * a + l16) * Ge::XPITCH + (32 * j + 8 * kb) * 2);
+              *reinterpret_cast<const bf16x8*>(xb + (16 * a + l16) * Ge::XPITCH + (32 * j + 8 * kb) * 2);
           yacc[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, yacc[a], 0, 0, 0);
         }
       }
+    }
+  };
+
+  if constexpr (NB > 0) {
+    // The whole K range (at most NB blocks; the launcher guarantees it) is
+    // requested up front, block by block, and multiplied as it lands.
+    // Slots past the range reload the last block and multiply it by zero
+    // activations (adding exact zeros to sums that start at +0), so the code
+    // has no branch: every load is issued before the first wait and each
+    // wait is an exact count.
+    const int nb = b1 - b0;
+    StreamLoads<Ge> ld[NB];
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) {
+      issue(ld[bb], b0 + (bb < nb ? bb : nb - 1));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) {
+      if (NBUF == 1 && bb > 0) wait_lds_barrier();  // the buffer's last reads are done
+      stage(ld[bb], bb % NBUF, bb < nb);
+      wait_lds_barrier();
+      compute(ld[bb].run, bb % NBUF);
+    }
+  } else {
+    // One block in flight while the previous one is multiplied.
+    StreamLoads<Ge> ld;
+    issue(ld, b0);
+    for (int blk = b0; blk < b1; ++blk) {
+      const int buf = (blk - b0) % NBUF;
+      if (NBUF == 1 && blk > b0) wait_lds_barrier();  // the buffer's last reads are done
+      stage(ld, buf, true);
+      uint32_t run[QW];
+#pragma unroll
+      for (int w = 0; w < QW; ++w) run[w] = ld.run[w];
+      if (blk + 1 < b1) issue(ld, blk + 1);
+      wait_lds_barrier();
+      compute(run, buf);
     }
   }
 
@@ -999,38 +1052,44 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const uint8_t* __restr
 
 int device_cus();
 
-template <int S, int G, int TM>
+template <int S, int G, int TM, int XB, int NB, int NBUF>
 hipError_t launch_stream_t(const uq_layout* L, const void* codes, const void* params, const uint16_t* x, float* y,
                            int m, float* part, unsigned* arrivals, hipStream_t stream) {
-  using Ge = SGeo<S, G, TM>;
+  using Ge = SGeo<S, G, TM, XB>;
   int n = int(L->n), k = int(L->k);
   int tiles_m = (m + Ge::BM - 1) / Ge::BM;
   const int64_t tiles = int64_t(tiles_m) * ((int64_t(n) + Ge::BN - 1) / Ge::BN);
   // K split: the workgroups the chip holds at once over the tiles, at most
   // kGemmMaxSplit (the workspace holds that many partial tiles of 32 rows),
-  // at least one block each.
+  // at least two blocks each where K has them.
   int ksplit = 1;
   if (tiles <= kGemmMaxSplitTiles) {
     static std::atomic<int> cached{0};
     int occ = cached.load(std::memory_order_relaxed);
     if (occ <= 0) {
       if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-              &occ, reinterpret_cast<const void*>(&gemm_stream_kernel<S, G, TM>), Ge::NT, 0) != hipSuccess ||
+              &occ, reinterpret_cast<const void*>(&gemm_stream_kernel<S, G, TM, XB, NB, NBUF>), Ge::NT, 0) != hipSuccess ||
           occ < 1)
         occ = 1;
       cached.store(occ, std::memory_order_relaxed);
     }
     int64_t ks = int64_t(device_cus()) * occ / tiles;
     if (ks > kGemmMaxSplit) ks = kGemmMaxSplit;
-    if (ks > k / Ge::XB) ks = k / Ge::XB;
+    if (ks > k / XB / (NB == 0 ? 2 : 1)) ks = k / XB / (NB == 0 ? 2 : 1);
     ksplit = ks > 1 ? int(ks) : 1;
+  }
+  if (NB > 0) {
+    // every split holds at most NB blocks
+    const int nblk = k / XB;
+    while (ksplit < kGemmMaxSplit && (nblk + ksplit - 1) / ksplit > NB) ++ksplit;
+    if ((nblk + ksplit - 1) / ksplit > NB || ksplit > nblk) return hipErrorInvalidValue;
   }
   const int64_t nb = tiles * ksplit;
   if (nb > 0x7fffffff) return hipErrorInvalidValue;
   const uint8_t* c8 = static_cast<const uint8_t*>(codes);
   const uint8_t* p8 = static_cast<const uint8_t*>(params);
   void* args[] = {&c8, &p8, (void*)&x, &y, &n, &k, &m, &tiles_m, &ksplit, &part, &arrivals};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&gemm_stream_kernel<S, G, TM>), dim3(unsigned(nb)),
+  return hipLaunchKernel(reinterpret_cast<const void*>(&gemm_stream_kernel<S, G, TM, XB, NB, NBUF>), dim3(unsigned(nb)),
                          dim3(Ge::NT), args, 0, stream);
 }
 
@@ -1122,13 +1181,20 @@ hipError_t launch_gemm(const uq_layout* L, const void* codes, const void* params
   unsigned* arrivals = reinterpret_cast<unsigned*>(ws + wl.counters);
   uint16_t* xb = plan.xf ? const_cast<uint16_t*>(x) : reinterpret_cast<uint16_t*>(ws + wl.act);
   float* part = reinterpret_cast<float*>(ws + wl.part);
-  if (m <= 32 && L->k % 1024 == 0) {
-    // the streaming kernel (16- or 32-row tiles; its partial tiles fit the
-    // region sized for the pipelined kernel's 32-row tiles)
-#define UQ_STREAM_CASE(SC, GR)                                                                 \
-  case SC * 1000 + GR:                                                                         \
-    return m <= 16 ? launch_stream_t<SC, GR, 1>(L, codes, params, x, y, m, part, arrivals, stream) \
-                   : launch_stream_t<SC, GR, 2>(L, codes, params, x, y, m, part, arrivals, stream);
+  if (m <= 32 && L->k % 256 == 0) {
+    // K up to 4096 in blocks of 512: a workgroup requests its whole K range
+    // (at most two blocks) at once; other K streams blocks of 256 with one
+    // in flight.  (Measured on MI355X, INT4 G128 K4096 N11008 at 16 rows:
+    // 14.4 us with four blocks of 256, 13.0 us with two of 512 in one LDS
+    // buffer; at 32 rows 18.1 -> 16.3 us.)
+    const bool all_in = L->k <= 4096 && L->k % 512 == 0;
+#define UQ_STREAM_CASE(SC, GR)                                                                          \
+  case SC * 1000 + GR:                                                                                  \
+    if (all_in)                                                                                         \
+      return m <= 16 ? launch_stream_t<SC, GR, 1, 512, 2, 1>(L, codes, params, x, y, m, part, arrivals, stream) \
+                     : launch_stream_t<SC, GR, 2, 512, 2, 1>(L, codes, params, x, y, m, part, arrivals, stream); \
+    return m <= 16 ? launch_stream_t<SC, GR, 1, 256, 0, 2>(L, codes, params, x, y, m, part, arrivals, stream)     \
+                   : launch_stream_t<SC, GR, 2, 256, 0, 2>(L, codes, params, x, y, m, part, arrivals, stream);
     switch (L->scheme * 1000 + L->group) {
       UQ_STREAM_CASE(UQ_INT2, 16)
       UQ_STREAM_CASE(UQ_INT2, 32)

@@ -271,10 +271,12 @@ def test_gemm_batched_equivalence(lib):
 
 @pytest.mark.parametrize("scheme,group", ALL_LAYOUTS)
 def test_gemm_streaming_rows(lib, scheme, group):
-    """Up to 32 rows with K a multiple of 1024 the GEMM streams codes into
+    """Up to 32 rows with K a multiple of 256 the GEMM streams codes into
     registers: 16- and 32-row tiles, N with a ragged last tile of 64 weight
-    rows, K over one block and over several (with and without a K split)."""
-    for n, k, seed in ((77, 1024, 41), (200, 3072, 42), (2100, 2048, 43)):
+    rows; K up to 4096 in blocks of 512 requested at once (K splits with one
+    block and with two, and with a split short of a block), other K in
+    blocks of 256 with one in flight (K = 1280 and 4864)."""
+    for n, k, seed in ((77, 1024, 41), (200, 3072, 42), (2100, 2048, 43), (130, 1280, 44), (70, 4864, 45)):
         w, x = workloads.make_random(n, k, 32, seed=seed, outliers=True)
         lay, codes, params = packed_on_device(lib, scheme, group, w)
         wdq = oracle_dequant(w, scheme, group)
