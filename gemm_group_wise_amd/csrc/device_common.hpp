@@ -139,17 +139,6 @@ __device__ __forceinline__ float dpp_mov(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
 }
 
-// Sum over the 64 lanes of a wavefront; every lane receives the total.
-__device__ __forceinline__ float wave_sum(float v) {
-  v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]
-  v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]
-  v += dpp_mov<0x141>(v);  // row_half_mirror
-  v += dpp_mov<0x140>(v);  // row_mirror
-  v += __shfl_xor(v, 16, 64);
-  v += __shfl_xor(v, 32, 64);
-  return v;
-}
-
 // Sum of each of four per-lane values over the 64 lanes of a wave, using the
 // gfx950 lane-swap instructions as a transpose-reduction.  v_permlane32_swap
 // exchanges the upper 32 lanes of its first operand with the lower 32 lanes of

@@ -29,6 +29,7 @@ namespace uq {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kComputeUnits = 256;  // MI355X
 constexpr int kWaves = kThreads / 64;
 // Activations staged per LDS block (all rows of x together).  INT2 takes
 // twice as many: with 5-8 activation rows its K = 4096 then fits one block
@@ -59,18 +60,22 @@ struct ChunkRegs {
   uint32_t par[R][Geo<S, G>::PPC];  // INT: (s | z << 16) per part; NF4: absmax bits
 };
 
-// Load 16-byte code chunk `chunk` of each of the wave's R rows, plus the
+// Load 16-byte code chunk `chunk` of each of the wave's R rows, and the
 // parameters of the groups it touches.  cbase/pbase point at the wave's first
 // row and roff/poff are the (clamped) row offsets -- all wave-uniform -- so
 // only the chunk offset is per lane.
 template <int S, int G, int R>
-__device__ __forceinline__ void load_chunk(ChunkRegs<S, G, R>& cr, const uint8_t* __restrict__ cbase,
-                                           const uint8_t* __restrict__ pbase, const int64_t (&roff)[R],
-                                           const int64_t (&poff)[R], int chunk) {
-  using Gm = Geo<S, G>;
-  constexpr int PB = Gm::NF ? 2 : 4;  // bytes of one group's parameters
+__device__ __forceinline__ void load_codes(ChunkRegs<S, G, R>& cr, const uint8_t* __restrict__ cbase,
+                                           const int64_t (&roff)[R], int chunk) {
 #pragma unroll
   for (int r = 0; r < R; ++r) cr.code[r] = load_stream<uint4>(cbase + roff[r] + uint32_t(chunk) * 16u);
+}
+
+template <int S, int G, int R>
+__device__ __forceinline__ void load_params(ChunkRegs<S, G, R>& cr, const uint8_t* __restrict__ pbase,
+                                            const int64_t (&poff)[R], int chunk) {
+  using Gm = Geo<S, G>;
+  constexpr int PB = Gm::NF ? 2 : 4;  // bytes of one group's parameters
   const uint32_t gb = uint32_t(chunk) * Gm::CW / G * PB;  // first group of the chunk, in bytes
 #pragma unroll
   for (int r = 0; r < R; ++r) {
@@ -92,6 +97,23 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<S, G, R>& cr, const uint8_t
     }
   }
 }
+
+template <int S, int G, int R>
+__device__ __forceinline__ void load_chunk(ChunkRegs<S, G, R>& cr, const uint8_t* __restrict__ cbase,
+                                           const uint8_t* __restrict__ pbase, const int64_t (&roff)[R],
+                                           const int64_t (&poff)[R], int chunk) {
+  load_codes<S, G, R>(cr, cbase, roff, chunk);
+  load_params<S, G, R>(cr, pbase, poff, chunk);
+}
+
+// Order of a K block's first weight loads: INT4 and NF4 ask for every
+// chunk's parameters before the codes (the parameters are needed first and
+// are a small share of the bytes; measured on MI355X: INT4 G64 K4096 N11008
+// M=1 6.72 -> 6.55 us, G128 6.72 -> 6.42 us, NF4 N14336 10.68 -> 10.42 us);
+// INT8 and INT2 load them per chunk after its codes (5.03 vs 5.12 us, 3.99
+// vs 4.05 us the other way).
+template <int S>
+constexpr bool params_first() { return S == UQ_INT4 || S == UQ_NF4; }
 
 __device__ __forceinline__ uint32_t dword_of(const uint4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
@@ -243,10 +265,23 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
     __builtin_amdgcn_sched_barrier(0);  // keep the activation loads ahead of the weight loads
     // (2) every weight chunk of the first 64*U columns, for all R rows
     ChunkRegs<S, G, R> cur[U];
+    if constexpr (params_first<S>()) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int c = lane + 64 * u;
-      load_chunk<S, G, R>(cur[u], cbase, pbase, roff, poff, int(ch0) + (c < nch ? c : nch - 1));
+      for (int u = 0; u < U; ++u) {
+        const int c = lane + 64 * u;
+        load_params<S, G, R>(cur[u], pbase, poff, int(ch0) + (c < nch ? c : nch - 1));
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = lane + 64 * u;
+        load_codes<S, G, R>(cur[u], cbase, roff, int(ch0) + (c < nch ? c : nch - 1));
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = lane + 64 * u;
+        load_chunk<S, G, R>(cur[u], cbase, pbase, roff, poff, int(ch0) + (c < nch ? c : nch - 1));
+      }
     }
     __builtin_amdgcn_sched_barrier(0);  // and all weight loads ahead of the staging work
 
@@ -415,21 +450,19 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
     for (int kb0 = 0; kb0 < k; kb0 += kb_max) k_block(kb0);
   }
 
-  // Reduce lane partials and store: four (row, m) outputs per swap-reduction.
+  // Reduce lane partials and store: four (row, m) outputs per swap-reduction,
+  // a last group of fewer padded with zeros.  Each output's additions do not
+  // depend on the other three, so every (row, m) is summed in one order
+  // whatever R and MT are.
   constexpr int NV = R * MT;
   float* yv = &acc_y[0][0];
 #pragma unroll
-  for (int q = 0; q + 4 <= NV; q += 4) {
-    const float v = wave_sum4(yv[q], yv[q + 1], yv[q + 2], yv[q + 3]);
+  for (int q = 0; q < NV; q += 4) {
+    const float v = wave_sum4(yv[q], q + 1 < NV ? yv[q + 1] : 0.0f, q + 2 < NV ? yv[q + 2] : 0.0f,
+                              q + 3 < NV ? yv[q + 3] : 0.0f);
     const int slot = q + ((lane >> 4) == 1 ? 2 : (lane >> 4) == 2 ? 1 : (lane >> 4));  // a, c, b, d
     const int r = slot / MT, mm = slot - r * MT;
-    if ((lane & 15) == 0 && row0 + r < n && mm < m) y[size_t(mm) * size_t(n) + size_t(row0 + r)] = v;
-  }
-#pragma unroll
-  for (int q = NV - NV % 4; q < NV; ++q) {
-    const float v = wave_sum(yv[q]);
-    const int r = q / MT, mm = q - r * MT;
-    if (lane == 0 && row0 + r < n && mm < m) y[size_t(mm) * size_t(n) + size_t(row0 + r)] = v;
+    if ((lane & 15) == 0 && slot < NV && row0 + r < n && mm < m) y[size_t(mm) * size_t(n) + size_t(row0 + r)] = v;
   }
 }
 
@@ -482,7 +515,16 @@ hipError_t launch(const uq_layout* L, const void* codes, const void* params, con
 template <int S, int G>
 hipError_t launch_m(const uq_layout* L, const void* codes, const void* params, const uint16_t* x,
                     float* y, int m, hipStream_t stream) {
-  if (m == 1) return launch<S, G, 1, rows_per_wave<S, 1>()>(L, codes, params, x, y, m, stream);
+  if (m == 1) {
+    // A weight matrix with too few rows to give every compute unit a
+    // workgroup at the usual rows per wave takes one row per wave, four times
+    // the workgroups (measured on MI355X, INT4 G32 K256 N768: 2.98 us with
+    // four rows per wave, 2.65 with two, 2.46 with one).
+    constexpr int R = rows_per_wave<S, 1>();
+    if ((L->n + int64_t(kWaves) * R - 1) / (int64_t(kWaves) * R) < kComputeUnits)
+      return launch<S, G, 1, 1>(L, codes, params, x, y, m, stream);
+    return launch<S, G, 1, R>(L, codes, params, x, y, m, stream);
+  }
   if (m == 2) return launch<S, G, 2, rows_per_wave<S, 2>()>(L, codes, params, x, y, m, stream);
   if (m <= 4) return launch<S, G, 4, rows_per_wave<S, 4>()>(L, codes, params, x, y, m, stream);
   return launch<S, G, 8, rows_per_wave<S, 8>()>(L, codes, params, x, y, m, stream);
