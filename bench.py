@@ -294,7 +294,7 @@ def _counter_rows(directory: str, counter: str):
 def traffic_parse(wl: workloads.Workload, m: int, fetch_dir: str, write_dir: str, cmds: list[str]) -> dict:
     """Scale the kernel's FETCH_SIZE / WRITE_SIZE (KiB per dispatch) by what the
     same counters read for the calibration copy, and store the result."""
-    kernel = "gemv_kernel" if wl.path == "gemv" else "gemm_kernel"
+    kernel = "gemv_" if wl.path == "gemv" else "gemm_"  # the dot-product, matrix-core or streaming kernel
     known = CALIBRATION_MIB * 2**20
     out = {}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
@@ -316,7 +316,7 @@ def traffic_parse(wl: workloads.Workload, m: int, fetch_dir: str, write_dir: str
     with open(traffic_path(wl.name, m, "json"), "w") as f:
         json.dump(t, f, indent=1)
     f_, w_ = out["FETCH_SIZE"], out["WRITE_SIZE"]
-    md = [f"# HBM traffic of {kernel}: {wl.name}, M={m}", "",
+    md = [f"# HBM traffic of the {wl.path} kernel: {wl.name}, M={m}", "",
           "Commands (MI355X host, repository root), one counter per run:", ""] + [f"    {c}" for c in cmds] + [
           "", "| counter | kernel KiB/dispatch (median) | dispatches | calibration copy KiB | scale | bytes/launch |",
           "|---|---|---|---|---|---|",
@@ -685,7 +685,7 @@ def main() -> None:
         return
     if args.trace_summary:
         wl_ = workloads.WORKLOADS.get(args.workload)
-        hint = "gemv_kernel" if wl_ is not None and wl_.path == "gemv" else "gemm_kernel"
+        hint = "gemv_" if wl_ is not None and wl_.path == "gemv" else "gemm_"  # dot-product or matrix-core kernels
         if args.a8:
             hint = "gemv_a8_kernel"
         trace_summary(args.trace_summary[0], args.trace_summary[1], args.traffic_cmd, hint,
