@@ -5,8 +5,8 @@
 //
 // With several activation rows the dot-product GEMV spends about half a
 // VALU instruction per weight per activation row on v_dot2; here the
-// products run on v_mfma_f32_16x16x32_f16 (16x16x16 for INT2, whose groups
-// can be 16 codes) and the VALU cost per weight no longer grows with M.
+// products run on v_mfma_f32_16x16x32_f16 and the VALU cost per weight no
+// longer grows with M.
 // The products are exact and accumulate in fp32, as in the dot-product
 // GEMV:
 //   * B operand: each code as the exact fp16 1024 + q (0x6400 | q, one
@@ -40,21 +40,20 @@ namespace {
 typedef _Float16 f16x8v __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4v __attribute__((ext_vector_type(4)));
 
-// k per MFMA; codes a lane of an MFMA uses sit in one dword (INT2: its 16
-// codes' dword, of which it takes 4; INT4: 8 codes; INT8: two dwords).
+// k per MFMA; codes a lane of an MFMA uses sit in one dword (INT4: 8 codes)
+// or two (INT8).
 template <int S> struct Mf;
 template <> struct Mf<UQ_INT4> { static constexpr int KM = 32; };
 template <> struct Mf<UQ_INT8> { static constexpr int KM = 32; };
-template <> struct Mf<UQ_INT2> { static constexpr int KM = 16; };
 
 constexpr int kMfBlock = 128;          // code bytes per row per block (two dense loads of 8 rows)
 constexpr int kMfRowPitch = 144;       // LDS bytes per row of a block: 16 rows of 16-byte reads hit distinct banks
 constexpr int kMfXBytes = 64 * 1024;   // most LDS the staged activations may take
 
 // Schemes and groups the matrix-core GEMV serves (16x16x32 MFMAs, chains of
-// one to four MFMAs per group); the others keep the dot-product kernel, which
-// measured faster for them (INT2, and INT4 with 32-code groups, where the
-// per-group scaling costs more than the MFMAs save).
+// one to four MFMAs per group); the others keep the dot-product kernel: INT4
+// with 32-code groups measured faster there (the per-group scaling costs more
+// than the MFMAs save), and INT2's 16-code groups are shorter than one MFMA.
 template <int S, int G>
 constexpr bool mfma_gemv_scheme() {
   return (S == UQ_INT4 && (G == 64 || G == 128)) || (S == UQ_INT8 && (G == 32 || G == 64 || G == 128));
@@ -97,10 +96,6 @@ __device__ __forceinline__ constexpr int mf_src(int p) {
   if constexpr (S == UQ_INT4) {
     const int e = p & 7;  // pairs (q0,q4)(q1,q5)(q2,q6)(q3,q7) of each 8
     return (p & 8) + (e >> 1) + 4 * (e & 1);
-  } else if constexpr (S == UQ_INT2) {
-    // lane block g of a 16-code MFMA takes pairs (c_2g, c_2g+8), (c_2g+1, c_2g+9)
-    const int g = p >> 2, e = p & 3;
-    return 2 * g + (e >> 1) + 8 * (e & 1);
   } else {
     return p;
   }
@@ -108,24 +103,18 @@ __device__ __forceinline__ constexpr int mf_src(int p) {
 
 // B operand of one MFMA from the lane's code dword(s): pairs of fp16 1024 + q.
 template <int S>
-__device__ __forceinline__ void mf_unpack(uint32_t d0, uint32_t d1, int g, uint32_t (&b)[4]) {
+__device__ __forceinline__ void mf_unpack(uint32_t d0, uint32_t d1, uint32_t (&b)[4]) {
   const uint32_t magic = kMagic2;
   if constexpr (S == UQ_INT4) {
     b[0] = and_or(d0, 0x000F000Fu, magic);
     b[1] = and_or(d0 >> 4, 0x000F000Fu, magic);
     b[2] = and_or(d0 >> 8, 0x000F000Fu, magic);
     b[3] = and_or(d0 >> 12, 0x000F000Fu, magic);
-  } else if constexpr (S == UQ_INT8) {
+  } else {  // INT8
     b[0] = __builtin_amdgcn_perm(magic, d0, 0x05010500u);
     b[1] = __builtin_amdgcn_perm(magic, d0, 0x05030502u);
     b[2] = __builtin_amdgcn_perm(magic, d1, 0x05010500u);
     b[3] = __builtin_amdgcn_perm(magic, d1, 0x05030502u);
-  } else {  // INT2: pairs j = 2g, 2g + 1 of the dword: (c_j, c_j+8)
-    const uint32_t v = d0 >> (4 * g);
-    b[0] = and_or(v, 0x00030003u, magic);
-    b[1] = and_or(v >> 2, 0x00030003u, magic);
-    b[2] = 0u;
-    b[3] = 0u;
   }
 }
 
@@ -309,13 +298,10 @@ __global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(const uint8_t* __rest
         if constexpr (S == UQ_INT4) {
           bd[j][0] = *reinterpret_cast<const uint32_t*>(bp + q * 16 + 4 * lg);
           bd[j][1] = 0u;
-        } else if constexpr (S == UQ_INT8) {
+        } else {
           const uint2 v = *reinterpret_cast<const uint2*>(bp + q * 32 + 8 * lg);
           bd[j][0] = v.x;
           bd[j][1] = v.y;
-        } else {
-          bd[j][0] = *reinterpret_cast<const uint32_t*>(bp + q * 4);
-          bd[j][1] = 0u;
         }
         av[j] = *reinterpret_cast<const uint4*>(xa + (kq0 + j * KM + 8 * lg) * 2);
       }
@@ -349,7 +335,7 @@ __global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(const uint8_t* __rest
         for (int jj = 0; jj < Ge::MPG; ++jj) {
           const int j = g * Ge::MPG + jj;
           uint32_t bb[4];
-          mf_unpack<S>(bd[j][0], bd[j][1], lg, bb);
+          mf_unpack<S>(bd[j][0], bd[j][1], bb);
           ca[jj] = __builtin_bit_cast(f16x8v, av[j]);
           cb[jj] = __builtin_bit_cast(f16x8v, make_uint4(bb[0], bb[1], bb[2], bb[3]));
         }
