@@ -5,8 +5,8 @@
 //
 // With several activation rows the dot-product GEMV spends about half a
 // VALU instruction per weight per activation row on v_dot2; here the
-// products run on v_mfma_f32_16x16x32_f16 and the VALU cost per weight no
-// longer grows with M.
+// products run on v_mfma_f32_16x16x32_f16 (16x16x16 for INT2, whose groups
+// are 16 codes) and the VALU cost per weight no longer grows with M.
 // The products are exact and accumulate in fp32, as in the dot-product
 // GEMV:
 //   * B operand: each code as the exact fp16 1024 + q (0x6400 | q, one
@@ -40,23 +40,26 @@ namespace {
 typedef _Float16 f16x8v __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4v __attribute__((ext_vector_type(4)));
 
-// k per MFMA; codes a lane of an MFMA uses sit in one dword (INT4: 8 codes)
-// or two (INT8).
+// k per MFMA; codes a lane of an MFMA uses sit in one dword (INT4: 8 codes;
+// INT2: the 16-code group's dword, of which it takes 4) or two (INT8).
 template <int S> struct Mf;
 template <> struct Mf<UQ_INT4> { static constexpr int KM = 32; };
 template <> struct Mf<UQ_INT8> { static constexpr int KM = 32; };
+template <> struct Mf<UQ_INT2> { static constexpr int KM = 16; };
 
 constexpr int kMfBlock = 128;          // code bytes per row per block (two dense loads of 8 rows)
 constexpr int kMfRowPitch = 144;       // LDS bytes per row of a block: 16 rows of 16-byte reads hit distinct banks
 constexpr int kMfXBytes = 64 * 1024;   // most LDS the staged activations may take
 
 // Schemes and groups the matrix-core GEMV serves (16x16x32 MFMAs, chains of
-// one to four MFMAs per group); the others keep the dot-product kernel: INT4
-// with 32-code groups measured faster there (the per-group scaling costs more
-// than the MFMAs save), and INT2's 16-code groups are shorter than one MFMA.
+// one to four MFMAs per group; INT2 with 16-code groups one 16x16x16 MFMA
+// per group); the others keep the dot-product kernel: INT4 with 32-code
+// groups measured faster there (the per-group scaling costs more than the
+// MFMAs save), and INT2 with longer groups is not built here.
 template <int S, int G>
 constexpr bool mfma_gemv_scheme() {
-  return (S == UQ_INT4 && (G == 64 || G == 128)) || (S == UQ_INT8 && (G == 32 || G == 64 || G == 128));
+  return (S == UQ_INT4 && (G == 64 || G == 128)) || (S == UQ_INT8 && (G == 32 || G == 64 || G == 128)) ||
+         (S == UQ_INT2 && G == 16);
 }
 
 template <int S, int G, int MT, int W, int NBLK>
@@ -96,6 +99,10 @@ __device__ __forceinline__ constexpr int mf_src(int p) {
   if constexpr (S == UQ_INT4) {
     const int e = p & 7;  // pairs (q0,q4)(q1,q5)(q2,q6)(q3,q7) of each 8
     return (p & 8) + (e >> 1) + 4 * (e & 1);
+  } else if constexpr (S == UQ_INT2) {
+    // lane block g of a 16-code MFMA takes codes g, g + 8, g + 4, g + 12
+    const int g = p >> 2, e = p & 3;
+    return g + 8 * (e & 1) + 4 * (e >> 1);
   } else {
     return p;
   }
@@ -103,9 +110,17 @@ __device__ __forceinline__ constexpr int mf_src(int p) {
 
 // B operand of one MFMA from the lane's code dword(s): pairs of fp16 1024 + q.
 template <int S>
-__device__ __forceinline__ void mf_unpack(uint32_t d0, uint32_t d1, uint32_t (&b)[4]) {
+__device__ __forceinline__ void mf_unpack(uint32_t d0, uint32_t d1, int lg, uint32_t (&b)[4]) {
   const uint32_t magic = kMagic2;
-  if constexpr (S == UQ_INT4) {
+  if constexpr (S == UQ_INT2) {
+    // the group's dword holds codes c0..c15 (crumb i at bit 2i); lane block
+    // lg takes (c_lg, c_lg+8) and (c_lg+4, c_lg+12): bits 2 lg and 2 lg + 8
+    // of each half
+    b[0] = and_or(d0 >> (2 * lg), 0x00030003u, magic);
+    b[1] = and_or(d0 >> (2 * lg + 8), 0x00030003u, magic);
+    b[2] = 0u;
+    b[3] = 0u;
+  } else if constexpr (S == UQ_INT4) {
     b[0] = and_or(d0, 0x000F000Fu, magic);
     b[1] = and_or(d0 >> 4, 0x000F000Fu, magic);
     b[2] = and_or(d0 >> 8, 0x000F000Fu, magic);
@@ -145,6 +160,10 @@ __device__ __forceinline__ void mfma_chain(f32x4& acc, const f16x8v (&a)[N], con
                  UQ_MF_PRE UQ_MF_OP "%0, %5, %6, %0\n\t" UQ_MF_PRE UQ_MF_OP "%0, %7, %8, %0" UQ_MF_POST
                  : "+v"(acc) : "v"(a[0]), "v"(b[0]), "v"(a[1]), "v"(b[1]), "v"(a[2]), "v"(b[2]), "v"(a[3]), "v"(b[3]));
   }
+}
+// INT2: one v_mfma_f32_16x16x16_f16 per 16-code group (4 fp16 per lane).
+__device__ __forceinline__ void mfma_chain16(f32x4& acc, const f16x4v& a, const f16x4v& b) {
+  asm volatile(UQ_MF_PRE "v_mfma_f32_16x16x16_f16 %0, %1, %2, %0" UQ_MF_POST : "+v"(acc) : "v"(a), "v"(b));
 }
 #undef UQ_MF_PRE
 #undef UQ_MF_OP
@@ -272,7 +291,7 @@ __global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(const uint8_t* __rest
   const int ln = lane & 15, lg = lane >> 4;   // MFMA column (weight row) and k block of this lane
   const uint8_t* xa = xs + (ln % MT) * Ge::XPITCH;  // this lane's A row (rows past MT repeat)
   const uint8_t* bp = blk + ln * kMfRowPitch;       // this lane's weight row of the block
-  constexpr int SB = Ge::MPB < 8 ? Ge::MPB : 8;     // MFMAs per sub-block
+  constexpr int SB = KM == 16 ? 4 : (Ge::MPB < 8 ? Ge::MPB : 8);  // MFMAs per sub-block
   constexpr int GS = SB / Ge::MPG;                  // groups per sub-block
   static_assert(Ge::MPB % SB == 0 && SB % Ge::MPG == 0, "sub-blocks hold whole groups");
   f32x4 yacc = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -286,6 +305,12 @@ __global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(const uint8_t* __rest
     asm volatile("" ::: "memory");
 #pragma unroll
     for (int sb = 0; sb < Ge::MPB / SB; ++sb) {
+      if constexpr (Ge::MPB / SB > 1) {
+        // one sub-block's reads in flight at a time (left free, the compiler
+        // hoists every sub-block's LDS reads and runs out of registers)
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+      }
       const int q0 = sb * SB;                                   // first MFMA of the sub-block in the block
       const int kq0 = wave * Ge::QK + (b * Ge::MPB + q0) * KM;  // its first k
       const int gi0 = (b * Ge::MPB + q0) / Ge::MPG;             // its first group within the wave
@@ -295,7 +320,10 @@ __global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(const uint8_t* __rest
 #pragma unroll
       for (int j = 0; j < SB; ++j) {
         const int q = q0 + j;
-        if constexpr (S == UQ_INT4) {
+        if constexpr (S == UQ_INT2) {
+          bd[j][0] = *reinterpret_cast<const uint32_t*>(bp + q * 4);  // the group's 16 codes
+          bd[j][1] = 0u;
+        } else if constexpr (S == UQ_INT4) {
           bd[j][0] = *reinterpret_cast<const uint32_t*>(bp + q * 16 + 4 * lg);
           bd[j][1] = 0u;
         } else {
@@ -303,7 +331,12 @@ __global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(const uint8_t* __rest
           bd[j][0] = v.x;
           bd[j][1] = v.y;
         }
-        av[j] = *reinterpret_cast<const uint4*>(xa + (kq0 + j * KM + 8 * lg) * 2);
+        if constexpr (KM == 16) {
+          const uint2 t = *reinterpret_cast<const uint2*>(xa + (kq0 + j * KM + 4 * lg) * 2);
+          av[j] = make_uint4(t.x, t.y, 0u, 0u);
+        } else {
+          av[j] = *reinterpret_cast<const uint4*>(xa + (kq0 + j * KM + 8 * lg) * 2);
+        }
       }
       float tc[GS][4], ts[GS][4];
       uint32_t par[GS];
@@ -330,16 +363,25 @@ __global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(const uint8_t* __rest
 #pragma unroll
       for (int g = 0; g < GS; ++g) {
         f32x4 acc = {tc[g][0], tc[g][1], tc[g][2], tc[g][3]};  // the chain starts at -1024 * SX
-        f16x8v ca[Ge::MPG], cb[Ge::MPG];
-#pragma unroll
-        for (int jj = 0; jj < Ge::MPG; ++jj) {
-          const int j = g * Ge::MPG + jj;
+        if constexpr (KM == 16) {
+          static_assert(Ge::MPG == 1, "16-code groups: one MFMA each");
           uint32_t bb[4];
-          mf_unpack<S>(bd[j][0], bd[j][1], bb);
-          ca[jj] = __builtin_bit_cast(f16x8v, av[j]);
-          cb[jj] = __builtin_bit_cast(f16x8v, make_uint4(bb[0], bb[1], bb[2], bb[3]));
+          mf_unpack<S>(bd[g][0], bd[g][1], lg, bb);
+          const f16x4v ca = __builtin_bit_cast(f16x4v, make_uint2(av[g].x, av[g].y));
+          const f16x4v cb = __builtin_bit_cast(f16x4v, make_uint2(bb[0], bb[1]));
+          mfma_chain16(acc, ca, cb);
+        } else {
+          f16x8v ca[Ge::MPG], cb[Ge::MPG];
+#pragma unroll
+          for (int jj = 0; jj < Ge::MPG; ++jj) {
+            const int j = g * Ge::MPG + jj;
+            uint32_t bb[4];
+            mf_unpack<S>(bd[j][0], bd[j][1], lg, bb);
+            ca[jj] = __builtin_bit_cast(f16x8v, av[j]);
+            cb[jj] = __builtin_bit_cast(f16x8v, make_uint4(bb[0], bb[1], bb[2], bb[3]));
+          }
+          mfma_chain<Ge::MPG>(acc, ca, cb);
         }
-        mfma_chain<Ge::MPG>(acc, ca, cb);
         // y += s * t + z * SX for the group
         const float sc = h2f(uint16_t(par[g] & 0xFFFFu)), zc = h2f(uint16_t(par[g] >> 16));
 #pragma unroll
@@ -347,6 +389,10 @@ __global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(const uint8_t* __rest
           yacc[i] = __builtin_fmaf(sc, acc[i], yacc[i]);
           yacc[i] = __builtin_fmaf(zc, ts[g][i], yacc[i]);
         }
+        // INT2's 32 groups per block: the scaling stays with its chain (left
+        // free, the compiler moved every group's scaling past the last chain
+        // and spilled the accumulators)
+        if constexpr (KM == 16) asm volatile("" : "+v"(yacc));
       }
     }
     asm volatile("" ::: "memory");  // the next block's writes stay after this block's reads
@@ -447,7 +493,10 @@ template <int S, int G>
 hipError_t launch_gemv_sel(const uq_layout* L, const void* codes, const void* params, const uint16_t* x, float* y,
                            int m, hipStream_t stream) {
   if constexpr (mfma_gemv_scheme<S, G>()) {
-    if (m >= 2) {
+    // INT2 (16-code groups, one MFMA and its scaling per group) pays off
+    // only with five or more rows: INT2 G16 N4096 M=8 9.6 -> 8.7 us, but M=2
+    // / 3 / 4 4.6 / 5.7 / 5.7 -> 8.2 / 8.5 / 8.6 us against the dot product.
+    if (m >= (S == UQ_INT2 ? 5 : 2)) {
       const int mt = m <= 2 ? 2 : m <= 4 ? 4 : 8;
       const int w = mt == 2 && (L->n + 15) / 16 >= 512 ? 4 : 8;
       if (mfma_fits<S, G>(L->k, mt, w))

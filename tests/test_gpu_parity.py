@@ -113,9 +113,10 @@ def test_gemv_one_hot_nf4(lib):
 def test_gemv_batched_equivalence(lib):
     """Row i of an M-row GEMV equals the single-row GEMV of x[i] within the gate
     (the pages' batched-decode equivalence; not bitwise, since the orders of
-    the fp32 sums differ).  INT2 / INT4 / INT8 calls with 2 to 8 rows run on
-    the matrix cores, whose sum order does not depend on M: their rows agree
-    bit for bit across M.  NF4 keeps the dot-product kernel for every M; with
+    the fp32 sums differ).  INT4 / INT8 calls with 2 to 8 rows (INT2 G16 with
+    5 to 8) run on the matrix cores, whose sum order does not depend on M:
+    their rows agree bit for bit across M, as do the dot-product kernel's
+    rows.  NF4 keeps the dot-product kernel for every M; with
     K in one LDS block of activations its rows agree with the single-row call
     bit for bit.
     """
@@ -135,24 +136,34 @@ def test_gemv_batched_equivalence(lib):
                 if scheme == "nf4" and k == 1024:
                     for i in range(m):
                         assert np.array_equal(y[i], ys[i]), (scheme, group, m, i)
-            if scheme != "nf4":
-                for m in (2, 3, 4, 5):
-                    assert np.array_equal(full[m].view(np.uint32), full[8][:m].view(np.uint32)), (scheme, group, k, m)
+            # calls served by one kernel agree bit for bit across M: INT4 / INT8
+            # rows 2-8 (matrix cores), INT2 rows 5-8 (matrix cores, G16) and 2-4
+            # (dot product, whose rows do not depend on M either)
+            if scheme in ("int4", "int8"):
+                sets = ((2, 3, 4, 5, 8),)
+            elif scheme == "int2":
+                sets = ((2, 3, 4), (5, 8)) if group == 16 else ((2, 3, 4, 5, 8),)
+            else:
+                sets = ()
+            for ms in sets:
+                for m in ms[:-1]:
+                    assert np.array_equal(full[m].view(np.uint32), full[ms[-1]][:m].view(np.uint32)), (scheme, group, k, m)
 
 
 @pytest.mark.parametrize("scheme,group,n,k", [
     ("int4", 64, 300, 4096), ("int4", 128, 777, 4096), ("int4", 64, 11008, 4096), ("int4", 64, 37, 1024),
     ("int4", 128, 129, 2560), ("int4", 64, 100, 16384), ("int8", 32, 333, 1024), ("int8", 64, 45, 2048),
-    ("int8", 128, 4096, 4096), ("int8", 128, 61, 8192), ("int8", 32, 17, 3968)])
+    ("int8", 128, 4096, 4096), ("int8", 128, 61, 8192), ("int8", 32, 17, 3968),
+    ("int2", 16, 300, 4096), ("int2", 16, 37, 1024), ("int2", 16, 129, 8192), ("int2", 16, 45, 3584)])
 def test_gemv_matrix_core_shapes(lib, scheme, group, n, k):
     """The matrix-core GEMV (2 to 8 activation rows, INT4 groups of 64 / 128 and
-    INT8): one to eight 128-byte blocks per wave, four and eight waves, K
+    INT8; 5 to 8 rows of INT2 G16): one to eight 128-byte blocks per wave, four and eight waves, K
     padded up to whole blocks (zero activations, groups past K ignored), a
     ragged last 16-row tile, and 2 / 4 / 8 staged activation rows."""
     w, x = workloads.make_random(n, k, 8, seed=42, outliers=True)
     lay, codes, params = packed_on_device(lib, scheme, group, w)
     wdq = oracle_dequant(w, scheme, group)
-    for m in (2, 3, 4, 6, 8):
+    for m in (2, 3, 4, 5, 6, 8):
         note(f"gemv matrix-core {scheme} G{group} n={n} k={k} m={m}")
         y = run_gemv(lib, lay, codes, params, x, m)
         gate(y, o.gemv_ref(x[:m], wdq), x[:m], wdq, f"mfma gemv {scheme} G{group} {n}x{k} m={m}")
