@@ -792,12 +792,13 @@ hipError_t launch(const uq_layout* L, const void* codes, const void* params, con
 // at once when it is at most NB blocks, else keeping one block's loads in
 // flight while the previous block is multiplied:
 //   * the loads of a block are its activations and its rows' group
-//     parameters (consecutive lanes, consecutive groups of a row), then the
-//     codes each lane multiplies, directly in the MFMA layout: lane l takes
-//     weight row l % 16, and of the row's 16-byte pieces of the block the
-//     pieces 4 q + l / 16, so the four lanes of a row read 64 contiguous
-//     bytes per load -- within an MFMA any k order serves as long as A and B
-//     agree, and the activations are staged in the same order;
+//     parameters (consecutive lanes, consecutive groups of a row), then its
+//     codes, whole rows per load (the wave's 16 rows' blocks, 1 KB per load
+//     instruction), moved through a per-wave LDS area into the MFMA layout:
+//     lane l takes weight row l % 16 and, of the row's 16-byte pieces of the
+//     block, the pieces 4 q + l / 16 -- within an MFMA any k order serves as
+//     long as A and B agree, and the activations are staged in the same
+//     order;
 //   * once they land, the activations are staged in LDS (fp16 -> bf16, round
 //     to nearest even) with the parameters, in one of NBUF buffers (with
 //     one, a barrier first lets every wave finish reading the previous
@@ -821,7 +822,12 @@ struct SGeo {
   static constexpr int NGB = XB / G;            // groups per block
   static constexpr int PPB = BN * NGB;          // parameters per block
   static constexpr int PPT = (PPB + NT - 1) / NT;
+  static constexpr int RB = XB * bits / 8;       // code bytes of a weight row per block
+  static constexpr int LPR = RB / 16;           // lanes reading one row's block (16 bytes each)
+  static constexpr int RPI = 64 / LPR;          // rows per wave load instruction
+  static constexpr int CPITCH = RB + 16;        // LDS bytes per row in a wave's code area
   static_assert(XI % NT == 0 && QW % 4 == 0 && NJ % 2 == 0 && Q % 16 == 0, "block geometry");
+  static_assert(LPR >= 1 && LPR <= 64 && 64 % LPR == 0 && QW / 4 * RPI == 16, "code loads: 16 rows per wave");
 };
 
 // One block's loads, in registers until staged.
@@ -843,6 +849,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const uint8_t* __restr
   constexpr int QW = Ge::QW, NGB = Ge::NGB;
   __shared__ __attribute__((aligned(16))) uint8_t xs[NBUF][BM * Ge::XPITCH];
   __shared__ __attribute__((aligned(16))) uint32_t ps[NBUF][Ge::PPT * NT];  // PPB used, the rest written blindly
+  __shared__ __attribute__((aligned(16))) uint8_t cs[4][16 * Ge::CPITCH];     // each wave's codes, row-major
   __shared__ float nf4[16];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -856,9 +863,17 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const uint8_t* __restr
   const int rowb = k * bits / 8;
   const int ng = k / G;
   const int l16 = lane & 15, kb = lane >> 4;
-  int wr = bn + 16 * wave + l16;
-  wr = wr < n ? wr : n - 1;  // rows past N: computed, not stored
-  const uint8_t* crow = codes + size_t(wr) * size_t(rowb) + 16 * kb;
+  // Code loads read whole rows: load i of a lane covers row RPI i + lane / LPR
+  // of the wave's 16, bytes 16 (lane % LPR) of the row's block (rows past N
+  // re-read row N - 1: computed, not stored).
+  const uint8_t* cptr[QW / 4];
+#pragma unroll
+  for (int i = 0; i < QW / 4; ++i) {
+    int r = bn + 16 * wave + Ge::RPI * i + lane / Ge::LPR;
+    r = r < n ? r : n - 1;
+    cptr[i] = codes + size_t(r) * size_t(rowb) + 16 * (lane % Ge::LPR);
+  }
+  uint8_t* cw = cs[wave];
   if constexpr (S == UQ_NF4) {
     if (tid < 16) nf4[tid] = nf4_value(tid);
   }
@@ -886,12 +901,33 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const uint8_t* __restr
       else ld.p[i] = load_stream<uint16_t>(src);
     }
 #pragma unroll
+    for (int i = 0; i < QW / 4; ++i) {
+      const uint4 v = load_stream<uint4>(cptr[i] + size_t(k0) * bits / 8);
+      ld.run[4 * i] = v.x;
+      ld.run[4 * i + 1] = v.y;
+      ld.run[4 * i + 2] = v.z;
+      ld.run[4 * i + 3] = v.w;
+    }
+  };
+  // Move a block's codes from the row-contiguous load layout into the MFMA
+  // layout through the wave's LDS area: lane (row l16, k-block kb) takes the
+  // row's 16-byte pieces 4 q + kb.  Only the wave touches its area, and a
+  // wave's LDS accesses complete in issue order; the empty asm statements
+  // keep the compiler from moving them across each other.
+  auto transpose = [&](const StreamLoads<Ge>& ld, uint32_t (&run)[QW]) {
+    asm volatile("" ::: "memory");  // the previous block's reads came first
+#pragma unroll
+    for (int i = 0; i < QW / 4; ++i)
+      *reinterpret_cast<uint4*>(cw + (Ge::RPI * i + lane / Ge::LPR) * Ge::CPITCH + 16 * (lane % Ge::LPR)) =
+          make_uint4(ld.run[4 * i], ld.run[4 * i + 1], ld.run[4 * i + 2], ld.run[4 * i + 3]);
+    asm volatile("" ::: "memory");
+#pragma unroll
     for (int q = 0; q < QW / 4; ++q) {
-      const uint4 v = load_stream<uint4>(crow + size_t(k0) * bits / 8 + 64 * q);
-      ld.run[4 * q] = v.x;
-      ld.run[4 * q + 1] = v.y;
-      ld.run[4 * q + 2] = v.z;
-      ld.run[4 * q + 3] = v.w;
+      const uint4 v = *reinterpret_cast<const uint4*>(cw + l16 * Ge::CPITCH + 16 * (4 * q + kb));
+      run[4 * q] = v.x;
+      run[4 * q + 1] = v.y;
+      run[4 * q + 2] = v.z;
+      run[4 * q + 3] = v.w;
     }
   };
 
@@ -970,10 +1006,12 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const uint8_t* __restr
     }
 #pragma unroll
     for (int bb = 0; bb < NB; ++bb) {
+      uint32_t run[QW];
+      transpose(ld[bb], run);
       if (NBUF == 1 && bb > 0) wait_lds_barrier();  // the buffer's last reads are done
       stage(ld[bb], bb % NBUF, bb < nb);
       wait_lds_barrier();
-      compute(ld[bb].run, bb % NBUF);
+      compute(run, bb % NBUF);
     }
   } else {
     // One block in flight while the previous one is multiplied.
@@ -984,8 +1022,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(const uint8_t* __restr
       if (NBUF == 1 && blk > b0) wait_lds_barrier();  // the buffer's last reads are done
       stage(ld, buf, true);
       uint32_t run[QW];
-#pragma unroll
-      for (int w = 0; w < QW; ++w) run[w] = ld.run[w];
+      transpose(ld, run);
       if (blk + 1 < b1) issue(ld, blk + 1);
       wait_lds_barrier();
       compute(run, buf);
