@@ -25,9 +25,11 @@
 //
 // Work split: a workgroup of W waves owns 16 weight rows; wave w takes the
 // w-th of W equal slices of every row's code bytes (whole 128-byte blocks).
-// Codes and parameters are loaded densely (eight rows x 128 bytes per wave
-// instruction, full cache lines), all at once, then moved through a per-wave
-// LDS block into the MFMA layout.  x is staged in LDS once per workgroup
+// Codes are loaded densely (eight rows x 128 bytes per wave instruction, full
+// cache lines), all at once, then moved through a per-wave LDS block into the
+// MFMA layout; a wave's parameters (up to 32 bytes per row) are loaded by
+// each lane for its own weight row and stay in registers (longer parameter
+// rows go through LDS like the codes).  x is staged in LDS once per workgroup
 // with the per-group sums.  The W partial 16 x 16 tiles are added in a fixed
 // order through LDS at the end (bitwise repeatable).
 #pragma once
@@ -79,9 +81,16 @@ struct MfGeo {
   static constexpr int X_BYTES = MT * XPITCH;
   static constexpr int T_BYTES = MT * NG * 8;                // (-1024 * SX, SX) per (group, row)
   static constexpr int B_BYTES = 16 * kMfRowPitch;           // one wave's block
-  static constexpr int P_BYTES = 16 * PP;                    // one wave's parameters
+  // A wave's parameters: up to two 16-byte slots per row go straight into
+  // each lane's registers (the lane's weight row; the four lanes of a row
+  // load the same bytes), which keeps them out of LDS so that more
+  // workgroups fit a CU; longer rows of parameters (INT2 G16: 32 groups per
+  // wave) go through a per-wave LDS area.
+  static constexpr bool PREG = QP <= 32;
+  static constexpr int PR = PREG ? QP / 16 : 1;              // 16-byte parameter loads per lane (registers)
+  static constexpr int P_BYTES = PREG ? 0 : 16 * PP;         // one wave's parameters in LDS
   static constexpr int LDS = X_BYTES + T_BYTES + W * (B_BYTES + P_BYTES);
-  static constexpr int PLOADS = (16 * QP + 1023) / 1024;     // 16-byte parameter loads per lane
+  static constexpr int PLOADS = (16 * QP + 1023) / 1024;     // 16-byte parameter loads per lane (LDS)
   static constexpr int XPIECES = MT * KP / 16;               // 16-activation pieces staged
   static constexpr int PIECES = (XPIECES + 64 * W - 1) / (64 * W);  // per thread
   // An MFMA lies in one group and a wave holds whole groups; a wave's
@@ -215,16 +224,27 @@ __global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(const uint8_t* __rest
   //  slots past the row's groups load a valid slot and are never used)
   const int pb0 = wave * Ge::QP;  // first parameter byte of the wave in a row
   constexpr int SPR = Ge::QP / 16;  // 16-byte slots per row
-  uint4 pr[Ge::PLOADS];
-#pragma unroll
-  for (int j = 0; j < Ge::PLOADS; ++j) {
-    const int q = j * 64 + lane;
-    const int r = q / SPR, o = (q % SPR) * 16;
-    int64_t row = row0 + (r < 16 ? r : 15);
+  uint4 pr[Ge::PREG ? Ge::PR : Ge::PLOADS];
+  if constexpr (Ge::PREG) {
+    int64_t row = row0 + (lane & 15);
     row = row < n ? row : n - 1;
-    int off = pb0 + o;
-    off = off + 16 <= ng * 4 ? off : ng * 4 - 16;
-    pr[j] = load_stream<uint4>(params + row * int64_t(ng) * 4 + off);
+#pragma unroll
+    for (int j = 0; j < Ge::PR; ++j) {
+      int off = pb0 + 16 * j;
+      off = off + 16 <= ng * 4 ? off : ng * 4 - 16;
+      pr[j] = load_stream<uint4>(params + row * int64_t(ng) * 4 + off);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < Ge::PLOADS; ++j) {
+      const int q = j * 64 + lane;
+      const int r = q / SPR, o = (q % SPR) * 16;
+      int64_t row = row0 + (r < 16 ? r : 15);
+      row = row < n ? row : n - 1;
+      int off = pb0 + o;
+      off = off + 16 <= ng * 4 ? off : ng * 4 - 16;
+      pr[j] = load_stream<uint4>(params + row * int64_t(ng) * 4 + off);
+    }
   }
   const int lr = lane >> 3, lp = lane & 7;  // dense code loads: row within 8, 16-byte piece
   uint4 cr[NBLK][2];
@@ -276,22 +296,27 @@ __global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(const uint8_t* __rest
   }
 
   // (4) this wave's parameters into its LDS rows
+  if constexpr (!Ge::PREG) {
 #pragma unroll
-  for (int j = 0; j < Ge::PLOADS; ++j) {
-    const int q = j * 64 + lane;
-    const int r = q / SPR, o = (q % SPR) * 16;
-    if (r < 16) *reinterpret_cast<uint4*>(pls + r * Ge::PP + o) = pr[j];
+    for (int j = 0; j < Ge::PLOADS; ++j) {
+      const int q = j * 64 + lane;
+      const int r = q / SPR, o = (q % SPR) * 16;
+      if (r < 16) *reinterpret_cast<uint4*>(pls + r * Ge::PP + o) = pr[j];
+    }
   }
   __syncthreads();
 
   // (5) blocks: move the two dense loads into the MFMA layout through LDS,
-  //     then the block in sub-blocks of up to eight MFMAs: every LDS read
+  //     then the block in sub-blocks of up to four MFMAs: every LDS read
   //     of a sub-block first (one wait), then per group its MFMA chain and
   //     its scaling.
   const int ln = lane & 15, lg = lane >> 4;   // MFMA column (weight row) and k block of this lane
   const uint8_t* xa = xs + (ln % MT) * Ge::XPITCH;  // this lane's A row (rows past MT repeat)
   const uint8_t* bp = blk + ln * kMfRowPitch;       // this lane's weight row of the block
-  constexpr int SB = KM == 16 ? 4 : (Ge::MPB < 8 ? Ge::MPB : 8);  // MFMAs per sub-block
+  // MFMAs per sub-block: four, which keeps the kernel within 80 VGPRs (with
+  // the parameters in registers and staging in LDS, three 8-wave workgroups
+  // per CU at up to four activation rows; eight MFMAs per sub-block took 128)
+  constexpr int SB = KM == 16 ? 4 : (Ge::MPB < 4 ? Ge::MPB : 4);
   constexpr int GS = SB / Ge::MPG;                  // groups per sub-block
   static_assert(Ge::MPB % SB == 0 && SB % Ge::MPG == 0, "sub-blocks hold whole groups");
   f32x4 yacc = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -358,7 +383,10 @@ __global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(const uint8_t* __rest
 #pragma unroll
           for (int i = 0; i < 4; ++i) { tc[g][i] = v.x; ts[g][i] = v.y; }
         }
-        par[g] = gk < ng ? *reinterpret_cast<const uint32_t*>(pls + ln * Ge::PP + (gi0 + g) * 4) : 0u;  // past K: 0
+        uint32_t pv;
+        if constexpr (Ge::PREG) pv = dword_of(pr[(gi0 + g) / 4], (gi0 + g) % 4);
+        else pv = *reinterpret_cast<const uint32_t*>(pls + ln * Ge::PP + (gi0 + g) * 4);
+        par[g] = gk < ng ? pv : 0u;  // past K: 0
       }
 #pragma unroll
       for (int g = 0; g < GS; ++g) {
