@@ -450,8 +450,7 @@ __global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(const uint8_t* __rest
 }
 
 // Launch for 2..8 activation rows when the shape fits (else returns false and
-// the dot-product GEMV serves the call).  W waves per workgroup: 4 when the
-// matrix has enough rows to give every CU several workgroups, else 8.
+// the dot-product GEMV serves the call), with W waves per workgroup.
 template <int S, int G, int MT, int W, int NBLK>
 hipError_t launch_mfma_t(const uq_layout* L, const void* codes, const void* params, const uint16_t* x, float* y,
                          int m, hipStream_t stream) {
@@ -513,10 +512,9 @@ hipError_t launch_mfma_m(const uq_layout* L, const void* codes, const void* para
 // The GEMV for INT2 / INT4 / INT8: 2..8 activation rows on the matrix cores
 // when the scheme and shape fit, otherwise (and for one row) the dot-product
 // kernel.  Eight waves per workgroup, each taking an eighth of every row
-// (less work per wave after its loads land: INT4 G64 N11008 M=4 13.1 ->
-// 10.9 us against four waves), except two activation rows on a matrix with
-// 512 or more 16-row workgroups, which measured slightly faster on four
-// (9.9 against 10.2 us at N11008).
+// (less work per wave after its loads land; measured on MI355X, INT4 G64
+// N11008: M=2 / 4 / 8 8.7 / 9.6 / 14.4 us against 9.3 / 10.7 / 19.1 us on
+// four waves).
 template <int S, int G>
 hipError_t launch_gemv_sel(const uq_layout* L, const void* codes, const void* params, const uint16_t* x, float* y,
                            int m, hipStream_t stream) {
@@ -526,10 +524,7 @@ hipError_t launch_gemv_sel(const uq_layout* L, const void* codes, const void* pa
     // / 3 / 4 4.6 / 5.7 / 5.7 -> 8.2 / 8.5 / 8.6 us against the dot product.
     if (m >= (S == UQ_INT2 ? 5 : 2)) {
       const int mt = m <= 2 ? 2 : m <= 4 ? 4 : 8;
-      const int w = mt == 2 && (L->n + 15) / 16 >= 512 ? 4 : 8;
-      if (mfma_fits<S, G>(L->k, mt, w))
-        return w == 4 ? launch_mfma_m<S, G, 4>(L, codes, params, x, y, m, mt, stream)
-                      : launch_mfma_m<S, G, 8>(L, codes, params, x, y, m, mt, stream);
+      if (mfma_fits<S, G>(L->k, mt, 8)) return launch_mfma_m<S, G, 8>(L, codes, params, x, y, m, mt, stream);
     }
   }
   return launch_m<S, G>(L, codes, params, x, y, m, stream);
