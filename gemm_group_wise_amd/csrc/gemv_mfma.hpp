@@ -55,12 +55,10 @@ constexpr int kMfXBytes = 64 * 1024;   // most LDS the staged activations may ta
 
 // Schemes and groups the matrix-core GEMV serves (16x16x32 MFMAs, chains of
 // one to four MFMAs per group; INT2 with 16-code groups one 16x16x16 MFMA
-// per group); the others keep the dot-product kernel: INT4 with 32-code
-// groups measured faster there (the per-group scaling costs more than the
-// MFMAs save), and INT2 with longer groups is not built here.
+// per group); INT2 with longer groups keeps the dot-product kernel.
 template <int S, int G>
 constexpr bool mfma_gemv_scheme() {
-  return (S == UQ_INT4 && (G == 64 || G == 128)) || (S == UQ_INT8 && (G == 32 || G == 64 || G == 128)) ||
+  return (S == UQ_INT4 && (G == 32 || G == 64 || G == 128)) || (S == UQ_INT8 && (G == 32 || G == 64 || G == 128)) ||
          (S == UQ_INT2 && G == 16);
 }
 
@@ -519,10 +517,15 @@ template <int S, int G>
 hipError_t launch_gemv_sel(const uq_layout* L, const void* codes, const void* params, const uint16_t* x, float* y,
                            int m, hipStream_t stream) {
   if constexpr (mfma_gemv_scheme<S, G>()) {
-    // INT2 (16-code groups, one MFMA and its scaling per group) pays off
-    // only with five or more rows: INT2 G16 N4096 M=8 9.6 -> 8.7 us, but M=2
-    // / 3 / 4 4.6 / 5.7 / 5.7 -> 8.2 / 8.5 / 8.6 us against the dot product.
-    if (m >= (S == UQ_INT2 ? 5 : 2)) {
+    // With one MFMA and its scaling per group (INT2 G16, INT4 G32) the
+    // matrix cores pay off only with more rows (measured on MI355X against
+    // the dot product): INT2 G16 N4096 M=8 9.6 -> 8.7 us, but M=2 / 3 / 4
+    // 4.6 / 5.7 / 5.7 -> 8.2 / 8.5 / 8.6 us; INT4 G32 N11008 M=3 / 4 / 5 / 8
+    // 11.7 / 11.9 / 20.4 / 21.6 -> 11.0 / 11.3 / 16.4 / 16.4 us and N4096
+    // M=5 / 8 10.2 / 10.2 -> 6.6 / 6.6 us, but N11008 M=2 8.2 -> 10.1 us and
+    // N4096 M=3 / 4 5.6 / 5.7 -> 6.3 / 6.3 us.
+    const int min_rows = S == UQ_INT2 ? 5 : S == UQ_INT4 && G == 32 ? (L->n >= 8192 ? 3 : 5) : 2;
+    if (m >= min_rows) {
       const int mt = m <= 2 ? 2 : m <= 4 ? 4 : 8;
       if (mfma_fits<S, G>(L->k, mt, 8)) return launch_mfma_m<S, G, 8>(L, codes, params, x, y, m, mt, stream);
     }

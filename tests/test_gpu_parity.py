@@ -116,7 +116,8 @@ def test_gemv_batched_equivalence(lib):
     the fp32 sums differ).  INT4 / INT8 calls with 2 to 8 rows (INT2 G16 with
     5 to 8) run on the matrix cores, whose sum order does not depend on M:
     their rows agree bit for bit across M, as do the dot-product kernel's
-    rows.  NF4 keeps the dot-product kernel for every M; with
+    rows (INT4 G32 on a matrix of fewer than 8192 rows runs the dot product up
+    to 4 rows and the matrix cores from 5).  NF4 keeps the dot-product kernel for every M; with
     K in one LDS block of activations its rows agree with the single-row call
     bit for bit.
     """
@@ -139,7 +140,9 @@ def test_gemv_batched_equivalence(lib):
             # calls served by one kernel agree bit for bit across M: INT4 / INT8
             # rows 2-8 (matrix cores), INT2 rows 5-8 (matrix cores, G16) and 2-4
             # (dot product, whose rows do not depend on M either)
-            if scheme in ("int4", "int8"):
+            if scheme == "int4" and group == 32:
+                sets = ((2, 3, 4), (5, 8))  # 300 rows: the dot product up to 4 rows, the matrix cores from 5
+            elif scheme in ("int4", "int8"):
                 sets = ((2, 3, 4, 5, 8),)
             elif scheme == "int2":
                 sets = ((2, 3, 4), (5, 8)) if group == 16 else ((2, 3, 4, 5, 8),)
@@ -154,10 +157,12 @@ def test_gemv_batched_equivalence(lib):
     ("int4", 64, 300, 4096), ("int4", 128, 777, 4096), ("int4", 64, 11008, 4096), ("int4", 64, 37, 1024),
     ("int4", 128, 129, 2560), ("int4", 64, 100, 16384), ("int8", 32, 333, 1024), ("int8", 64, 45, 2048),
     ("int8", 128, 4096, 4096), ("int8", 128, 61, 8192), ("int8", 32, 17, 3968),
-    ("int2", 16, 300, 4096), ("int2", 16, 37, 1024), ("int2", 16, 129, 8192), ("int2", 16, 45, 3584)])
+    ("int2", 16, 300, 4096), ("int2", 16, 37, 1024), ("int2", 16, 129, 8192), ("int2", 16, 45, 3584),
+    ("int4", 32, 300, 4096), ("int4", 32, 8200, 1024), ("int4", 32, 45, 3584)])
 def test_gemv_matrix_core_shapes(lib, scheme, group, n, k):
     """The matrix-core GEMV (2 to 8 activation rows, INT4 groups of 64 / 128 and
-    INT8; 5 to 8 rows of INT2 G16): one to eight 128-byte blocks per wave, four and eight waves, K
+    INT8; 5 to 8 rows of INT2 G16 and of INT4 G32, 3 to 8 of INT4 G32 on 8192 or
+    more weight rows): one to eight 128-byte blocks per wave, K
     padded up to whole blocks (zero activations, groups past K ignored), a
     ragged last 16-row tile, and 2 / 4 / 8 staged activation rows."""
     w, x = workloads.make_random(n, k, 8, seed=42, outliers=True)
