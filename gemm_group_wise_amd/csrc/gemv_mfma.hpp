@@ -168,9 +168,38 @@ __device__ __forceinline__ void mfma_chain(f32x4& acc, const f16x8v (&a)[N], con
                  : "+v"(acc) : "v"(a[0]), "v"(b[0]), "v"(a[1]), "v"(b[1]), "v"(a[2]), "v"(b[2]), "v"(a[3]), "v"(b[3]));
   }
 }
-// INT2: one v_mfma_f32_16x16x16_f16 per 16-code group (4 fp16 per lane).
-__device__ __forceinline__ void mfma_chain16(f32x4& acc, const f16x4v& a, const f16x4v& b) {
-  asm volatile(UQ_MF_PRE "v_mfma_f32_16x16x16_f16 %0, %1, %2, %0" UQ_MF_POST : "+v"(acc) : "v"(a), "v"(b));
+// Several groups' chains in one statement, independent accumulators
+// interleaved: the wait states before the first MFMA, between the dependent
+// MFMAs of a chain and after the last are paid once for all of them (each
+// dependent MFMA still has sixteen or more wait states after the one it
+// adds to; the operands were all written before the statement).
+template <int C>
+__device__ __forceinline__ void mfma_chains1(f32x4 (&acc)[C], const f16x8v (&a)[C], const f16x8v (&b)[C]) {
+  static_assert(C == 2 || C == 4, "two or four one-MFMA chains");
+  if constexpr (C == 2) {
+    asm volatile(UQ_MF_PRE UQ_MF_OP "%0, %2, %3, %0\n\t" UQ_MF_OP "%1, %4, %5, %1" UQ_MF_POST
+                 : "+v"(acc[0]), "+v"(acc[1]) : "v"(a[0]), "v"(b[0]), "v"(a[1]), "v"(b[1]));
+  } else {
+    asm volatile(UQ_MF_PRE UQ_MF_OP "%0, %4, %5, %0\n\t" UQ_MF_OP "%1, %6, %7, %1\n\t" UQ_MF_OP "%2, %8, %9, %2\n\t"
+                 UQ_MF_OP "%3, %10, %11, %3" UQ_MF_POST
+                 : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3])
+                 : "v"(a[0]), "v"(b[0]), "v"(a[1]), "v"(b[1]), "v"(a[2]), "v"(b[2]), "v"(a[3]), "v"(b[3]));
+  }
+}
+// Two chains of two MFMAs: a0 b0 of each, then a1 b1 of each.
+__device__ __forceinline__ void mfma_chains2x2(f32x4 (&acc)[2], const f16x8v (&a)[2][2], const f16x8v (&b)[2][2]) {
+  asm volatile(UQ_MF_PRE UQ_MF_OP "%0, %2, %3, %0\n\t" UQ_MF_OP "%1, %6, %7, %1\n\t"
+               UQ_MF_PRE UQ_MF_OP "%0, %4, %5, %0\n\t" UQ_MF_OP "%1, %8, %9, %1" UQ_MF_POST
+               : "+v"(acc[0]), "+v"(acc[1])
+               : "v"(a[0][0]), "v"(b[0][0]), "v"(a[0][1]), "v"(b[0][1]), "v"(a[1][0]), "v"(b[1][0]), "v"(a[1][1]),
+                 "v"(b[1][1]));
+}
+// INT2: four 16-code groups, one v_mfma_f32_16x16x16_f16 each (4 fp16 per lane).
+__device__ __forceinline__ void mfma_chains16x4(f32x4 (&acc)[4], const f16x4v (&a)[4], const f16x4v (&b)[4]) {
+  asm volatile(UQ_MF_PRE "v_mfma_f32_16x16x16_f16 %0, %4, %5, %0\n\tv_mfma_f32_16x16x16_f16 %1, %6, %7, %1\n\t"
+               "v_mfma_f32_16x16x16_f16 %2, %8, %9, %2\n\tv_mfma_f32_16x16x16_f16 %3, %10, %11, %3" UQ_MF_POST
+               : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3])
+               : "v"(a[0]), "v"(b[0]), "v"(a[1]), "v"(b[1]), "v"(a[2]), "v"(b[2]), "v"(a[3]), "v"(b[3]));
 }
 #undef UQ_MF_PRE
 #undef UQ_MF_OP
@@ -386,33 +415,56 @@ __global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(const uint8_t* __rest
         else pv = *reinterpret_cast<const uint32_t*>(pls + ln * Ge::PP + (gi0 + g) * 4);
         par[g] = gk < ng ? pv : 0u;  // past K: 0
       }
+      // every group's chain starts at -1024 * SX; the sub-block's chains run
+      // in one asm statement where a helper covers the shape
+      f32x4 acc[GS];
 #pragma unroll
-      for (int g = 0; g < GS; ++g) {
-        f32x4 acc = {tc[g][0], tc[g][1], tc[g][2], tc[g][3]};  // the chain starts at -1024 * SX
-        if constexpr (KM == 16) {
-          static_assert(Ge::MPG == 1, "16-code groups: one MFMA each");
+      for (int g = 0; g < GS; ++g) acc[g] = f32x4{tc[g][0], tc[g][1], tc[g][2], tc[g][3]};
+      if constexpr (KM == 16) {
+        static_assert(Ge::MPG == 1 && GS == 4, "16-code groups: one MFMA each, four per sub-block");
+        f16x4v ca[4], cb[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
           uint32_t bb[4];
           mf_unpack<S>(bd[g][0], bd[g][1], lg, bb);
-          const f16x4v ca = __builtin_bit_cast(f16x4v, make_uint2(av[g].x, av[g].y));
-          const f16x4v cb = __builtin_bit_cast(f16x4v, make_uint2(bb[0], bb[1]));
-          mfma_chain16(acc, ca, cb);
-        } else {
-          f16x8v ca[Ge::MPG], cb[Ge::MPG];
+          ca[g] = __builtin_bit_cast(f16x4v, make_uint2(av[g].x, av[g].y));
+          cb[g] = __builtin_bit_cast(f16x4v, make_uint2(bb[0], bb[1]));
+        }
+        mfma_chains16x4(acc, ca, cb);
+      } else {
+        f16x8v ca[GS][Ge::MPG], cb[GS][Ge::MPG];
+#pragma unroll
+        for (int g = 0; g < GS; ++g)
 #pragma unroll
           for (int jj = 0; jj < Ge::MPG; ++jj) {
             const int j = g * Ge::MPG + jj;
             uint32_t bb[4];
             mf_unpack<S>(bd[j][0], bd[j][1], lg, bb);
-            ca[jj] = __builtin_bit_cast(f16x8v, av[j]);
-            cb[jj] = __builtin_bit_cast(f16x8v, make_uint4(bb[0], bb[1], bb[2], bb[3]));
+            ca[g][jj] = __builtin_bit_cast(f16x8v, av[j]);
+            cb[g][jj] = __builtin_bit_cast(f16x8v, make_uint4(bb[0], bb[1], bb[2], bb[3]));
           }
-          mfma_chain<Ge::MPG>(acc, ca, cb);
+        if constexpr (Ge::MPG == 1 && (GS == 2 || GS == 4)) {
+          f16x8v a1[GS], b1[GS];
+#pragma unroll
+          for (int g = 0; g < GS; ++g) {
+            a1[g] = ca[g][0];
+            b1[g] = cb[g][0];
+          }
+          mfma_chains1<GS>(acc, a1, b1);
+        } else if constexpr (Ge::MPG == 2 && GS == 2) {
+          mfma_chains2x2(acc, ca, cb);
+        } else {
+#pragma unroll
+          for (int g = 0; g < GS; ++g) mfma_chain<Ge::MPG>(acc[g], ca[g], cb[g]);
         }
+      }
+#pragma unroll
+      for (int g = 0; g < GS; ++g) {
         // y += s * t + z * SX for the group
         const float sc = h2f(uint16_t(par[g] & 0xFFFFu)), zc = h2f(uint16_t(par[g] >> 16));
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          yacc[i] = __builtin_fmaf(sc, acc[i], yacc[i]);
+          yacc[i] = __builtin_fmaf(sc, acc[g][i], yacc[i]);
           yacc[i] = __builtin_fmaf(zc, ts[g][i], yacc[i]);
         }
         // INT2's 32 groups per block: the scaling stays with its chain (left
