@@ -50,7 +50,6 @@ template <> struct Mf<UQ_INT8> { static constexpr int KM = 32; };
 template <> struct Mf<UQ_INT2> { static constexpr int KM = 16; };
 
 constexpr int kMfBlock = 128;          // code bytes per row per block (two dense loads of 8 rows)
-constexpr int kMfRowPitch = 144;       // LDS bytes per row of a block: 16 rows of 16-byte reads hit distinct banks
 constexpr int kMfXBytes = 64 * 1024;   // most LDS the staged activations may take
 
 // Schemes and groups the matrix-core GEMV serves (16x16x32 MFMAs, chains of
@@ -78,7 +77,16 @@ struct MfGeo {
   static constexpr int XPITCH = KP * 2 + 16;                 // LDS bytes per staged activation row
   static constexpr int X_BYTES = MT * XPITCH;
   static constexpr int T_BYTES = MT * NG * 8;                // (-1024 * SX, SX) per (group, row)
-  static constexpr int B_BYTES = 16 * kMfRowPitch;           // one wave's block
+  // With eight staged activation rows, INT4 with its parameters in registers
+  // stages each block in two halves of 64 bytes per row, one per four-MFMA
+  // sub-block, so that two workgroups fit a CU (80,000 bytes of LDS; measured
+  // on MI355X, INT4 G64 N11008 M=8 13.6 -> 11.4 us, N14336 17.5 -> 14.0 us;
+  // with fewer rows the whole blocks measured faster: M=2 / 4 8.5 / 9.3
+  // against 9.3 / 10.0 us, the half-line code loads costing more than the
+  // occupancy they no longer buy).
+  static constexpr int HB = (bits == 4 && QP <= 32 && MT == 8) ? 2 : 1;
+  static constexpr int BPITCH = kMfBlock / HB + 16;          // LDS bytes per row (16-byte reads: distinct banks)
+  static constexpr int B_BYTES = 16 * BPITCH;                // one wave's block (or half block)
   // A wave's parameters: up to two 16-byte slots per row go straight into
   // each lane's registers (the lane's weight row; the four lanes of a row
   // load the same bytes), which keeps them out of LDS so that more
@@ -273,15 +281,18 @@ __global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(const uint8_t* __rest
       pr[j] = load_stream<uint4>(params + row * int64_t(ng) * 4 + off);
     }
   }
-  const int lr = lane >> 3, lp = lane & 7;  // dense code loads: row within 8, 16-byte piece
+  // Dense code loads, two per block: rows 0-7 then 8-15 (lane: row within
+  // eight, 16-byte piece of the 128 bytes), or with half blocks the first then
+  // the second 64 bytes of all 16 rows (lane: row, 16-byte piece of the half).
+  const int lr = Ge::HB == 1 ? lane >> 3 : lane >> 2, lp = Ge::HB == 1 ? lane & 7 : lane & 3;
   uint4 cr[NBLK][2];
 #pragma unroll
   for (int b = 0; b < NBLK; ++b)
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      int64_t row = row0 + 8 * h + lr;
+      int64_t row = row0 + (Ge::HB == 1 ? 8 * h + lr : lr);
       row = row < n ? row : n - 1;
-      int off = wave * Ge::QB + b * kMfBlock + 16 * lp;
+      int off = wave * Ge::QB + b * kMfBlock + (Ge::HB == 1 ? 16 * lp : 64 * h + 16 * lp);
       off = off + 16 <= rowb ? off : rowb - 16;
       cr[b][h] = load_stream<uint4>(codes + row * int64_t(rowb) + off);
     }
@@ -339,19 +350,22 @@ __global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(const uint8_t* __rest
   //     its scaling.
   const int ln = lane & 15, lg = lane >> 4;   // MFMA column (weight row) and k block of this lane
   const uint8_t* xa = xs + (ln % MT) * Ge::XPITCH;  // this lane's A row (rows past MT repeat)
-  const uint8_t* bp = blk + ln * kMfRowPitch;       // this lane's weight row of the block
+  const uint8_t* bp = blk + ln * Ge::BPITCH;        // this lane's weight row of the block
   // MFMAs per sub-block: four, which keeps the kernel within 80 VGPRs (with
   // the parameters in registers and staging in LDS, three 8-wave workgroups
   // per CU at up to four activation rows; eight MFMAs per sub-block took 128)
   constexpr int SB = KM == 16 ? 4 : (Ge::MPB < 4 ? Ge::MPB : 4);
   constexpr int GS = SB / Ge::MPG;                  // groups per sub-block
   static_assert(Ge::MPB % SB == 0 && SB % Ge::MPG == 0, "sub-blocks hold whole groups");
+  static_assert(Ge::HB == 1 || Ge::MPB / SB == Ge::HB, "a half block per sub-block");
   f32x4 yacc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int b = 0; b < NBLK; ++b) {
+    if constexpr (Ge::HB == 1) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-      *reinterpret_cast<uint4*>(blk + (8 * h + lr) * kMfRowPitch + 16 * lp) = cr[b][h];
+      for (int h = 0; h < 2; ++h)
+        *reinterpret_cast<uint4*>(blk + (8 * h + lr) * Ge::BPITCH + 16 * lp) = cr[b][h];
+    }
     // (a wave's LDS accesses execute in issue order: only the compiler must
     //  not move the block's reads and writes across each other)
     asm volatile("" ::: "memory");
@@ -362,6 +376,12 @@ __global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(const uint8_t* __rest
         // hoists every sub-block's LDS reads and runs out of registers)
         asm volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr (Ge::HB == 2) {
+        // this sub-block's half of the block (written after the previous
+        // sub-block's reads, which a wave's LDS accesses keep in order)
+        *reinterpret_cast<uint4*>(blk + lr * Ge::BPITCH + 16 * lp) = cr[b][sb];
+        asm volatile("" ::: "memory");
       }
       const int q0 = sb * SB;                                   // first MFMA of the sub-block in the block
       const int kq0 = wave * Ge::QK + (b * Ge::MPB + q0) * KM;  // its first k
@@ -376,7 +396,7 @@ __global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(const uint8_t* __rest
           bd[j][0] = *reinterpret_cast<const uint32_t*>(bp + q * 4);  // the group's 16 codes
           bd[j][1] = 0u;
         } else if constexpr (S == UQ_INT4) {
-          bd[j][0] = *reinterpret_cast<const uint32_t*>(bp + q * 16 + 4 * lg);
+          bd[j][0] = *reinterpret_cast<const uint32_t*>(bp + (q % (Ge::MPB / Ge::HB)) * 16 + 4 * lg);
           bd[j][1] = 0u;
         } else {
           const uint2 v = *reinterpret_cast<const uint2*>(bp + q * 32 + 8 * lg);

@@ -153,6 +153,23 @@ def test_gemv_batched_equivalence(lib):
                     assert np.array_equal(full[m].view(np.uint32), full[ms[-1]][:m].view(np.uint32)), (scheme, group, k, m)
 
 
+def test_gemv_g32_large_matrix_rows_agree(lib):
+    """INT4 G32 on a matrix of 8192 or more weight rows runs on the matrix cores
+    from three activation rows: rows of M = 3, 4, 5, 8 agree bit for bit (one
+    kernel, a sum order that does not depend on M) and with the oracle within
+    the gate; M = 2 (the dot product) agrees within the gate."""
+    w, x = workloads.make_random(8200, 1024, 8, seed=21, outliers=True)
+    lay, codes, params = packed_on_device(lib, "int4", 32, w)
+    wdq = oracle_dequant(w, "int4", 32)
+    full = {}
+    for m in (2, 3, 4, 5, 8):
+        note(f"gemv int4 G32 n=8200 m={m}")
+        full[m] = run_gemv(lib, lay, codes, params, x, m)
+        gate(full[m], o.gemv_ref(x[:m], wdq), x[:m], wdq, f"int4 G32 8200 m={m}")
+    for m in (3, 4, 5):
+        assert np.array_equal(full[m].view(np.uint32), full[8][:m].view(np.uint32)), m
+
+
 @pytest.mark.parametrize("scheme,group,n,k", [
     ("int4", 64, 300, 4096), ("int4", 128, 777, 4096), ("int4", 64, 11008, 4096), ("int4", 64, 37, 1024),
     ("int4", 128, 129, 2560), ("int4", 64, 100, 16384), ("int8", 32, 333, 1024), ("int8", 64, 45, 2048),
