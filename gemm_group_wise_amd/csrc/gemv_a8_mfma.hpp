@@ -134,6 +134,28 @@ __device__ __forceinline__ void a8_chain(i32x4v& acc, const uint4 (&a)[N], const
                  : "+v"(acc) : "v"(av[0]), "v"(bv[0]), "v"(av[1]), "v"(bv[1]));
   }
 }
+// Several groups' chains in one statement with independent accumulators
+// interleaved, so that the wait states are paid once for all of them (each
+// dependent MFMA still follows the one it adds to by sixteen or more).
+template <int C>
+__device__ __forceinline__ void a8_chains1(i32x4v (&acc)[C], const uint4 (&a)[C], const uint4 (&b)[C]) {
+  static_assert(C == 2 || C == 4, "two or four one-MFMA chains");
+  i32x4v av[C], bv[C];
+#pragma unroll
+  for (int j = 0; j < C; ++j) {
+    av[j] = __builtin_bit_cast(i32x4v, a[j]);
+    bv[j] = __builtin_bit_cast(i32x4v, b[j]);
+  }
+  if constexpr (C == 2) {
+    asm volatile(UQ_A8M_PRE "v_mfma_i32_16x16x64_i8 %0, %2, %3, %0\n\tv_mfma_i32_16x16x64_i8 %1, %4, %5, %1" UQ_A8M_POST
+                 : "+v"(acc[0]), "+v"(acc[1]) : "v"(av[0]), "v"(bv[0]), "v"(av[1]), "v"(bv[1]));
+  } else {
+    asm volatile(UQ_A8M_PRE "v_mfma_i32_16x16x64_i8 %0, %4, %5, %0\n\tv_mfma_i32_16x16x64_i8 %1, %6, %7, %1\n\t"
+                 "v_mfma_i32_16x16x64_i8 %2, %8, %9, %2\n\tv_mfma_i32_16x16x64_i8 %3, %10, %11, %3" UQ_A8M_POST
+                 : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3])
+                 : "v"(av[0]), "v"(bv[0]), "v"(av[1]), "v"(bv[1]), "v"(av[2]), "v"(bv[2]), "v"(av[3]), "v"(bv[3]));
+  }
+}
 #undef UQ_A8M_PRE
 #undef UQ_A8M_POST
 
@@ -266,36 +288,56 @@ __global__ __launch_bounds__(64 * W) void gemv_a8_mfma_kernel(const uint8_t* __r
     asm volatile("" ::: "memory");
     constexpr int GPB = Ge::MPB / Ge::MPG;  // groups per block (a group never straddles blocks)
     static_assert(Ge::MPB % Ge::MPG == 0, "blocks hold whole groups");
+    // the block's groups: operands first, then their chains (one-MFMA chains
+    // in one asm statement: measured on MI355X, INT4 G64 N11008 M=2 / 4 / 8
+    // 8.7 / 10.3 / 13.1 -> 8.1 / 9.8 / 12.7 us), then each group's scaling
+    uint4 av[GPB][Ge::MPG], bv[GPB][Ge::MPG];
+    float sx[GPB][4];
+    int qs[GPB][4];
+    uint32_t par[GPB];
 #pragma unroll
     for (int g = 0; g < GPB; ++g) {
-      const int q0 = g * Ge::MPG;                             // first MFMA of the group in the block
+      const int q0 = g * Ge::MPG;                               // first MFMA of the group in the block
       const int kq0 = wave * Ge::QK + (b * Ge::MPB + q0) * KM;  // its first k
-      const int gk = kq0 / G;                                 // global group
-      const int gi = (b * Ge::MPB + q0) / Ge::MPG;            // group within the wave
-      uint4 av[Ge::MPG], bv[Ge::MPG];
+      const int gk = kq0 / G;                                   // global group
+      const int gi = (b * Ge::MPB + q0) / Ge::MPG;              // group within the wave
 #pragma unroll
       for (int jj = 0; jj < Ge::MPG; ++jj) {
         const int q = q0 + jj;
-        bv[jj] = a8m_unpack<S>(bp + (q * KM + KL * lg) * bits / 8);
-        av[jj] = *reinterpret_cast<const uint4*>(xa + kq0 + jj * KM + KL * lg);
+        bv[g][jj] = a8m_unpack<S>(bp + (q * KM + KL * lg) * bits / 8);
+        av[g][jj] = *reinterpret_cast<const uint4*>(xa + kq0 + jj * KM + KL * lg);
       }
-      float sx[4];
-      int qs[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float2 t = tab[gk * MT + (4 * lg + i) % MT];
-        sx[i] = t.x;
-        qs[i] = __float_as_int(t.y);
+        sx[g][i] = t.x;
+        qs[g][i] = __float_as_int(t.y);
       }
-      const uint32_t par = gk < ng ? *reinterpret_cast<const uint32_t*>(pls + ln * Ge::PP + gi * 4) : 0u;  // past K: 0
-      i32x4v acc = {0, 0, 0, 0};
-      a8_chain<Ge::MPG>(acc, av, bv);
-      const float sc = h2f(uint16_t(par & 0xFFFFu)), zc = h2f(uint16_t(par >> 16));
+      par[g] = gk < ng ? *reinterpret_cast<const uint32_t*>(pls + ln * Ge::PP + gi * 4) : 0u;  // past K: 0
+    }
+    i32x4v acc[GPB];
+#pragma unroll
+    for (int g = 0; g < GPB; ++g) acc[g] = i32x4v{0, 0, 0, 0};
+    if constexpr (Ge::MPG == 1 && (GPB == 2 || GPB == 4)) {
+      uint4 a1[GPB], b1[GPB];
+#pragma unroll
+      for (int g = 0; g < GPB; ++g) {
+        a1[g] = av[g][0];
+        b1[g] = bv[g][0];
+      }
+      a8_chains1<GPB>(acc, a1, b1);
+    } else {  // two-MFMA chains (128-code groups): sharing one statement measured no faster
+#pragma unroll
+      for (int g = 0; g < GPB; ++g) a8_chain<Ge::MPG>(acc[g], av[g], bv[g]);
+    }
+#pragma unroll
+    for (int g = 0; g < GPB; ++g) {
+      const float sc = h2f(uint16_t(par[g] & 0xFFFFu)), zc = h2f(uint16_t(par[g] >> 16));
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int dd = S == UQ_INT8 ? acc[i] + 128 * qs[i] : acc[i];
-        const float t = __builtin_fmaf(sc, float(dd), zc * float(qs[i]));
-        yacc[i] = __builtin_fmaf(sx[i], t, yacc[i]);
+        const int dd = S == UQ_INT8 ? acc[g][i] + 128 * qs[g][i] : acc[g][i];
+        const float t = __builtin_fmaf(sc, float(dd), zc * float(qs[g][i]));
+        yacc[i] = __builtin_fmaf(sx[g][i], t, yacc[i]);
       }
     }
     asm volatile("" ::: "memory");  // the next block's writes stay after this block's reads
