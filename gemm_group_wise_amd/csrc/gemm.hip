@@ -7,7 +7,8 @@
 // both casts round to nearest even.
 //
 // One or two launches on the caller's stream:
-//   1. From 65 activation rows: x (fp16) -> bf16 into an activation
+//   1. From 65 activation rows (INT4 and NF4 always; INT8 and INT2 on
+//      128-row tiles): x (fp16) -> bf16 into an activation
 //      workspace, once per call, so the conversion is not repeated by every
 //      column tile (there the GEMM is bound by VALU issue).  Up to 64 rows
 //      the GEMM is bound by memory latency instead; it stages the caller's
@@ -1190,7 +1191,7 @@ hipError_t gemm_scratch(hipStream_t stream, void** out) {
 
 hipError_t launch_gemm(const uq_layout* L, const void* codes, const void* params, const uint16_t* x,
                        float* y, int m, void* workspace, hipStream_t stream) {
-  GemmPlan plan = plan_gemm(m, L->n);
+  GemmPlan plan = plan_gemm(m, L->n, L->scheme);
 #define UQ_GEMM_CASE(SC, GR) \
   case SC * 1000 + GR: plan.ksplit = plan_ksplit<SC, GR>(plan, m, L->n, L->k); break;
   switch (L->scheme * 1000 + L->group) {

@@ -91,10 +91,17 @@ struct GemmPlan {
   bool xf;  // the GEMM stages the caller's fp16 x and rounds it to bf16 itself
 };
 
-inline GemmPlan plan_gemm(int64_t m, int64_t n) {
+// Above 64 rows on 64-row tiles, INT8 and INT2 (whose dequant leaves room in
+// the VALU budget) also stage the caller's fp16 x and round it themselves,
+// which saves the conversion launch (measured on MI355X, N = 4096: INT8 M =
+// 80 / 128 / 256 25.3 / 25.7 / 26.9 -> 23.2 / 23.5 / 24.0 us, Q8_0-style
+// INT8 G32 M = 256 28.0 -> 24.7 us, INT2 M = 256 23.9 -> 22.5 us),
+// while INT4 and NF4 measured slower that way (INT4 N = 11008 M = 128 37.3
+// -> 38.0 us, NF4 N = 14336 M = 128 47.2 -> 50.4 us).
+inline GemmPlan plan_gemm(int64_t m, int64_t n, int32_t scheme) {
   auto tiles = [&](int64_t bm, int64_t bn) { return ((m + bm - 1) / bm) * ((n + bn - 1) / bn); };
   if (m > 64 && tiles(128, 128) >= kGemmMinTiles) return {128, 2, 1, false};
-  if (m > 64) return {64, 1, 1, false};
+  if (m > 64) return {64, 1, 1, scheme == UQ_INT8 || scheme == UQ_INT2};
   if (m > 32) return {64, 1, 1, true};
   return {32, 1, 1, true};
 }
@@ -111,7 +118,7 @@ struct GemmWorkspace {
 
 inline GemmWorkspace gemm_workspace(const uq_layout* L, int64_t m) {
   auto up = [](size_t v) { return (v + 255) / 256 * 256; };
-  const GemmPlan p = plan_gemm(m, L->n);
+  const GemmPlan p = plan_gemm(m, L->n, L->scheme);
   GemmWorkspace w;
   w.counters = 0;
   w.act = up(size_t(kGemmMaxSplitTiles) * 4);

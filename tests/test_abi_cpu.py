@@ -228,6 +228,13 @@ def test_gemm_workspace_size(lib):
     assert lib.uq_gemm_workspace_size(lay, 64) == up(65536 + 4 * 64 * n * 4)
     assert lib.uq_gemm_workspace_size(lay, 256) == up(65536 + 256 * k * 2)
     assert lib.uq_gemm_workspace_size(lay, 300) == up(65536 + 384 * k * 2)
+    # N = 4096 above 64 rows runs 64-row tiles: INT8 and INT2 stage the caller's
+    # fp16 x themselves (no bf16 copy), INT4 and NF4 read a bf16 copy
+    n2 = 4096
+    for scheme, group, bf16_copy in (("int8", 128, False), ("int2", 16, False), ("int4", 128, True), ("nf4", 64, True)):
+        lay2 = lib.layout(scheme, group, n2, k)
+        want = up(65536 + (256 * k * 2 if bf16_copy else 0) + 4 * 256 * n2 * 4)
+        assert lib.uq_gemm_workspace_size(lay2, 256) == want, scheme
     for bad in (0, -1, 65537):
         with pytest.raises(lib.UQError) as e:
             lib.uq_gemm_workspace_size(lay, bad)
