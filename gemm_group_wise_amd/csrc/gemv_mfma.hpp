@@ -351,9 +351,8 @@ __global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(const uint8_t* __rest
   const int ln = lane & 15, lg = lane >> 4;   // MFMA column (weight row) and k block of this lane
   const uint8_t* xa = xs + (ln % MT) * Ge::XPITCH;  // this lane's A row (rows past MT repeat)
   const uint8_t* bp = blk + ln * Ge::BPITCH;        // this lane's weight row of the block
-  // MFMAs per sub-block: four, which keeps the kernel within 80 VGPRs (with
-  // the parameters in registers and staging in LDS, three 8-wave workgroups
-  // per CU at up to four activation rows; eight MFMAs per sub-block took 128)
+  // MFMAs per sub-block: four (67-90 VGPRs up to eight activation rows;
+  // eight MFMAs per sub-block took 128 and left two workgroups per CU)
   constexpr int SB = KM == 16 ? 4 : (Ge::MPB < 4 ? Ge::MPB : 4);
   constexpr int GS = SB / Ge::MPG;                  // groups per sub-block
   static_assert(Ge::MPB % SB == 0 && SB % Ge::MPG == 0, "sub-blocks hold whole groups");
