@@ -1,5 +1,5 @@
 // Activation-quantized GEMV on the integer matrix cores, 2 to 8 activation
-// rows of INT4 and INT8 weights with groups of 64 or 128 ("Ultra LLM Engine", Core Components
+// rows of INT4 and INT8 weights with groups of 32, 64 or 128 ("Ultra LLM Engine", Core Components
 // > Quantized Model: the quantized layers quantize their activations on the
 // fly; Fused Kernels: the decode GEMV).
 //
@@ -8,15 +8,15 @@
 //     y[m][n] = sum_g s_x * (s * D + z * Q),  D = sum q_w * q_x,  Q = sum q_x,
 // with D and Q exact integers and only the per-group scaling in fp32.  Here
 // D comes from v_mfma_i32_16x16x64_i8: one chain of G / 64 MFMAs per group,
-// int32 accumulation (|D| < 2^22).  (With 32-code groups, on
-// v_mfma_i32_16x16x32_i8, it measured slower than the dot-product kernel.)
+// int32 accumulation (|D| < 2^22); 32-code groups take one
+// v_mfma_i32_16x16x32_i8 each (8 codes per lane).
 //   * B operand: the codes as bytes, INT8 with the sign bit flipped (q - 128,
 //     corrected by 128 * Q), INT4 nibbles spread to bytes with two masks;
 //   * A operand: the activation codes, staged in LDS in the order the
 //     unpacked weight bytes take (INT4: even codes, then odd codes, of each
 //     8), with (s_x, Q) per (group, activation row);
 //   * MFMA lane layout (16x16x64): lane l holds A[row l % 16][k-block l / 16]
-//     and B[k-block l / 16][column l % 16], 16 consecutive k per lane;
+//     and B[k-block l / 16][column l % 16], 16 consecutive k per lane (8 on the 16x16x32);
 //     D rows 4 (l / 16) .. + 3 are activation rows, column l % 16 a weight row.
 // Work split as in the fp16 matrix-core GEMV (gemv_mfma.hpp): a workgroup of
 // W waves owns 16 weight rows, wave w takes the w-th of W equal slices of
@@ -27,6 +27,8 @@
 // The sums of a row do not depend on how many activation rows the call has:
 // the rows of calls with 2 to 8 activation rows agree bit for bit.
 #pragma once
+
+#include <type_traits>
 
 #include "device_common.hpp"
 
@@ -39,13 +41,13 @@ constexpr int kA8mXBytes = 64 * 1024;  // most LDS the staged activation codes m
 
 template <int S, int G>
 constexpr bool a8_mfma_scheme() {
-  return (S == UQ_INT4 || S == UQ_INT8) && (G == 64 || G == 128);
+  return (S == UQ_INT4 || S == UQ_INT8) && (G == 32 || G == 64 || G == 128);
 }
 
 template <int S, int G, int MT, int W, int NBLK>
 struct A8mGeo {
   static constexpr int bits = Fmt<S>::bits;
-  static constexpr int KM = 64;                              // k per MFMA
+  static constexpr int KM = G == 32 ? 32 : 64;               // k per MFMA (16x16x32 for 32-code groups)
   static constexpr int KL = KM / 4;                          // k per lane per MFMA
   static constexpr int QB = NBLK * kA8mBlock;                // code bytes per row per wave
   static constexpr int QK = QB * 8 / bits;                   // k per wave
@@ -156,11 +158,42 @@ __device__ __forceinline__ void a8_chains1(i32x4v (&acc)[C], const uint4 (&a)[C]
                  : "v"(av[0]), "v"(bv[0]), "v"(av[1]), "v"(bv[1]), "v"(av[2]), "v"(bv[2]), "v"(av[3]), "v"(bv[3]));
   }
 }
+// 32-code groups: one v_mfma_i32_16x16x32_i8 per group (8 codes per lane),
+// up to four groups' MFMAs in one statement.
+template <int C>
+__device__ __forceinline__ void a8_chains32(i32x4v (&acc)[C], const uint2 (&a)[C], const uint2 (&b)[C]) {
+  static_assert(C == 2 || C == 4, "two or four one-MFMA chains");
+  long av[C], bv[C];
+#pragma unroll
+  for (int j = 0; j < C; ++j) {
+    av[j] = __builtin_bit_cast(long, a[j]);
+    bv[j] = __builtin_bit_cast(long, b[j]);
+  }
+  if constexpr (C == 2) {
+    asm volatile(UQ_A8M_PRE "v_mfma_i32_16x16x32_i8 %0, %2, %3, %0\n\tv_mfma_i32_16x16x32_i8 %1, %4, %5, %1" UQ_A8M_POST
+                 : "+v"(acc[0]), "+v"(acc[1]) : "v"(av[0]), "v"(bv[0]), "v"(av[1]), "v"(bv[1]));
+  } else {
+    asm volatile(UQ_A8M_PRE "v_mfma_i32_16x16x32_i8 %0, %4, %5, %0\n\tv_mfma_i32_16x16x32_i8 %1, %6, %7, %1\n\t"
+                 "v_mfma_i32_16x16x32_i8 %2, %8, %9, %2\n\tv_mfma_i32_16x16x32_i8 %3, %10, %11, %3" UQ_A8M_POST
+                 : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3])
+                 : "v"(av[0]), "v"(bv[0]), "v"(av[1]), "v"(bv[1]), "v"(av[2]), "v"(bv[2]), "v"(av[3]), "v"(bv[3]));
+  }
+}
 #undef UQ_A8M_PRE
 #undef UQ_A8M_POST
 
 // B operand bytes of one MFMA from the lane's 16 codes: INT8 q - 128 as
 // signed bytes, INT4 nibbles as bytes (low nibbles, then high, per dword).
+template <int S>
+__device__ __forceinline__ uint2 a8m_unpack8(const uint8_t* p) {
+  if constexpr (S == UQ_INT8) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    return make_uint2(v.x ^ 0x80808080u, v.y ^ 0x80808080u);
+  } else {
+    const uint32_t v = *reinterpret_cast<const uint32_t*>(p);
+    return make_uint2(v & 0x0F0F0F0Fu, (v >> 4) & 0x0F0F0F0Fu);
+  }
+}
 template <int S>
 __device__ __forceinline__ uint4 a8m_unpack(const uint8_t* p) {
   if constexpr (S == UQ_INT8) {
@@ -288,56 +321,75 @@ __global__ __launch_bounds__(64 * W) void gemv_a8_mfma_kernel(const uint8_t* __r
     asm volatile("" ::: "memory");
     constexpr int GPB = Ge::MPB / Ge::MPG;  // groups per block (a group never straddles blocks)
     static_assert(Ge::MPB % Ge::MPG == 0, "blocks hold whole groups");
-    // the block's groups: operands first, then their chains (one-MFMA chains
-    // in one asm statement: measured on MI355X, INT4 G64 N11008 M=2 / 4 / 8
-    // 8.7 / 10.3 / 13.1 -> 8.1 / 9.8 / 12.7 us), then each group's scaling
-    uint4 av[GPB][Ge::MPG], bv[GPB][Ge::MPG];
-    float sx[GPB][4];
-    int qs[GPB][4];
-    uint32_t par[GPB];
+    constexpr int SBG = GPB < 4 ? GPB : 4;  // groups per sub-block
+    static_assert(GPB % SBG == 0, "sub-blocks hold whole groups");
+    using Frag = typename std::conditional<KM == 64, uint4, uint2>::type;
 #pragma unroll
-    for (int g = 0; g < GPB; ++g) {
-      const int q0 = g * Ge::MPG;                               // first MFMA of the group in the block
-      const int kq0 = wave * Ge::QK + (b * Ge::MPB + q0) * KM;  // its first k
-      const int gk = kq0 / G;                                   // global group
-      const int gi = (b * Ge::MPB + q0) / Ge::MPG;              // group within the wave
+    for (int sbk = 0; sbk < GPB / SBG; ++sbk) {
+      if constexpr (GPB / SBG > 1) {
+        // one sub-block's reads in flight at a time
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // the sub-block's groups: operands first, then their chains (one-MFMA
+      // chains in one asm statement: measured on MI355X, INT4 G64 N11008 M=2
+      // / 4 / 8 8.7 / 10.3 / 13.1 -> 8.1 / 9.8 / 12.7 us), then each group's
+      // scaling
+      Frag av[SBG][Ge::MPG], bv[SBG][Ge::MPG];
+      float sx[SBG][4];
+      int qs[SBG][4];
+      uint32_t par[SBG];
 #pragma unroll
-      for (int jj = 0; jj < Ge::MPG; ++jj) {
-        const int q = q0 + jj;
-        bv[g][jj] = a8m_unpack<S>(bp + (q * KM + KL * lg) * bits / 8);
-        av[g][jj] = *reinterpret_cast<const uint4*>(xa + kq0 + jj * KM + KL * lg);
+      for (int g = 0; g < SBG; ++g) {
+        const int q0 = (sbk * SBG + g) * Ge::MPG;                // first MFMA of the group in the block
+        const int kq0 = wave * Ge::QK + (b * Ge::MPB + q0) * KM;  // its first k
+        const int gk = kq0 / G;                                   // global group
+        const int gi = (b * Ge::MPB + q0) / Ge::MPG;              // group within the wave
+#pragma unroll
+        for (int jj = 0; jj < Ge::MPG; ++jj) {
+          const int q = q0 + jj;
+          if constexpr (KM == 64) {
+            bv[g][jj] = a8m_unpack<S>(bp + (q * KM + KL * lg) * bits / 8);
+            av[g][jj] = *reinterpret_cast<const uint4*>(xa + kq0 + jj * KM + KL * lg);
+          } else {
+            bv[g][jj] = a8m_unpack8<S>(bp + (q * KM + KL * lg) * bits / 8);
+            av[g][jj] = *reinterpret_cast<const uint2*>(xa + kq0 + jj * KM + KL * lg);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float2 t = tab[gk * MT + (4 * lg + i) % MT];
+          sx[g][i] = t.x;
+          qs[g][i] = __float_as_int(t.y);
+        }
+        par[g] = gk < ng ? *reinterpret_cast<const uint32_t*>(pls + ln * Ge::PP + gi * 4) : 0u;  // past K: 0
+      }
+      i32x4v acc[SBG];
+#pragma unroll
+      for (int g = 0; g < SBG; ++g) acc[g] = i32x4v{0, 0, 0, 0};
+      if constexpr (Ge::MPG == 1 && (SBG == 2 || SBG == 4)) {
+        Frag a1[SBG], b1[SBG];
+#pragma unroll
+        for (int g = 0; g < SBG; ++g) {
+          a1[g] = av[g][0];
+          b1[g] = bv[g][0];
+        }
+        if constexpr (KM == 64) a8_chains1<SBG>(acc, a1, b1);
+        else a8_chains32<SBG>(acc, a1, b1);
+      } else {  // two-MFMA chains (128-code groups): sharing one statement measured no faster
+        static_assert(KM == 64, "32-code groups: one MFMA each");
+#pragma unroll
+        for (int g = 0; g < SBG; ++g) a8_chain<Ge::MPG>(acc[g], av[g], bv[g]);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float2 t = tab[gk * MT + (4 * lg + i) % MT];
-        sx[g][i] = t.x;
-        qs[g][i] = __float_as_int(t.y);
-      }
-      par[g] = gk < ng ? *reinterpret_cast<const uint32_t*>(pls + ln * Ge::PP + gi * 4) : 0u;  // past K: 0
-    }
-    i32x4v acc[GPB];
+      for (int g = 0; g < SBG; ++g) {
+        const float sc = h2f(uint16_t(par[g] & 0xFFFFu)), zc = h2f(uint16_t(par[g] >> 16));
 #pragma unroll
-    for (int g = 0; g < GPB; ++g) acc[g] = i32x4v{0, 0, 0, 0};
-    if constexpr (Ge::MPG == 1 && (GPB == 2 || GPB == 4)) {
-      uint4 a1[GPB], b1[GPB];
-#pragma unroll
-      for (int g = 0; g < GPB; ++g) {
-        a1[g] = av[g][0];
-        b1[g] = bv[g][0];
-      }
-      a8_chains1<GPB>(acc, a1, b1);
-    } else {  // two-MFMA chains (128-code groups): sharing one statement measured no faster
-#pragma unroll
-      for (int g = 0; g < GPB; ++g) a8_chain<Ge::MPG>(acc[g], av[g], bv[g]);
-    }
-#pragma unroll
-    for (int g = 0; g < GPB; ++g) {
-      const float sc = h2f(uint16_t(par[g] & 0xFFFFu)), zc = h2f(uint16_t(par[g] >> 16));
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int dd = S == UQ_INT8 ? acc[g][i] + 128 * qs[g][i] : acc[g][i];
-        const float t = __builtin_fmaf(sc, float(dd), zc * float(qs[g][i]));
-        yacc[i] = __builtin_fmaf(sx[g][i], t, yacc[i]);
+        for (int i = 0; i < 4; ++i) {
+          const int dd = S == UQ_INT8 ? acc[g][i] + 128 * qs[g][i] : acc[g][i];
+          const float t = __builtin_fmaf(sc, float(dd), zc * float(qs[g][i]));
+          yacc[i] = __builtin_fmaf(sx[g][i], t, yacc[i]);
+        }
       }
     }
     asm volatile("" ::: "memory");  // the next block's writes stay after this block's reads
