@@ -1,5 +1,6 @@
 // Activation-quantized GEMV on the integer matrix cores, 2 to 8 activation
-// rows of INT4 and INT8 weights with groups of 32, 64 or 128 ("Ultra LLM Engine", Core Components
+// rows of INT4 and INT8 weights with groups of 32, 64 or 128 and of INT2
+// weights with groups of 16 ("Ultra LLM Engine", Core Components
 // > Quantized Model: the quantized layers quantize their activations on the
 // fly; Fused Kernels: the decode GEMV).
 //
@@ -9,7 +10,8 @@
 // with D and Q exact integers and only the per-group scaling in fp32.  Here
 // D comes from v_mfma_i32_16x16x64_i8: one chain of G / 64 MFMAs per group,
 // int32 accumulation (|D| < 2^22); 32-code groups take one
-// v_mfma_i32_16x16x32_i8 each (8 codes per lane).
+// v_mfma_i32_16x16x32_i8 each (8 codes per lane), and so do 16-code groups,
+// two to a k range, each with the other group's B lanes zeroed.
 //   * B operand: the codes as bytes, INT8 with the sign bit flipped (q - 128,
 //     corrected by 128 * Q), INT4 nibbles spread to bytes with two masks;
 //   * A operand: the activation codes, staged in LDS in the order the
@@ -41,21 +43,25 @@ constexpr int kA8mXBytes = 64 * 1024;  // most LDS the staged activation codes m
 
 template <int S, int G>
 constexpr bool a8_mfma_scheme() {
-  return (S == UQ_INT4 || S == UQ_INT8) && (G == 32 || G == 64 || G == 128);
+  return ((S == UQ_INT4 || S == UQ_INT8) && (G == 32 || G == 64 || G == 128)) || (S == UQ_INT2 && G == 16);
 }
 
 template <int S, int G, int MT, int W, int NBLK>
 struct A8mGeo {
   static constexpr int bits = Fmt<S>::bits;
-  static constexpr int KM = G == 32 ? 32 : 64;               // k per MFMA (16x16x32 for 32-code groups)
+  static constexpr int KM = G <= 32 ? 32 : 64;               // k per MFMA (16x16x32 for 16- and 32-code groups)
   static constexpr int KL = KM / 4;                          // k per lane per MFMA
   static constexpr int QB = NBLK * kA8mBlock;                // code bytes per row per wave
   static constexpr int QK = QB * 8 / bits;                   // k per wave
   static constexpr int KP = W * QK;                          // padded K of a launch
   static constexpr int GPW = QK / G;                         // groups per wave
   static constexpr int NG = KP / G;                          // groups of the padded K
-  static constexpr int MPB = kA8mBlock * 8 / bits / KM;      // MFMAs per block
-  static constexpr int MPG = G / KM;                         // MFMAs per group
+  static constexpr int MPB = kA8mBlock * 8 / bits / KM;      // k ranges of one MFMA per block
+  // 16-code groups (INT2 G16) share a k range two to an MFMA: each group's
+  // MFMA takes the range with the other group's half of the B lanes zeroed
+  static constexpr bool HALF = G < KM;
+  static constexpr int MPG = HALF ? 1 : G / KM;              // MFMAs per group
+  static constexpr int GPB = HALF ? MPB * (KM / G) : MPB / MPG;  // groups per block
   static constexpr int QP = GPW * 4;                         // parameter bytes per row per wave
   static constexpr int PP = QP + 16;                         // their LDS pitch per row
   static constexpr int XPITCH = KP + 16;                     // LDS bytes per staged activation row
@@ -70,7 +76,7 @@ struct A8mGeo {
   // An MFMA lies in one group and a wave holds whole groups; whole 16-byte
   // parameter slots per row; a group's pieces are consecutive lanes of one
   // wave; the staged codes fit their LDS budget.
-  static constexpr bool ok = a8_mfma_scheme<S, G>() && G % KM == 0 && QK % G == 0 && QP % 16 == 0 &&
+  static constexpr bool ok = a8_mfma_scheme<S, G>() && (G % KM == 0 || KM == 2 * G) && QK % G == 0 && QP % 16 == 0 &&
                              64 % (G / 16) == 0 && X_BYTES <= kA8mXBytes && B_BYTES + P_BYTES >= 1024 &&
                              LDS <= 160 * 1024;
 };
@@ -81,6 +87,7 @@ struct A8mGeo {
 template <int S>
 __device__ __forceinline__ constexpr int a8m_src(int p) {
   if constexpr (S == UQ_INT4) return (p & 8) + 2 * (p & 3) + ((p >> 2) & 1);
+  else if constexpr (S == UQ_INT2) return (p & 8) + 4 * (p & 1) + ((p >> 1) & 3);  // per 8: 0 4 1 5 2 6 3 7
   else return p;
 }
 
@@ -189,6 +196,11 @@ __device__ __forceinline__ uint2 a8m_unpack8(const uint8_t* p) {
   if constexpr (S == UQ_INT8) {
     const uint2 v = *reinterpret_cast<const uint2*>(p);
     return make_uint2(v.x ^ 0x80808080u, v.y ^ 0x80808080u);
+  } else if constexpr (S == UQ_INT2) {
+    // crumbs c0..c7 of two bytes -> bytes c0 c4 c1 c5 | c2 c6 c3 c7
+    const uint32_t h = *reinterpret_cast<const uint16_t*>(p);
+    const uint32_t v0 = h & 0x0303u, v1 = (h >> 2) & 0x0303u, v2 = (h >> 4) & 0x0303u, v3 = (h >> 6) & 0x0303u;
+    return make_uint2(v0 | (v1 << 16), v2 | (v3 << 16));
   } else {
     const uint32_t v = *reinterpret_cast<const uint32_t*>(p);
     return make_uint2(v & 0x0F0F0F0Fu, (v >> 4) & 0x0F0F0F0Fu);
@@ -319,8 +331,8 @@ __global__ __launch_bounds__(64 * W) void gemv_a8_mfma_kernel(const uint8_t* __r
     // (a wave's LDS accesses execute in issue order: only the compiler must
     //  not move the block's reads and writes across each other)
     asm volatile("" ::: "memory");
-    constexpr int GPB = Ge::MPB / Ge::MPG;  // groups per block (a group never straddles blocks)
-    static_assert(Ge::MPB % Ge::MPG == 0, "blocks hold whole groups");
+    constexpr int GPB = Ge::GPB;  // groups per block (a group never straddles blocks)
+    static_assert(Ge::HALF || Ge::MPB % Ge::MPG == 0, "blocks hold whole groups");
     constexpr int SBG = GPB < 4 ? GPB : 4;  // groups per sub-block
     static_assert(GPB % SBG == 0, "sub-blocks hold whole groups");
     using Frag = typename std::conditional<KM == 64, uint4, uint2>::type;
@@ -341,14 +353,21 @@ __global__ __launch_bounds__(64 * W) void gemv_a8_mfma_kernel(const uint8_t* __r
       uint32_t par[SBG];
 #pragma unroll
       for (int g = 0; g < SBG; ++g) {
-        const int q0 = (sbk * SBG + g) * Ge::MPG;                // first MFMA of the group in the block
-        const int kq0 = wave * Ge::QK + (b * Ge::MPB + q0) * KM;  // its first k
-        const int gk = kq0 / G;                                   // global group
-        const int gi = (b * Ge::MPB + q0) / Ge::MPG;              // group within the wave
+        const int gb = sbk * SBG + g;                             // group within the block
+        const int q0 = Ge::HALF ? gb / 2 : gb * Ge::MPG;          // its (first) k range in the block
+        const int kq0 = wave * Ge::QK + (b * Ge::MPB + q0) * KM;  // that range's first k
+        const int gk = kq0 / G + (Ge::HALF ? gb % 2 : 0);         // global group
+        const int gi = b * GPB + gb;                              // group within the wave
 #pragma unroll
         for (int jj = 0; jj < Ge::MPG; ++jj) {
           const int q = q0 + jj;
-          if constexpr (KM == 64) {
+          if constexpr (Ge::HALF) {
+            // the range's other group: its lanes' B bytes zeroed
+            const uint2 v = a8m_unpack8<S>(bp + (q * KM + KL * lg) * bits / 8);
+            const bool mine = (lg >> 1) == (gb % 2);
+            bv[g][jj] = make_uint2(mine ? v.x : 0u, mine ? v.y : 0u);
+            av[g][jj] = *reinterpret_cast<const uint2*>(xa + kq0 + KL * lg);
+          } else if constexpr (KM == 64) {
             bv[g][jj] = a8m_unpack<S>(bp + (q * KM + KL * lg) * bits / 8);
             av[g][jj] = *reinterpret_cast<const uint4*>(xa + kq0 + jj * KM + KL * lg);
           } else {
@@ -390,6 +409,9 @@ __global__ __launch_bounds__(64 * W) void gemv_a8_mfma_kernel(const uint8_t* __r
           const float t = __builtin_fmaf(sc, float(dd), zc * float(qs[g][i]));
           yacc[i] = __builtin_fmaf(sx[g][i], t, yacc[i]);
         }
+        // 16-code groups (32 per block): the scaling stays with its chain
+        // (left free, the compiler moves it past the last chain and spills)
+        if constexpr (Ge::HALF) asm volatile("" : "+v"(yacc));
       }
     }
     asm volatile("" ::: "memory");  // the next block's writes stay after this block's reads

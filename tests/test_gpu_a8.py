@@ -109,12 +109,14 @@ def test_gemv_a8_long_k(lib):
 
 def test_gemv_a8_batched_equivalence(lib):
     """Row i of an M-row call equals the single-row call: bit for bit where both
-    run the dot-product kernel (INT2, and K in one block), within fp32 rounding
-    where 2-8 rows run on the integer matrix cores (INT4 / INT8; INT4 G32 from
-    4 rows), whose rows agree bit for bit across M."""
+    run the dot-product kernel (INT2 G32, INT2 G16 at 2 rows, and K in one
+    block), within fp32 rounding where 2-8 rows run on the integer matrix cores
+    (INT4 / INT8; INT4 G32 from 4 rows, INT2 G16 from 3), whose rows agree bit
+    for bit across M."""
     n, k = 200, 2048
     w, x = workloads.make_random(n, k, 8, seed=44, outliers=True)
-    for scheme, group in (("int4", 64), ("int2", 32), ("int8", 64), ("int8", 128), ("int4", 32), ("int8", 32)):
+    for scheme, group in (("int4", 64), ("int2", 32), ("int8", 64), ("int8", 128), ("int4", 32), ("int8", 32),
+                          ("int2", 16)):
         lay, codes, params = packed_on_device(lib, scheme, group, w)
         ys = [run_a8(lib, lay, codes, params, x[i:i + 1], 1)[0] for i in range(8)]
         full = {}
@@ -122,15 +124,15 @@ def test_gemv_a8_batched_equivalence(lib):
             note(f"a8 batched equivalence {scheme} G{group} m={m}")
             y = run_a8(lib, lay, codes, params, x, m)
             full[m] = y
-            if scheme == "int2":
+            if (scheme, group) == ("int2", 32) or ((scheme, group) == ("int2", 16) and m == 2):
                 for i in range(m):
                     assert np.array_equal(y[i], ys[i]), (scheme, group, m, i)
             else:
                 tight(y, np.stack(ys[:m]).astype(np.float64), f"a8 equiv {scheme} G{group} m={m}")
-        if scheme != "int2":
+        if (scheme, group) != ("int2", 32):
             # one kernel per set of row counts (INT4 G32: the dot product below
-            # four rows, the matrix cores from four)
-            sets = ((2, 3), (4, 8)) if (scheme, group) == ("int4", 32) else ((2, 3, 4, 8),)
+            # four rows, the matrix cores from four; INT2 G16 from three)
+            sets = {("int4", 32): ((2, 3), (4, 8)), ("int2", 16): ((3, 4, 8),)}.get((scheme, group), ((2, 3, 4, 8),))
             for ms in sets:
                 for m in ms[:-1]:
                     assert np.array_equal(full[m].view(np.uint32), full[ms[-1]][:m].view(np.uint32)), (scheme, group, m)
