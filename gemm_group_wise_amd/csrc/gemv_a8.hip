@@ -346,12 +346,12 @@ hipError_t launch_a8_sel(const uq_layout* L, const void* codes, const void* para
                          int m, hipStream_t stream) {
   if constexpr (a8_mfma_scheme<S, G>()) {
     constexpr int W = 8;
-    // INT4 with 32-code groups (eight one-MFMA groups per block) pays off from
-    // four rows (measured on MI355X, N11008 M=2 / 4 / 8: 10.9 / 16.9 / 43.6 us
-    // on the dot product against 13.3 / 15.3 / 18.7 us here); INT8 G32 from
-    // two (N4096 M=2 / 4 / 8 9.1 / 13.1 / 18.4 -> 7.3 / 7.9 / 8.6 us); INT2
-    // G16 from three (N4096 M=2 / 3 / 8 7.7 / 11.5 / 18.3 -> 7.8 / 8.4 / 8.7 us).
-    constexpr int min_rows = S == UQ_INT4 && G == 32 ? 4 : S == UQ_INT2 ? 3 : 2;
+    // Measured on MI355X against the dot product: INT4 G32 N11008 M=2 / 3 / 4
+    // / 8 10.9 / 16.7 / 16.9 / 43.6 -> 9.6 / 11.4 / 12.0 / 14.7 us, INT8 G32
+    // N4096 M=2 / 4 / 8 9.1 / 13.1 / 18.4 -> 7.3 / 7.9 / 8.5 us; INT2 G16 pays
+    // off from three rows (N4096 M=2 / 3 / 8 7.6 / 11.5 / 18.3 -> 7.7 / 8.4 /
+    // 8.7 us).
+    constexpr int min_rows = S == UQ_INT2 ? 3 : 2;
     if (m >= min_rows && a8m_fits<S, G>(L->k, 8, W)) {
       if (m <= 2) return launch_a8m_w<S, G, 2, W>(L, codes, params, x, y, m, stream);
       if (m <= 4) return launch_a8m_w<S, G, 4, W>(L, codes, params, x, y, m, stream);

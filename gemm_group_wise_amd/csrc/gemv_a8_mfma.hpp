@@ -409,9 +409,10 @@ __global__ __launch_bounds__(64 * W) void gemv_a8_mfma_kernel(const uint8_t* __r
           const float t = __builtin_fmaf(sc, float(dd), zc * float(qs[g][i]));
           yacc[i] = __builtin_fmaf(sx[g][i], t, yacc[i]);
         }
-        // 16-code groups (32 per block): the scaling stays with its chain
-        // (left free, the compiler moves it past the last chain and spills)
-        if constexpr (Ge::HALF) asm volatile("" : "+v"(yacc));
+        // with several sub-blocks per block (16- and 32-code groups) the
+        // scaling stays with its chain (left free, the compiler moves it past
+        // the last chain and spills: 256 VGPRs and scratch)
+        asm volatile("" : "+v"(yacc));
       }
     }
     asm volatile("" ::: "memory");  // the next block's writes stay after this block's reads

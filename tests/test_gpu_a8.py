@@ -111,8 +111,7 @@ def test_gemv_a8_batched_equivalence(lib):
     """Row i of an M-row call equals the single-row call: bit for bit where both
     run the dot-product kernel (INT2 G32, INT2 G16 at 2 rows, and K in one
     block), within fp32 rounding where 2-8 rows run on the integer matrix cores
-    (INT4 / INT8; INT4 G32 from 4 rows, INT2 G16 from 3), whose rows agree bit
-    for bit across M."""
+    (INT4 / INT8; INT2 G16 from 3 rows), whose rows agree bit for bit across M."""
     n, k = 200, 2048
     w, x = workloads.make_random(n, k, 8, seed=44, outliers=True)
     for scheme, group in (("int4", 64), ("int2", 32), ("int8", 64), ("int8", 128), ("int4", 32), ("int8", 32),
@@ -130,9 +129,9 @@ def test_gemv_a8_batched_equivalence(lib):
             else:
                 tight(y, np.stack(ys[:m]).astype(np.float64), f"a8 equiv {scheme} G{group} m={m}")
         if (scheme, group) != ("int2", 32):
-            # one kernel per set of row counts (INT4 G32: the dot product below
-            # four rows, the matrix cores from four; INT2 G16 from three)
-            sets = {("int4", 32): ((2, 3), (4, 8)), ("int2", 16): ((3, 4, 8),)}.get((scheme, group), ((2, 3, 4, 8),))
+            # one kernel per set of row counts (INT2 G16: the dot product at two
+            # rows, the matrix cores from three)
+            sets = ((3, 4, 8),) if (scheme, group) == ("int2", 16) else ((2, 3, 4, 8),)
             for ms in sets:
                 for m in ms[:-1]:
                     assert np.array_equal(full[m].view(np.uint32), full[ms[-1]][:m].view(np.uint32)), (scheme, group, m)
