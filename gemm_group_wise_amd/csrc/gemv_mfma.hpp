@@ -202,12 +202,15 @@ __device__ __forceinline__ void mfma_chains2x2(f32x4 (&acc)[2], const f16x8v (&a
                : "v"(a[0][0]), "v"(b[0][0]), "v"(a[0][1]), "v"(b[0][1]), "v"(a[1][0]), "v"(b[1][0]), "v"(a[1][1]),
                  "v"(b[1][1]));
 }
-// INT2: four 16-code groups, one v_mfma_f32_16x16x16_f16 each (4 fp16 per lane).
-__device__ __forceinline__ void mfma_chains16x4(f32x4 (&acc)[4], const f16x4v (&a)[4], const f16x4v (&b)[4]) {
-  asm volatile(UQ_MF_PRE "v_mfma_f32_16x16x16_f16 %0, %4, %5, %0\n\tv_mfma_f32_16x16x16_f16 %1, %6, %7, %1\n\t"
-               "v_mfma_f32_16x16x16_f16 %2, %8, %9, %2\n\tv_mfma_f32_16x16x16_f16 %3, %10, %11, %3" UQ_MF_POST
-               : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3])
-               : "v"(a[0]), "v"(b[0]), "v"(a[1]), "v"(b[1]), "v"(a[2]), "v"(b[2]), "v"(a[3]), "v"(b[3]));
+// INT2: eight 16-code groups, one v_mfma_f32_16x16x16_f16 each (4 fp16 per lane).
+__device__ __forceinline__ void mfma_chains16x8(f32x4 (&acc)[8], const f16x4v (&a)[8], const f16x4v (&b)[8]) {
+  asm volatile(UQ_MF_PRE "v_mfma_f32_16x16x16_f16 %0, %8, %9, %0\n\tv_mfma_f32_16x16x16_f16 %1, %10, %11, %1\n\t"
+               "v_mfma_f32_16x16x16_f16 %2, %12, %13, %2\n\tv_mfma_f32_16x16x16_f16 %3, %14, %15, %3\n\t"
+               "v_mfma_f32_16x16x16_f16 %4, %16, %17, %4\n\tv_mfma_f32_16x16x16_f16 %5, %18, %19, %5\n\t"
+               "v_mfma_f32_16x16x16_f16 %6, %20, %21, %6\n\tv_mfma_f32_16x16x16_f16 %7, %22, %23, %7" UQ_MF_POST
+               : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]), "+v"(acc[4]), "+v"(acc[5]), "+v"(acc[6]), "+v"(acc[7])
+               : "v"(a[0]), "v"(b[0]), "v"(a[1]), "v"(b[1]), "v"(a[2]), "v"(b[2]), "v"(a[3]), "v"(b[3]),
+                 "v"(a[4]), "v"(b[4]), "v"(a[5]), "v"(b[5]), "v"(a[6]), "v"(b[6]), "v"(a[7]), "v"(b[7]));
 }
 #undef UQ_MF_PRE
 #undef UQ_MF_OP
@@ -352,8 +355,11 @@ __global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(const uint8_t* __rest
   const uint8_t* xa = xs + (ln % MT) * Ge::XPITCH;  // this lane's A row (rows past MT repeat)
   const uint8_t* bp = blk + ln * Ge::BPITCH;        // this lane's weight row of the block
   // MFMAs per sub-block: four (67-90 VGPRs up to eight activation rows;
-  // eight MFMAs per sub-block took 128 and left two workgroups per CU)
-  constexpr int SB = KM == 16 ? 4 : (Ge::MPB < 4 ? Ge::MPB : 4);
+  // eight MFMAs per sub-block took 128 and left two workgroups per CU); INT2
+  // G16, which runs five to eight rows at one workgroup per CU (its staged
+  // activations and per-group sums take 82 KB of LDS), eight, one per group
+  // (118-162 VGPRs; measured on MI355X, N4096 M=8 7.2 -> 7.0 us)
+  constexpr int SB = KM == 16 ? 8 : (Ge::MPB < 4 ? Ge::MPB : 4);
   constexpr int GS = SB / Ge::MPG;                  // groups per sub-block
   static_assert(Ge::MPB % SB == 0 && SB % Ge::MPG == 0, "sub-blocks hold whole groups");
   static_assert(Ge::HB == 1 || Ge::MPB / SB == Ge::HB, "a half block per sub-block");
@@ -440,16 +446,16 @@ __global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(const uint8_t* __rest
 #pragma unroll
       for (int g = 0; g < GS; ++g) acc[g] = f32x4{tc[g][0], tc[g][1], tc[g][2], tc[g][3]};
       if constexpr (KM == 16) {
-        static_assert(Ge::MPG == 1 && GS == 4, "16-code groups: one MFMA each, four per sub-block");
-        f16x4v ca[4], cb[4];
+        static_assert(Ge::MPG == 1 && GS == 8, "16-code groups: one MFMA each, eight per sub-block");
+        f16x4v ca[8], cb[8];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
+        for (int g = 0; g < 8; ++g) {
           uint32_t bb[4];
           mf_unpack<S>(bd[g][0], bd[g][1], lg, bb);
           ca[g] = __builtin_bit_cast(f16x4v, make_uint2(av[g].x, av[g].y));
           cb[g] = __builtin_bit_cast(f16x4v, make_uint2(bb[0], bb[1]));
         }
-        mfma_chains16x4(acc, ca, cb);
+        mfma_chains16x8(acc, ca, cb);
       } else {
         f16x8v ca[GS][Ge::MPG], cb[GS][Ge::MPG];
 #pragma unroll
