@@ -160,6 +160,26 @@ def test_gemv_a8_full_workloads(lib, name, ms):
         tight(y, y_ref[:m], f"a8 {name} m={m}")
 
 
+@pytest.mark.parametrize("name,ms", [("q4_0_k4096_n11008", (1, 2, 4)), ("q8_0_k4096_n4096", (1, 8))])
+def test_gemv_a8_full_gguf_workloads(lib, name, ms):
+    """GGUF Q4_0 / Q8_0 blocks through the import, then the A8 GEMV at full size:
+    the oracle's reference takes the same blocks as INT codes with (d, -offset*d)."""
+    wl = workloads.WORKLOADS[name]
+    blob, x = workloads.make_gguf_workload(wl)
+    lay, codes, params = lib.uq_import_gguf(wl.gguf, blob, wl.n, wl.k)
+    codes, params = dev(codes), dev(params)
+    q_w, s16, z16 = o.gguf_as_int(blob, wl.gguf, wl.n, wl.k)
+    q_x, s_x = o.quantize_activations(x[:max(ms)], wl.group)
+    y_ref = o.gemv_a8_ref(q_x, s_x, q_w, s16, z16, wl.group)
+    xd = o.dequant_activations(q_x, s_x, wl.group)
+    wd = o.decode_gguf(blob, wl.gguf, wl.n, wl.k)
+    for m in ms:
+        note(f"a8 full GGUF workload {name} m={m}")
+        y = run_a8(lib, lay, codes, params, x, m)
+        gate(y, y_ref[:m], xd[:m], wd, f"a8 {name} m={m}")
+        tight(y, y_ref[:m], f"a8 {name} m={m}")
+
+
 def test_gemv_a8_refuses_nf4(lib):
     n, k = 16, 256
     w, x = workloads.make_random(n, k, 1, seed=46)
