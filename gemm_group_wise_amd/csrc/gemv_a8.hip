@@ -333,14 +333,14 @@ hipError_t launch_a8_m(const uq_layout* L, const void* codes, const void* params
 namespace uq {
 namespace {
 
-// 2 to 8 activation rows of INT4 / INT8 weights with groups of 64 or 128 on
-// the integer matrix cores when the shape fits (judged at eight rows, so
+// 2 to 8 activation rows (3 to 8 for INT2) on the integer matrix cores when
+// the layout has a matrix-core form (INT4 / INT8 with groups of 32, 64 or
+// 128, INT2 with groups of 16) and the shape fits (judged at eight rows, so
 // every such M takes the same kernel), else the dot-product kernel.  Eight
 // waves per workgroup, each an eighth of every row.  Measured on MI355X
 // (graph replay): INT8 G128 N4096 M=8 18.7 -> 8.0 us, INT4 G64 N11008 M=4
-// 16.9 -> 11.3 us; a single row (INT8 5.8 against 6.0 us, INT4 7.8 against
-// 8.8) and 32-code groups (Q8_0 M=8 18.5 against 19.3 us) stay on the
-// dot-product kernel.
+// 16.9 -> 11.3 us when first moved; a single row stays on the dot-product
+// kernel (INT8 5.8 against 6.0 us, INT4 7.8 against 8.8).
 template <int S, int G>
 hipError_t launch_a8_sel(const uq_layout* L, const void* codes, const void* params, const uint16_t* x, float* y,
                          int m, hipStream_t stream) {
