@@ -468,13 +468,16 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
 
 // Weight rows per wave.  Four for a single activation row (two for INT8,
 // whose rows hold twice the bytes: N4096 M=1 5.43 -> 5.03 us; INT4 is slower
-// with two, 6.79 -> 7.24 us, and every scheme with eight); with two or more
-// activation rows the per-row state grows and two rows per wave keep more
-// waves resident (measured on MI355X: 5-14 % faster for INT4 M=4 and INT8
-// M=8).  INT2 keeps four (its LDS traffic per code byte is the highest).
+// with two, 6.79 -> 7.24 us, and every scheme with eight; two for NF4, the
+// fastest of one to five rows or within 3 % of it at every shape tried:
+// K4096 N14336 9.79 -> 9.18 us, N11008 8.18 -> 8.07, N4096 5.03 -> 4.75,
+// K14336 N4096 16.2 -> 11.4); with two or more activation rows the
+// per-row state grows and two rows per wave keep more waves resident
+// (measured on MI355X: 5-14 % faster for INT4 M=4 and INT8 M=8).  INT2 keeps
+// four (its LDS traffic per code byte is the highest).
 template <int S, int MT>
 constexpr int rows_per_wave() {
-  if (MT == 1) return S == UQ_INT8 ? 2 : 4;
+  if (MT == 1) return S == UQ_INT8 || S == UQ_NF4 ? 2 : 4;
   return S == UQ_INT2 ? 4 : 2;
 }
 
