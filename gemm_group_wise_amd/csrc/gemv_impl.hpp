@@ -490,16 +490,32 @@ hipError_t launch_ipt(int ipt, dim3 grid, void** args, size_t shmem, hipStream_t
   return hipLaunchKernel(fn, grid, dim3(kThreads), args, shmem, stream);
 }
 
+// Activations staged per K block: one LDS block of x, at most kMaxIPT group
+// parts per thread (kMaxIPT * kThreads parts of GP activations across the MT
+// rows), at most K.
+template <int S, int G, int MT>
+int block_k(int k) {
+  using Gm = Geo<S, G, MT>;
+  int kb_max = x_block<S>() / MT;
+  if (kb_max > k) kb_max = k;
+  if (int64_t(MT) * (kb_max / Gm::GP) > int64_t(kMaxIPT) * kThreads) kb_max = kMaxIPT * kThreads * Gm::GP / MT;
+  return kb_max;
+}
+
+// Whether the whole K range is one K block and one group of 64 * U chunks per
+// lane: the loop-free kernel body.
+template <int S, int G, int MT>
+bool one_block(int k) {
+  using Gm = Geo<S, G, MT>;
+  return block_k<S, G, MT>(k) == k && k <= 64 * Gm::U * Gm::CW;
+}
+
 template <int S, int G, int MT, int R>
 hipError_t launch(const uq_layout* L, const void* codes, const void* params, const uint16_t* x,
                   float* y, int m, hipStream_t stream) {
   using Gm = Geo<S, G, MT>;
   const int k = int(L->k), n = int(L->n);
-  int kb_max = x_block<S>() / MT;
-  if (kb_max > k) kb_max = k;
-  // At most 8 staged activation parts per thread (kMaxIPT): a block holds at
-  // most kMaxIPT * kThreads parts of GP activations across the MT rows.
-  if (int64_t(MT) * (kb_max / Gm::GP) > int64_t(kMaxIPT) * kThreads) kb_max = kMaxIPT * kThreads * Gm::GP / MT;
+  int kb_max = block_k<S, G, MT>(k);
   const size_t shmem = (Gm::NF ? 2048 : 0) + size_t(MT) * kb_max * 2 + (Gm::NF ? 0 : size_t(MT) * (kb_max / Gm::GP) * 8);
   const int64_t rows_per_block = kWaves * R;
   const int64_t blocks = (int64_t(n) + rows_per_block - 1) / rows_per_block;  // n < 2^31: no overflow in int64
@@ -510,7 +526,7 @@ hipError_t launch(const uq_layout* L, const void* codes, const void* params, con
   void* args[] = {&c8, &p8, (void*)&x, &y, (void*)&n, (void*)&k, &m, &kb_max};
   const int items = MT * (kb_max / Gm::GP);  // staged activation parts per K block
   const int ipt = items <= kThreads ? 1 : items <= 2 * kThreads ? 2 : items <= 4 * kThreads ? 4 : 8;
-  const bool one = kb_max == k && k <= 64 * Gm::U * Gm::CW;
+  const bool one = one_block<S, G, MT>(k);
   return one ? launch_ipt<S, G, MT, R, true>(ipt, grid, args, shmem, stream)
              : launch_ipt<S, G, MT, R, false>(ipt, grid, args, shmem, stream);
 }
@@ -526,6 +542,15 @@ hipError_t launch_m(const uq_layout* L, const void* codes, const void* params, c
     constexpr int R = rows_per_wave<S, 1>();
     if ((L->n + int64_t(kWaves) * R - 1) / (int64_t(kWaves) * R) < kComputeUnits)
       return launch<S, G, 1, 1>(L, codes, params, x, y, m, stream);
+    // Past one K block (the kernel loops over K blocks and chunk groups) two
+    // rows per wave beat four (measured on MI355X, M=1: INT4 G64 K14336 N4096
+    // 11.4 -> 8.7 us, K11008 N4096 9.7 -> 7.7, K8192 N8192 10.2 -> 8.9, INT2
+    // G16 K14336 N4096 11.0 -> 8.8; one row per wave slower than two at every
+    // such shape), while four stay faster within one block (K4096 N11008 6.53
+    // against 6.75 us).
+    if constexpr (R > 2) {
+      if (!one_block<S, G, 1>(int(L->k))) return launch<S, G, 1, 2>(L, codes, params, x, y, m, stream);
+    }
     return launch<S, G, 1, R>(L, codes, params, x, y, m, stream);
   }
   if (m == 2) return launch<S, G, 2, rows_per_wave<S, 2>()>(L, codes, params, x, y, m, stream);

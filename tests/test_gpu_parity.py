@@ -206,6 +206,24 @@ def test_gemv_k_blocks(lib, m, k):
         gate(y, o.gemv_ref(x[:m], wdq), x[:m], wdq, f"k-blocks {scheme} m={m} k={k}")
 
 
+@pytest.mark.parametrize("k", [8192, 8320])
+def test_gemv_long_k_many_rows(lib, k):
+    """One activation row, K past one block and N large enough for the usual
+    rows per wave (INT4 and INT2 then take two rows per wave instead of four),
+    a ragged last workgroup (N = 4100) and, at K = 8320, a ragged chunk group."""
+    n = 4100
+    w, x = workloads.make_random(n, k, 1, seed=90 + k % 7, outliers=True)
+    for scheme, group in (("int4", 64), ("int4", 32), ("int4", 128), ("int2", 16), ("int2", 64),
+                          ("nf4", 64), ("int8", 128)):
+        if k % max(group, CW[scheme]):
+            continue
+        note(f"gemv long K {scheme} G{group} n={n} k={k} m=1")
+        lay, codes, params = packed_on_device(lib, scheme, group, w)
+        wdq = oracle_dequant(w, scheme, group)
+        y = run_gemv(lib, lay, codes, params, x, 1)
+        gate(y, o.gemv_ref(x[:1], wdq), x[:1], wdq, f"long K {scheme} G{group} k={k}")
+
+
 def test_gemv_on_side_stream(lib):
     import torch
     w, x = workloads.make_random(64, 512, 1, seed=10)
